@@ -1,0 +1,315 @@
+"""Pins of the oracle's dequantisation, activations, combine and whole layer
+(CPU only): closed forms computed by hand with ``math``, a per-element brute
+force, the page's de-interleave golden and invariants of the definition."""
+import json
+import math
+import os
+import struct
+from types import SimpleNamespace as NS
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import moe as O
+from oracle import formats as F
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _silu(v):
+    return v / (1.0 + math.exp(-v))
+
+
+def _sig(v):
+    return 1.0 / (1.0 + math.exp(-v))
+
+
+def _bf16(v):
+    """bits of a float that is exactly bf16-representable (checked)."""
+    b = struct.unpack("<I", struct.pack("<f", v))[0]
+    assert b & 0xFFFF == 0, v
+    return b >> 16
+
+
+def _const_proj(n_rows_codes, K, scale_code, dtype_scale, group, gs=None, bias=None):
+    """One expert; row r gets nibble n_rows_codes[r] in every K position."""
+    codes = np.array([[c | (c << 4)] * (K // 2) for c in n_rows_codes], dtype=np.uint8)[None]
+    scales = np.full((1, len(n_rows_codes), K // group), scale_code, dtype=dtype_scale)
+    return NS(codes=codes, scales=scales,
+              gs=None if gs is None else np.array([gs], dtype=np.float32),
+              bias=None if bias is None else np.array([bias], dtype=np.uint16))
+
+
+# ----------------------------------------------------------------------------- dequant
+def _brute_dequant_matvec(qtype, codes, scales, gs, x):
+    """Per-element reading of the packed layout, independent of the oracle's
+    vectorised unpack: byte k//2 of row n, low nibble for even k."""
+    N, Kh = codes.shape
+    K = Kh * 2
+    e4m3 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().tolist()
+    out = []
+    for n in range(N):
+        acc = 0.0
+        for k in range(K):
+            byte = int(codes[n, k // 2])
+            u = (byte >> 4) if (k & 1) else (byte & 0xF)
+            if qtype == "int4_g128":
+                s = struct.unpack("<f", struct.pack("<I", int(scales[n, k // 128]) << 16))[0]
+                w = (u - 8) * s
+            else:
+                sign = -1.0 if u & 8 else 1.0
+                e, m = (u >> 1) & 3, u & 1
+                v = sign * (m * 0.5 if e == 0 else 2.0 ** (e - 1) * (1 + m / 2))
+                if qtype == "nvfp4_g16":
+                    w = v * e4m3[int(scales[n, k // 16])] * float(gs)
+                else:
+                    w = v * 2.0 ** (int(scales[n, k // 32]) - 127)
+            acc += w * x[k]
+        out.append(acc)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("qtype,N,K", [("int4_g128", 3, 256), ("nvfp4_g16", 5, 48), ("mxfp4_g32", 4, 96)])
+def test_dequant_matches_per_element_brute_force(qtype, N, K):
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    g = W.GROUP[qtype]
+    if qtype == "int4_g128":
+        scales = W._to_bf16_bits(rng.uniform(0.002, 0.02, (N, K // g)).astype(np.float32))
+        gs = None
+    elif qtype == "nvfp4_g16":
+        scales = rng.integers(0x20, 0x70, size=(N, K // g), dtype=np.uint8)
+        gs = np.float32(3.1e-3)
+    else:
+        scales = rng.integers(118, 130, size=(N, K // g), dtype=np.uint8)
+        gs = None
+    x = rng.standard_normal(K)
+    got = O.dequant(qtype, codes, scales, gs) @ x
+    ref = _brute_dequant_matvec(qtype, codes, scales, gs, x)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_dequant_constant_closed_forms():
+    # int4: nibble 13 -> 5, scale 2^-7 ; NVFP4: code 0xB -> -1.5, e4m3 0x40 = 2, gs 0.25 ;
+    # MXFP4: code 0x7 -> 6, E8M0 130 -> 8
+    d = O.dequant("int4_g128", np.full((2, 64), 0xDD, np.uint8), np.full((2, 1), _bf16(2.0 ** -7), np.uint16))
+    assert np.all(d == 5 * 2.0 ** -7)
+    d = O.dequant("nvfp4_g16", np.full((2, 8), 0xBB, np.uint8), np.full((2, 1), 0x40, np.uint8), 0.25)
+    assert np.all(d == -1.5 * 2 * 0.25)
+    d = O.dequant("mxfp4_g32", np.full((2, 16), 0x77, np.uint8), np.full((2, 1), 130, np.uint8))
+    assert np.all(d == 48.0)
+    # nibble order: low nibble is the even K index
+    d = O.dequant("mxfp4_g32", np.full((1, 16), 0x72, np.uint8), np.full((1, 1), 127, np.uint8))
+    assert d[0, 0] == 1.0 and d[0, 1] == 6.0
+
+
+# ----------------------------------------------------------------------------- activations
+def test_silu_mul_hand_values():
+    g = np.array([1.0, -2.0, 0.0, 3.5])
+    u = np.array([2.0, 0.5, 7.0, -1.0])
+    want = [_silu(a) * b for a, b in zip(g, u)]
+    assert np.allclose(O.act_silu_mul(g, u), want, rtol=1e-15)
+
+
+def test_swiglu_alpha_hand_values():
+    g = np.array([1.75, -0.5, 4.0, 12.0])
+    u = np.array([0.375, -1.0, -9.0, 2.0])
+    a, lim = 1.702, 7.0
+    want = [min(x, lim) * _sig(a * min(x, lim)) * (max(-lim, min(y, lim)) + 1) for x, y in zip(g, u)]
+    assert np.allclose(O.act_swiglu_alpha(g, u, a, lim), want, rtol=1e-15)
+    # up = -1 zeroes the output, gate = 0 zeroes it; no clamp with an infinite limit
+    assert O.act_swiglu_alpha(np.array([3.0]), np.array([-1.0]), a, math.inf)[0] == 0.0
+    assert O.act_swiglu_alpha(np.array([0.0]), np.array([5.0]), a, math.inf)[0] == 0.0
+    assert O.act_swiglu_alpha(np.array([12.0]), np.array([9.0]), a, math.inf)[0] == pytest.approx(
+        12.0 * _sig(a * 12.0) * 10.0, rel=1e-15)
+
+
+def test_split_gate_up_golden():
+    g = json.load(open(os.path.join(GOLDEN, "deinterleave_small.json")))
+    rows = np.array(g["rows_in"], dtype=object)
+    gate, up = O.split_gate_up(rows, interleaved=True)
+    assert list(gate) == g["gate_rows"] and list(up) == g["up_rows"]
+    gate, up = O.split_gate_up(np.array(g["gate_rows"] + g["up_rows"], dtype=object), interleaved=False)
+    assert list(gate) == g["gate_rows"] and list(up) == g["up_rows"]
+
+
+# ----------------------------------------------------------------------------- combine
+def test_combine_norm_weight_first_and_eps_placement():
+    # H = 2, one live slot, one dead slot (its row is NaN and must not leak)
+    Y = np.array([[3e-4, 4e-4], [np.nan, np.nan]])
+    g = np.array([[0.6, 0.4]])
+    loc = np.array([[0, -1]])
+    nw = np.array([2.0, 0.5])
+    out = O.combine(Y, g, loc, nw, 1e-8)
+    z = [6e-4, 2e-4]
+    inv = 1 / math.sqrt((z[0] ** 2 + z[1] ** 2) / 2 + 1e-8)
+    assert np.allclose(out[0], [0.6 * inv * z[0], 0.6 * inv * z[1]], rtol=1e-14)
+
+
+def test_combine_reduces_to_rmsnorm_and_weighted_sum():
+    rng = np.random.default_rng(3)
+    y = rng.standard_normal((1, 64))
+    out = O.combine(y, np.array([[1.0]]), np.array([[0]]), np.ones(64), 1e-8)
+    rms = np.sqrt(np.mean(y ** 2) + 1e-8)
+    assert np.allclose(out, y / rms, rtol=1e-14)
+    Y = rng.standard_normal((6, 64))
+    g = rng.random((2, 3))
+    loc = np.array([[0, 1, -1], [2, -1, 0]])
+    out = O.combine(Y, g, loc, None, 1e-8)
+    assert np.allclose(out[0], g[0, 0] * Y[0] + g[0, 1] * Y[1], rtol=1e-14)
+    assert np.allclose(out[1], g[1, 0] * Y[3] + g[1, 2] * Y[5], rtol=1e-14)
+
+
+def test_norm_weight_rounds_one_plus_w_to_bf16():
+    w = np.array([_bf16(0.0), _bf16(2.0 ** -9), _bf16(-0.25), _bf16(3 * 2.0 ** -9)], dtype=np.uint16)
+    nw = O.norm_weight(w)
+    # 1 + 2^-9 is below half an ulp (2^-8) of 1 -> 1 ; 1 + 3*2^-9 -> 1 + 2^-7 (nearest)
+    assert list(nw) == [1.0, 1.0, 0.75, 1 + 2.0 ** -7]
+
+
+# ----------------------------------------------------------------------------- whole layer
+def test_layer_int4_one_token_one_expert_closed_form():
+    H = I = 128
+    x0 = 0.5
+    w13 = _const_proj([10] * I + [5] * I, H, _bf16(2.0 ** -7), np.uint16, 128)   # gate 2, up -3
+    w2 = _const_proj([12] * H, I, _bf16(2.0 ** -6), np.uint16, 128)              # 4
+    x = np.full((1, H), _bf16(x0), np.uint16)
+    out = O.moe_layer("int4_g128", x, np.array([[0]], np.int32), np.array([[0.75]], np.float32),
+                      w13, w2, expert_start=0, n_local=1, bf16_intermediates=False)
+    hg, hu = 2 * 2.0 ** -7 * H * x0, -3 * 2.0 ** -7 * H * x0
+    y = 4 * 2.0 ** -6 * I * (_silu(hg) * hu)
+    assert np.allclose(out, 0.75 * y, rtol=1e-14)
+
+
+def test_layer_nvfp4_norm_closed_form_with_dead_slot():
+    H = I = 32
+    x0 = 0.125
+    w13 = _const_proj([2] * I + [11] * I, H, 0x40, np.uint8, 16, gs=0.25)        # 1.0 / -1.5, scale 2
+    w2 = _const_proj([4] * H, I, 0x40, np.uint8, 16, gs=0.5)                     # 2.0 * 2 * 0.5
+    x = np.full((1, H), _bf16(x0), np.uint16)
+    ids = np.array([[5, 0]], np.int32)   # expert 5 is outside the single-expert slice
+    gw = np.array([[0.3, 0.7]], np.float32)
+    nwb = np.full(H, _bf16(0.0), np.uint16)
+    out = O.moe_layer("nvfp4_g16", x, ids, gw, w13, w2, expert_start=0, n_local=1,
+                      norm_w_bits=nwb, eps=1e-8, bf16_intermediates=False)
+    hg, hu = 0.5 * H * x0, -0.75 * H * x0
+    y = 2.0 * I * _silu(hg) * hu
+    want = float(gw[0, 1]) * y / math.sqrt(y * y + 1e-8)
+    assert np.allclose(out, want, rtol=1e-14)
+
+
+@pytest.mark.parametrize("limit", [math.inf, 1.0])
+def test_layer_mxfp4_swiglu_interleaved_bias_closed_form(limit):
+    H = I = 32
+    x0 = 0.0625
+    b13 = [_bf16(0.25), _bf16(-0.125)] * I                 # interleaved gate/up bias
+    w13 = _const_proj([3, 1] * I, H, 126, np.uint8, 32, bias=b13)   # gate 1.5, up 0.5, scale 0.5
+    w2 = _const_proj([2] * H, I, 125, np.uint8, 32, bias=[_bf16(0.5)] * H)  # 1.0 * 0.25
+    x = np.full((1, H), _bf16(x0), np.uint16)
+    out = O.moe_layer("mxfp4_g32", x, np.array([[0]], np.int32), np.array([[0.875]], np.float32),
+                      w13, w2, expert_start=0, n_local=1, act="swiglu_alpha", alpha=1.702,
+                      limit=limit, interleaved_w13=True, bf16_intermediates=False)
+    hg = 1.5 * 0.5 * H * x0 + 0.25
+    hu = 0.5 * 0.5 * H * x0 - 0.125
+    g, u = min(hg, limit), max(-limit, min(hu, limit))
+    a = g * _sig(1.702 * g) * (u + 1)
+    y = 0.25 * I * a + 0.5
+    assert np.allclose(out, 0.875 * y, rtol=1e-14)
+
+
+def _small(qtype, M=None, **kw):
+    wl = W.small_workload(qtype, **kw)
+    lw = W.make_weights(wl)
+    inp = W.make_inputs(wl, M or wl.Ms[0])
+    return wl, lw, inp
+
+
+def _run(wl, lw, inp, ids=None, gw=None, **kw):
+    args = dict(expert_start=wl.expert_start, n_local=wl.n_local, act=wl.act, alpha=wl.alpha,
+                limit=wl.limit, norm_w_bits=lw.norm_w, eps=wl.eps,
+                interleaved_w13=wl.interleaved_w13)
+    args.update(kw)
+    return O.moe_layer(wl.qtype, inp.x, inp.topk_ids if ids is None else ids,
+                       inp.topk_weights if gw is None else gw, lw.w13, lw.w2, **args)
+
+
+@pytest.mark.parametrize("qtype", W.QTYPES)
+def test_layer_linear_in_topk_weights(qtype):
+    wl, lw, inp = _small(qtype)
+    rng = np.random.default_rng(11)
+    g1 = rng.random(inp.topk_weights.shape)
+    g2 = rng.random(inp.topk_weights.shape)
+    o1 = _run(wl, lw, inp, gw=g1, bf16_intermediates=False)
+    o2 = _run(wl, lw, inp, gw=g2, bf16_intermediates=False)
+    o12 = _run(wl, lw, inp, gw=g1 + g2, bf16_intermediates=False)
+    assert np.allclose(o12, o1 + o2, rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("qtype", W.QTYPES)
+def test_layer_token_permutation_invariance(qtype):
+    wl, lw, inp = _small(qtype)
+    perm = np.random.default_rng(12).permutation(inp.M)
+    base = _run(wl, lw, inp)
+    pin = W.LayerInputs(inp.x[perm], inp.topk_ids[perm], inp.topk_weights[perm], inp.M)
+    other = _run(wl, lw, pin)
+    assert np.allclose(other, base[perm], rtol=1e-12, atol=1e-12)
+
+
+def test_layer_zero_for_off_slice_tokens():
+    wl, lw, inp = _small("nvfp4_g16")
+    ids = inp.topk_ids.copy()
+    ids[::3] = (ids[::3] % 8) + 40         # all of every third token's slots outside [8, 24)
+    out = _run(wl, lw, inp, ids=ids)
+    assert np.all(out[::3] == 0.0)
+    assert np.any(out[1::3] != 0.0)
+
+
+def test_layer_token_subset_matches_full():
+    wl, lw, inp = _small("mxfp4_g32")
+    full = _run(wl, lw, inp)
+    sub = [5, 0, 17, 40]
+    part = _run(wl, lw, inp, tokens=sub)
+    assert np.array_equal(part, full[sub])
+
+
+def test_layer_zero_padding_of_intermediate_is_neutral():
+    wl, lw, inp = _small("int4_g128", I=256)
+    base = _run(wl, lw, inp)
+    I, P = 256, 128
+    E = wl.n_local
+    zero = 0x88                            # int4 nibble 8 is the value 0
+
+    def pad_rows(a, fill, axis):
+        shape = list(a.shape)
+        shape[axis] = P
+        return np.full(shape, fill, a.dtype)
+    w13 = lw.w13
+    c = np.concatenate([w13.codes[:, :I], pad_rows(w13.codes, zero, 1)[:, :P],
+                        w13.codes[:, I:], pad_rows(w13.codes, zero, 1)[:, :P]], axis=1)
+    s = np.concatenate([w13.scales[:, :I], pad_rows(w13.scales, _bf16(1.0), 1),
+                        w13.scales[:, I:], pad_rows(w13.scales, _bf16(1.0), 1)], axis=1)
+    w2 = lw.w2
+    c2 = np.concatenate([w2.codes, np.full((E, w2.codes.shape[1], P // 2), zero, np.uint8)], axis=2)
+    s2 = np.concatenate([w2.scales, np.full((E, w2.scales.shape[1], P // 128), _bf16(1.0), np.uint16)], axis=2)
+    lp = W.LayerWeights(NS(codes=c, scales=s, gs=None, bias=None), NS(codes=c2, scales=s2, gs=None, bias=None), None)
+    padded = _run(wl, lp, inp)
+    assert np.allclose(padded, base, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("qtype", W.QTYPES)
+def test_bf16_intermediates_stay_within_layer_tolerance(qtype):
+    wl, lw, inp = _small(qtype)
+    a = _run(wl, lw, inp, bf16_intermediates=True)
+    b = _run(wl, lw, inp, bf16_intermediates=False)
+    assert np.all(np.abs(a - b) <= 0.06 + 0.04 * np.abs(b))
+    assert np.abs(a - b).max() < 0.05 * np.abs(b).max()
+
+
+def test_intermediates_route_to_slot_rows():
+    wl, lw, inp = _small("int4_g128")
+    out, inter = _run(wl, lw, inp, return_intermediates=True)
+    loc = O.route_local(inp.topk_ids, wl.expert_start, wl.n_local).reshape(-1)
+    assert sorted(inter["y"].keys()) == [i for i in range(loc.size) if loc[i] >= 0]
+    assert all(v.shape == (wl.H,) for v in inter["y"].values())

@@ -1,0 +1,202 @@
+"""Seeded synthetic inputs for the W4A16 MoE expert layer.
+
+This module only draws random data in the canonical layouts; it holds none of
+the layer's arithmetic (no dequantisation, routing, GEMM, activation or
+combine).  Both the CPU oracle (through the tests) and the HIP path consume
+exactly the arrays produced here, so the two sides see identical bytes.
+
+Canonical layouts (shared vocabulary of every caller):
+
+* ``codes``   uint8 ``[E, N, K/2]``: two 4-bit codes per byte, the low nibble
+  holds the even K index.
+* ``scales``  ``[E, N, K/g]``: bf16 bit patterns (uint16) for int4 (g = 128),
+  float8 e4m3fn codes (uint8) for NVFP4 (g = 16), E8M0 codes (uint8) for
+  MXFP4 (g = 32).
+* ``gs``      float32 ``[E]``: NVFP4 per-expert global scale (else ``None``).
+* ``bias``    bf16 bits ``[E, N]`` or ``None``.
+* ``x``       bf16 bits ``[M, H]``; ``topk_ids`` int32 ``[M, k]`` global ids;
+  ``topk_weights`` float32 ``[M, k]``; ``norm_w`` bf16 bits ``[H]``.
+
+For the gate/up projection N = 2I with gate rows ``[0, I)`` then up rows
+``[I, 2I)``, except for the MXFP4 workload whose rows arrive interleaved
+(``gate0, up0, gate1, up1, ...``) the way GPT-OSS checkpoints store them.
+
+Workloads follow the shapes of the pages: the sglang Marlin MoE unit test
+(int4, E=8, top-2, H=512, I=1024), the Muse Spark EP8 expert slice (NVFP4,
+256 experts of which 32 are local, top-8, H=I=4096) and GPT-OSS MXFP4
+(E=128, top-4, H=I=2880).
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+QTYPES = ("int4_g128", "nvfp4_g16", "mxfp4_g32")
+GROUP = {"int4_g128": 128, "nvfp4_g16": 16, "mxfp4_g32": 32}
+
+# stream ids of the seed sequence
+_S_WEIGHTS, _S_HIDDEN, _S_ROUTING, _S_AUX = 0, 1, 2, 3
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One layer configuration; ``M`` tokens are drawn per call of make_inputs."""
+    name: str
+    qtype: str
+    n_global: int          # experts in the model
+    expert_start: int      # first local expert
+    n_local: int           # local experts [expert_start, expert_start + n_local)
+    top_k: int
+    H: int
+    I: int
+    Ms: tuple
+    bias: bool = False
+    act: str = "silu_mul"  # or "swiglu_alpha"
+    alpha: float = 1.702
+    limit: float = float("inf")
+    norm: bool = False
+    eps: float = 1e-8
+    interleaved_w13: bool = False
+    routing: str = "uniform"   # or "zipf"
+    zipf_s: float = 1.2
+    seed: int = 0              # seed id of the weights (and default input seed)
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+    @property
+    def group(self) -> int:
+        return GROUP[self.qtype]
+
+
+CONFIGS = {
+    0: Workload("int4_m123_e8_top2_h512_i1024", "int4_g128", 8, 0, 8, 2, 512, 1024,
+                (123,), seed=0),
+    1: Workload("int4_bias_m2304_e8_top2_h512_i1024", "int4_g128", 8, 0, 8, 2, 512, 1024,
+                (2304,), bias=True, seed=1),
+    2: Workload("nvfp4_ep8_slice_decode_h4096_i4096", "nvfp4_g16", 256, 0, 32, 8, 4096, 4096,
+                (1, 4, 16, 64), norm=True, seed=2),
+    3: Workload("nvfp4_ep8_slice_zipf_prefill_h4096_i4096", "nvfp4_g16", 256, 0, 32, 8, 4096, 4096,
+                (256, 1024, 4096), norm=True, routing="zipf", seed=2),
+    4: Workload("mxfp4_swiglu_e128_top4_h2880_i2880", "mxfp4_g32", 128, 0, 128, 4, 2880, 2880,
+                (1, 32, 2048), bias=True, act="swiglu_alpha", interleaved_w13=True, seed=4),
+}
+
+
+def _rng(a: int, b: int, stream: int) -> np.random.Generator:
+    return np.random.default_rng([a, b, stream])
+
+
+def _to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (torch's round-to-nearest-even cast)."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def _to_e4m3_codes(a: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().copy()
+
+
+@dataclass
+class ExpertWeights:
+    """One projection's canonical weights for the local experts."""
+    codes: np.ndarray
+    scales: np.ndarray
+    gs: Optional[np.ndarray]
+    bias: Optional[np.ndarray]
+    N: int
+    K: int
+
+
+@dataclass
+class LayerWeights:
+    w13: ExpertWeights
+    w2: ExpertWeights
+    norm_w: Optional[np.ndarray]
+
+
+@dataclass
+class LayerInputs:
+    x: np.ndarray
+    topk_ids: np.ndarray
+    topk_weights: np.ndarray
+    M: int
+
+
+def _projection(rng: np.random.Generator, wl: Workload, E: int, N: int, K: int) -> ExpertWeights:
+    g = wl.group
+    codes = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    if wl.qtype == "int4_g128":
+        scales = _to_bf16_bits(rng.uniform(0.002, 0.02, size=(E, N, K // g)).astype(np.float32))
+        gs = None
+    elif wl.qtype == "nvfp4_g16":
+        scales = _to_e4m3_codes(np.exp2(rng.uniform(4.0, 8.0, size=(E, N, K // g))).astype(np.float32))
+        gs = (4.92e-5 * rng.uniform(0.75, 1.25, size=(E,))).astype(np.float32)
+    elif wl.qtype == "mxfp4_g32":
+        scales = rng.integers(118, 122, size=(E, N, K // g), dtype=np.uint8)
+        gs = None
+    else:
+        raise ValueError(wl.qtype)
+    return ExpertWeights(codes, scales, gs, None, N, K)
+
+
+def make_weights(wl: Workload) -> LayerWeights:
+    """Canonical weights of the local experts (only these are ever passed on)."""
+    E, H, I = wl.n_local, wl.H, wl.I
+    if H % wl.group or I % wl.group:
+        raise ValueError("H and I must be multiples of the quantisation group")
+    rng = _rng(wl.seed, 0, _S_WEIGHTS)
+    w13 = _projection(rng, wl, E, 2 * I, H)
+    w2 = _projection(rng, wl, E, H, I)
+    aux = _rng(wl.seed, 0, _S_AUX)
+    if wl.bias:
+        w13.bias = _to_bf16_bits(aux.normal(0.0, 0.1, size=(E, 2 * I)).astype(np.float32))
+        w2.bias = _to_bf16_bits(aux.normal(0.0, 0.1, size=(E, H)).astype(np.float32))
+    norm_w = None
+    if wl.norm:
+        norm_w = _to_bf16_bits(aux.normal(0.0, 0.1, size=(H,)).astype(np.float32))
+    return LayerWeights(w13, w2, norm_w)
+
+
+def _distinct_topk(keys: np.ndarray, k: int) -> np.ndarray:
+    # k largest keys per row, as distinct column indices
+    return np.argsort(-keys, axis=1, kind="stable")[:, :k].astype(np.int32)
+
+
+def make_inputs(wl: Workload, M: int, seed: Optional[int] = None) -> LayerInputs:
+    s = wl.seed if seed is None else seed
+    hid = _rng(s, M, _S_HIDDEN)
+    x = _to_bf16_bits(hid.standard_normal((M, wl.H), dtype=np.float32))
+    r = _rng(s, M, _S_ROUTING)
+    E = wl.n_global
+    if wl.routing == "uniform":
+        keys = r.random((M, E))
+    elif wl.routing == "zipf":
+        # Gumbel-top-k: k distinct draws without replacement with P(e) ~ (e+1)^-s
+        logp = -wl.zipf_s * np.log(np.arange(1, E + 1, dtype=np.float64))
+        keys = logp[None, :] + r.gumbel(size=(M, E))
+    else:
+        raise ValueError(wl.routing)
+    ids = _distinct_topk(keys, wl.top_k)
+    logits = r.standard_normal((M, wl.top_k))
+    w = np.exp(logits - logits.max(axis=1, keepdims=True))
+    w = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+    return LayerInputs(x, ids, w, M)
+
+
+def small_workload(qtype: str, **kw) -> Workload:
+    """Reduced shapes that the oracle finishes in well under a second while the
+    GPU kernels still see several tiles and ragged tails."""
+    base = {
+        "int4_g128": Workload("int4_small", "int4_g128", 8, 0, 8, 2, 512, 384, (37,), seed=100),
+        "nvfp4_g16": Workload("nvfp4_small", "nvfp4_g16", 64, 8, 16, 8, 512, 320, (29,),
+                              norm=True, seed=101),
+        "mxfp4_g32": Workload("mxfp4_small", "mxfp4_g32", 16, 0, 16, 4, 448, 320, (41,),
+                              bias=True, act="swiglu_alpha", interleaved_w13=True, seed=102),
+    }[qtype]
+    return base.replace(**kw) if kw else base
