@@ -1,0 +1,238 @@
+/*
+ * moe_w4a16.h -- C ABI of the MI355X (gfx950) W4A16 mixture-of-experts expert layer.
+ *
+ * The layer, for one GPU's slice of experts [expert_start, expert_start + n_local):
+ *
+ *   moe_align        route the top-k (token, slot) assignments to local experts and
+ *                    sort them into per-expert blocks of block_m rows
+ *   moe_w4a16_gemm   gate/up projection: h[slot] = dequant(W13[e]) x[slot / top_k] (+ b13[e])
+ *   moe_act          a = silu(gate) * up, or GPT-OSS gate * sigmoid(alpha * gate) * (up + 1)
+ *   moe_w4a16_gemm   down projection:    y[slot] = dequant(W2[e]) a[slot] (+ b2[e])
+ *   moe_combine      out[t] = sum over live slots of g * y, optionally after the
+ *                    weight-first post-expert RMSNorm with weight bf16(1 + w)
+ *
+ * Sources.  The steps and their arguments follow the pages the method is described on:
+ * the Muse Spark NVFP4 experiment "013-moe-middle-tiles.py" (bishal.us open-kernel-challenge):
+ * Inputs / Weights / Config, prepare and kernel_fn (expert_map, moe_align_block_size, two
+ * moe_wna16_marlin_gemm calls, silu_and_mul, _expert_norm_factors / _expert_norm_sum); the
+ * "sglang PR 31552" summary (Marlin MoE W4A16: kIsEP / kHasBias, the per-expert reference loop
+ * with biases); the "sglang PR 28231" summary (MXFP4 on Marlin: gate/up de-interleave, tile
+ * padding, swiglu_gpt_oss_sigmoid_alpha_contiguous).
+ *
+ * Conventions (every function):
+ *   - Pointers marked "device" are device memory owned by the caller; host structs and sizes
+ *     are passed by value or by host pointer.  Nothing is allocated or freed, nothing is
+ *     synchronised: work is enqueued on `stream` (0 = the null stream) and returns at once.
+ *   - bf16 tensors are passed as uint16_t bit patterns, row-major, rows contiguous unless a
+ *     leading dimension is given.
+ *   - Return 0 (MOE_OK) or a negative moe_status.  Arguments are validated on the host before
+ *     anything is launched; on error nothing is launched and moe_last_error() describes why.
+ *   - Device data is never trusted to be in range: expert ids outside the local range are
+ *     dropped, sorted ids at or past `numel` are padding and are skipped.
+ *   - Calls are thread-safe (no global mutable state besides the thread-local error text).
+ */
+#ifndef MOE_W4A16_H
+#define MOE_W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,        /* bad argument: null pointer, negative or inconsistent size */
+  MOE_EUNSUPPORTED = -2,  /* valid but not implemented (shape not a tile multiple, ...) */
+  MOE_ESIZE = -3,         /* caller buffer too small */
+  MOE_EHIP = -4           /* a HIP runtime call failed (launch error, no device) */
+} moe_status;
+
+typedef enum {
+  MOE_Q_INT4_G128 = 0,    /* uint4b8: nibble u means u - 8; bf16 scale per 128 along K       */
+  MOE_Q_NVFP4_G16 = 1,    /* E2M1 codes; float8 e4m3fn scale per 16 along K; fp32 global/expert */
+  MOE_Q_MXFP4_G32 = 2     /* E2M1 codes; E8M0 scale per 32 along K                            */
+} moe_qtype;
+
+typedef enum {
+  MOE_ACT_SILU_MUL = 0,      /* silu(gate) * up                                     */
+  MOE_ACT_SWIGLU_ALPHA = 1   /* min(g,L) * sigmoid(alpha * min(g,L)) * (clamp(u,-L,L) + 1) */
+} moe_act_kind;
+
+/* ----------------------------------------------------------------------------- errors */
+
+/* Text of the last non-zero return on the calling thread ("" if none).  Owned by the library. */
+const char* moe_last_error(void);
+
+/* Library ABI version (incremented on any incompatible change). */
+int32_t moe_abi_version(void);
+
+/* ----------------------------------------------------------------------------- align */
+
+/*
+ * Sizes of the align outputs for M tokens with top_k slots each:
+ *   *sorted_len = number of int32 entries of sorted_token_ids,
+ *   *blocks_len = number of int32 entries of expert_ids = *sorted_len / block_m.
+ * At most min(n_local, M*top_k) experts are non-empty and each pads by at most block_m - 1,
+ * so the padded total never exceeds numel + min(n_local, numel) * (block_m - 1); rounded up
+ * to whole blocks.  Pure host function.
+ */
+int moe_align_capacity(int64_t M, int32_t top_k, int32_t n_local, int32_t block_m,
+                       int64_t* sorted_len, int64_t* blocks_len);
+
+/*
+ * Route and align (the experiment's expert_map gather + moe_align_block_size).
+ *   topk_ids          device int32 [M, top_k], global expert ids
+ *   expert_start,
+ *   n_local           local experts are [expert_start, expert_start + n_local); 1..512
+ *   block_m           rows per block, 1..256
+ * Outputs (device, caller-allocated with moe_align_capacity sizes):
+ *   sorted_token_ids  int32 [sorted_len] (may be NULL when sorted_len is 0): expert 0's flat slot ids t*top_k+s in ascending order,
+ *                     padded with the sentinel numel = M*top_k to a multiple of block_m, then
+ *                     expert 1's, ...; empty experts get no block; the rest is the sentinel.
+ *   expert_ids        int32 [blocks_len]: local expert of each block, -1 after the last block.
+ *   num_tokens_post_padded  int32 [1]: total padded length (a multiple of block_m).
+ *   slot_local_ids    int32 [M, top_k] or NULL: local expert of each slot, -1 when the
+ *                     assignment is outside the local range (dropped).
+ * The result is unique (a stable counting sort), computed by one workgroup without atomics
+ * deciding the order.
+ */
+int moe_align(const int32_t* topk_ids, int64_t M, int32_t top_k, int32_t expert_start,
+              int32_t n_local, int32_t block_m, int32_t* sorted_token_ids, int32_t* expert_ids,
+              int32_t* num_tokens_post_padded, int32_t* slot_local_ids, hipStream_t stream);
+
+/* ----------------------------------------------------------------------------- weights */
+
+/* prepare flags */
+#define MOE_PREP_GATE_UP      0x1u  /* rows are a gate/up pair: N = 2I, gate rows [0, I), up [I, 2I) */
+#define MOE_PREP_INTERLEAVED  0x2u  /* with GATE_UP: rows arrive as gate0, up0, gate1, up1, ...   */
+#define MOE_PREP_PAD          0x4u  /* zero-pad K (and with GATE_UP each half of N) to a multiple of 64 */
+
+/* Prepared (device-resident) weights of one projection, filled by moe_w4a16_prepare.  Plain
+ * data: it may be copied; the pointers are into the caller's `out` buffer. */
+typedef struct moe_weights {
+  int32_t qtype;          /* moe_qtype */
+  int32_t n_experts;      /* E */
+  int32_t N;              /* output rows per expert in the prepared layout (padded)   */
+  int32_t K;              /* reduction length in the prepared layout (padded)         */
+  int32_t N_logical;      /* rows as given (2I for a gate/up pair)                     */
+  int32_t K_logical;
+  uint32_t flags;         /* the MOE_PREP_* flags used                                 */
+  int32_t reserved;
+  const void* codes;      /* tiled 4-bit codes                                         */
+  const void* scales;     /* tiled group scales                                        */
+  const float* global_scale; /* [E] NVFP4 per-expert scale, else NULL                  */
+  const uint16_t* bias;   /* bf16 [E, N] or NULL                                       */
+} moe_weights;
+
+/* Prepared dimensions and the number of bytes moe_w4a16_prepare writes.  Pure host function.
+ * Requirements: N % 16 == 0 (N % 32 with GATE_UP) and K % 64 == 0 unless MOE_PREP_PAD is set;
+ * K % group == 0 always (group 128 / 16 / 32 by qtype). */
+int moe_w4a16_prepared_size(moe_qtype q, int32_t E, int32_t N, int32_t K, uint32_t flags,
+                            int32_t has_bias, int32_t* N_out, int32_t* K_out, size_t* bytes);
+
+/*
+ * Load-time repack (the experiment's prepare / prepare_moe_nvfp4_layer_for_marlin step, and
+ * for GPT-OSS the de-interleave and tile padding of sglang PR 28231).  Untimed.
+ *   codes         device uint8 [E, N, K/2], two codes per byte, low nibble = even k
+ *   scales        device [E, N, K/g]: bf16 bits (int4), e4m3fn codes (NVFP4), E8M0 codes (MXFP4)
+ *   global_scale  device fp32 [E] (NVFP4 only, else NULL)
+ *   bias          device bf16 [E, N] or NULL (interleaved like the rows when INTERLEAVED)
+ *   out           device buffer of at least `bytes` from moe_w4a16_prepared_size, 256-B aligned
+ *   desc          host struct filled with the prepared dims and device pointers into `out`
+ * Padded rows/columns get zero codes, unit scales and zero bias, which leaves the layer's
+ * result unchanged (act(0, 0) = 0 for both activations).
+ */
+int moe_w4a16_prepare(moe_qtype q, const uint8_t* codes, const void* scales,
+                      const float* global_scale, const uint16_t* bias, int32_t E, int32_t N,
+                      int32_t K, uint32_t flags, void* out, size_t out_bytes, moe_weights* desc,
+                      hipStream_t stream);
+
+/* The post-expert norm's effective weight: out[h] = bf16(1 + w[h]) (round to nearest even),
+ * as the experiment's prepare binds it once.  w, out: device bf16 [H]. */
+int moe_norm_weight(const uint16_t* w, int32_t H, uint16_t* out, hipStream_t stream);
+
+/* ----------------------------------------------------------------------------- GEMM */
+
+typedef enum {
+  MOE_GEMM_AUTO = 0,
+  MOE_GEMM_DECODE = 1,    /* block_m <= 16: 16-row weight tiles, K split over waves,
+                             dot-product (GEMV) or one MFMA column of 16 rows per block  */
+  MOE_GEMM_MFMA = 2       /* block_m in {16,32,64,128}: bf16 MFMA 16x16x32 tiles           */
+} moe_gemm_kernel;
+
+/* Launch configuration.  Any valid configuration gives the same result bit for bit for a given
+ * kernel (the K order of every output is fixed); AUTO picks one from the shapes. */
+typedef struct moe_gemm_config {
+  int32_t kernel;         /* moe_gemm_kernel                                               */
+  int32_t ng;             /* MFMA: 16-row n-tiles per wave: 1, 2 or 4 (4 waves per group)  */
+  int32_t ksplit;         /* DECODE: waves splitting K in one workgroup: 1, 2 or 4         */
+  int32_t gemv_rows;      /* DECODE: blocks with at most this many live rows use the
+                             dot-product path (0..4), others the MFMA column              */
+} moe_gemm_config;
+
+/* Host heuristic: block_m for the align and the GEMM configuration for a problem of `numel`
+ * slots over `n_local` experts with projection (N, K).  Pure host function. */
+int moe_choose_block_m(int64_t numel, int32_t n_local, int32_t* block_m);
+int moe_gemm_choose(const moe_weights* W, int64_t numel, int32_t block_m, int32_t num_cus,
+                    moe_gemm_config* cfg);
+
+/*
+ * Grouped W4A16 GEMM over the align blocks (moe_wna16_marlin_gemm with mul_topk_weights=False,
+ * fp32 accumulation).  For every sorted entry s < numel of block b (expert e = expert_ids[b]):
+ *     C[s, n] = bf16( gs[e] * sum_k dequant(W[e])[n, k] * A[s / top_k, k]  (+ bias[e, n]) )
+ *   A        device bf16 [a_rows, lda], K = W->K columns read (columns >= K_logical of the
+ *            padded part must be zero or finite: their weights are zero)
+ *   C        device bf16 [numel, ldc]; only rows of live slots are written, N = W->N columns
+ *   sorted_token_ids, expert_ids, num_tokens_post_padded: moe_align outputs for
+ *            n_local = W->n_experts and this block_m; `numel` = M * top_k of that align
+ *   top_k    A row of entry s is s / top_k (the token); 1 for the down projection
+ *   cfg      NULL for AUTO
+ * Dequantised weights are rounded to bf16 before the bf16 x bf16 MFMA products (exact for
+ * NVFP4 and MXFP4; int4 (u-8)*s is rounded like the Marlin kernel does).
+ */
+int moe_w4a16_gemm(const uint16_t* A, int64_t a_rows, int32_t lda, uint16_t* C, int32_t ldc,
+                   const moe_weights* W, const int32_t* sorted_token_ids,
+                   const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                   int64_t numel, int32_t top_k, int32_t block_m, const moe_gemm_config* cfg,
+                   hipStream_t stream);
+
+/* ----------------------------------------------------------------------------- act */
+
+/*
+ * Gated activation over rows of the GEMM1 output (silu_and_mul of the experiment; GPT-OSS
+ * swiglu_gpt_oss_sigmoid_alpha_contiguous of sglang PR 28231):
+ *   in   device bf16 [R, ld_in]: gate = columns [0, I), up = [I, 2I)
+ *   out  device bf16 [R, ld_out]: I columns
+ *   slot_local_ids  device int32 [R] or NULL: rows whose id is < 0 are skipped (not written)
+ *   alpha, limit    SWIGLU_ALPHA only; limit = +inf disables the clamps
+ * Computed in fp32 from the bf16 inputs, rounded to bf16 once.
+ */
+int moe_act(moe_act_kind kind, const uint16_t* in, int32_t ld_in, uint16_t* out, int32_t ld_out,
+            int64_t R, int32_t I, const int32_t* slot_local_ids, float alpha, float limit,
+            hipStream_t stream);
+
+/* ----------------------------------------------------------------------------- combine */
+
+/*
+ * Top-k weighted combine, optionally after the weight-first post-expert RMSNorm
+ * (_expert_norm_factors + _expert_norm_sum of the experiment):
+ *   y               device bf16 [M * top_k, H]: GEMM2 output, row t*top_k+s
+ *   topk_weights    device fp32 [M, top_k]
+ *   slot_local_ids  device int32 [M, top_k]: slots with id < 0 are dead and contribute 0
+ *                   (their y rows are never read)
+ *   norm_w          device bf16 [H] = bf16(1 + w) (moe_norm_weight), or NULL for no norm
+ *   out             device bf16 [M, H], every row written (zeros for tokens with no live slot)
+ * With norm: z = y * norm_w, factor = g / sqrt(sum(z^2) / H + eps), out = sum factor * z.
+ * Without:   out = sum g * y.   fp32 accumulation, one bf16 rounding at the end.
+ */
+int moe_combine(const uint16_t* y, const float* topk_weights, const int32_t* slot_local_ids,
+                const uint16_t* norm_w, float eps, int64_t M, int32_t top_k, int32_t H,
+                uint16_t* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_W4A16_H */

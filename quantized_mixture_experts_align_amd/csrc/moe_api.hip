@@ -1,0 +1,130 @@
+// Host-side parts of the C ABI: error text, size queries and launch heuristics.
+#include <algorithm>
+#include <cstring>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static thread_local char g_err[512];
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return MOE_OK;
+}
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" const char* moe_last_error(void) { return g_err; }
+
+extern "C" int32_t moe_abi_version(void) { return 1; }
+
+extern "C" int moe_align_capacity(int64_t M, int32_t top_k, int32_t n_local, int32_t block_m,
+                                  int64_t* sorted_len, int64_t* blocks_len) {
+  MOE_REQUIRE(sorted_len && blocks_len, MOE_EINVAL, "moe_align_capacity: null output pointer");
+  MOE_REQUIRE(M >= 0 && top_k >= 1 && n_local >= 1 && block_m >= 1, MOE_EINVAL,
+              "moe_align_capacity: M=%lld top_k=%d n_local=%d block_m=%d out of range",
+              (long long)M, top_k, n_local, block_m);
+  const int64_t numel = M * top_k;
+  const int64_t worst = numel + std::min<int64_t>(n_local, numel) * (block_m - 1);
+  const int64_t blocks = (worst + block_m - 1) / block_m;
+  *sorted_len = blocks * block_m;
+  *blocks_len = blocks;
+  return ok();
+}
+
+extern "C" int moe_w4a16_prepared_size(moe_qtype q, int32_t E, int32_t N, int32_t K, uint32_t flags,
+                                       int32_t has_bias, int32_t* N_out, int32_t* K_out,
+                                       size_t* bytes) {
+  MOE_REQUIRE(q == MOE_Q_INT4_G128 || q == MOE_Q_NVFP4_G16 || q == MOE_Q_MXFP4_G32, MOE_EINVAL,
+              "unknown qtype %d", (int)q);
+  MOE_REQUIRE(E >= 1 && N >= 1 && K >= 1, MOE_EINVAL, "E=%d N=%d K=%d must be positive", E, N, K);
+  MOE_REQUIRE((flags & ~(MOE_PREP_GATE_UP | MOE_PREP_INTERLEAVED | MOE_PREP_PAD)) == 0, MOE_EINVAL,
+              "unknown prepare flags 0x%x", flags);
+  MOE_REQUIRE(!(flags & MOE_PREP_INTERLEAVED) || (flags & MOE_PREP_GATE_UP), MOE_EINVAL,
+              "MOE_PREP_INTERLEAVED needs MOE_PREP_GATE_UP");
+  const int g = group_of(q);
+  MOE_REQUIRE(K % g == 0, MOE_EUNSUPPORTED, "K=%d is not a multiple of the group size %d", K, g);
+  const bool pad = flags & MOE_PREP_PAD;
+  int nout = N, kout = K;
+  if (flags & MOE_PREP_GATE_UP) {
+    MOE_REQUIRE(N % 2 == 0, MOE_EINVAL, "gate/up rows: N=%d must be even", N);
+    const int I = N / 2;
+    const int Ip = pad ? (I + kTileK - 1) / kTileK * kTileK : I;
+    MOE_REQUIRE(Ip % kTileN == 0, MOE_EUNSUPPORTED,
+                "gate/up halves of %d rows are not a multiple of %d (use MOE_PREP_PAD)", I, kTileN);
+    nout = 2 * Ip;
+  } else {
+    MOE_REQUIRE(N % kTileN == 0, MOE_EUNSUPPORTED, "N=%d is not a multiple of %d", N, kTileN);
+  }
+  if (pad) kout = (K + kTileK - 1) / kTileK * kTileK;
+  MOE_REQUIRE(kout % kTileK == 0, MOE_EUNSUPPORTED,
+              "K=%d is not a multiple of %d (use MOE_PREP_PAD)", K, kTileK);
+  if (q == MOE_Q_INT4_G128)
+    MOE_REQUIRE(kout % 128 == 0, MOE_EUNSUPPORTED, "int4: K=%d must be a multiple of 128", kout);
+  const size_t tiles = (size_t)E * (nout / kTileN) * (kout / kTileK);
+  size_t total = align256(tiles * kTileBytes);
+  total += align256(tiles * (size_t)scale_bytes_per_tile(q));
+  if (q == MOE_Q_NVFP4_G16) total += align256((size_t)E * 4);
+  if (has_bias) total += align256((size_t)E * nout * 2);
+  if (N_out) *N_out = nout;
+  if (K_out) *K_out = kout;
+  if (bytes) *bytes = total;
+  return ok();
+}
+
+// BLOCK_SIZE_M for the align.  The Muse Spark experiment picks from (8, 16, 32, 48, 64) by the
+// expected rows per expert; here the choice also selects the kernel: up to 16 expected rows per
+// local expert go to the decode kernel (one 16-row block), larger counts to MFMA tiles of
+// 32/64/128 rows so that the padding of the last block of each expert stays a small fraction.
+extern "C" int moe_choose_block_m(int64_t numel, int32_t n_local, int32_t* block_m) {
+  MOE_REQUIRE(block_m && numel >= 0 && n_local >= 1, MOE_EINVAL, "moe_choose_block_m: bad arguments");
+  const double rows = (double)numel / n_local;
+  int b = 16;
+  if (rows > 16) b = 32;
+  if (rows > 48) b = 64;
+  if (rows > 160) b = 128;
+  *block_m = b;
+  return ok();
+}
+
+extern "C" int moe_gemm_choose(const moe_weights* W, int64_t numel, int32_t block_m, int32_t num_cus,
+                               moe_gemm_config* cfg) {
+  MOE_REQUIRE(W && cfg, MOE_EINVAL, "moe_gemm_choose: null pointer");
+  MOE_REQUIRE(block_m >= 1 && numel >= 0, MOE_EINVAL, "moe_gemm_choose: bad block_m/numel");
+  if (num_cus <= 0) num_cus = 256;
+  moe_gemm_config c{};
+  const int nt = W->N / kTileN;
+  if (block_m <= 16) {
+    c.kernel = MOE_GEMM_DECODE;
+    c.gemv_rows = 4;
+    // enough waves to keep every CU streaming: split K when there are few n-tiles x blocks
+    const int64_t blocks = std::min<int64_t>(std::max<int64_t>(numel, 1), W->n_experts);
+    const int64_t groups = (int64_t)nt * blocks;
+    const int kt = W->K / kTileK;
+    c.ksplit = (groups >= 8 * num_cus || kt < 8) ? 1 : (groups >= 2 * num_cus || kt < 16 ? 2 : 4);
+  } else {
+    c.kernel = MOE_GEMM_MFMA;
+    const int64_t mblocks = numel / block_m + std::min<int64_t>(numel, W->n_experts);
+    c.ng = 4;
+    while (c.ng > 1 && ((int64_t)(nt + 4 * c.ng - 1) / (4 * c.ng)) * mblocks < 2 * num_cus) c.ng /= 2;
+  }
+  *cfg = c;
+  return ok();
+}

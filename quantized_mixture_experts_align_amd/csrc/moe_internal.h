@@ -1,0 +1,63 @@
+// Internal helpers shared by the HIP sources of libmoe_w4a16 (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cstdarg>
+#include <cstdio>
+
+#include "moe_w4a16.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------- errors
+// Sets the thread-local error text and returns `code` (negative moe_status).
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int ok();  // clears the error text, returns MOE_OK
+int check_launch(const char* what);  // MOE_EHIP with text if the last launch failed
+
+#define MOE_REQUIRE(cond, code, ...) \
+  do {                               \
+    if (!(cond)) return ::moe::fail(code, __VA_ARGS__); \
+  } while (0)
+
+// ---------------------------------------------------------------------------- tiled layout
+// A weight tile is 16 output rows x 64 reduction columns of one expert: 512 bytes of codes.
+// Lane l (0..63) of a wave owns 8 bytes at offset 8*l: two dwords, dword i holding the eight
+// codes of row (l % 16), k = 32*i + 8*(l / 16) + 0..7 (low nibble = even k).  That is exactly
+// the A operand of v_mfma_f32_16x16x32_bf16 for k-steps i = 0, 1 (row = output feature), and a
+// contiguous 512-byte read for the whole wave.
+constexpr int kTileN = 16;
+constexpr int kTileK = 64;
+constexpr int kTileBytes = kTileN * kTileK / 2;
+
+inline __host__ __device__ int group_of(int q) { return q == MOE_Q_INT4_G128 ? 128 : (q == MOE_Q_NVFP4_G16 ? 16 : 32); }
+
+// Scale bytes per (16-row x 64-column) tile.  NVFP4: 16 rows x 4 e4m3 codes; MXFP4: 16 rows x
+// 2 E8M0 codes; int4: the group of 128 spans two tiles, stored per tile pair as 16 bf16.
+inline __host__ __device__ int scale_bytes_per_tile(int q) {
+  return q == MOE_Q_NVFP4_G16 ? 64 : (q == MOE_Q_MXFP4_G32 ? 32 : 16);
+}
+
+inline __host__ __device__ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------------------- device math
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return (uint16_t)(__builtin_bit_cast(uint16_t, (__bf16)f));
+}
+
+}  // namespace moe

@@ -1,0 +1,163 @@
+// Load-time weight repack into the tiled gfx950 layout (untimed; the Muse Spark experiment's
+// prepare step, and for GPT-OSS checkpoints the gate/up de-interleave and the zero-padding of
+// the intermediate dimension described in the "sglang PR 28231" summary).
+//
+// Prepared buffer, each section 256-byte aligned:
+//   codes   [E][N/16][K/64] tiles of 512 bytes; lane l's 8 bytes = dword i (i = 0, 1) holding the
+//           eight codes of row l%16 at k = 32 i + 8 (l/16) + 0..7, low nibble = even k
+//   scales  NVFP4: [E][N/16][K/64][16 rows][4 e4m3]   (the four groups of 16 of the tile)
+//           MXFP4: [E][N/16][K/64][16 rows][2 E8M0]   (the two groups of 32)
+//           int4:  [E][N/16][K/128][16 rows] bf16      (one group of 128 per tile pair)
+//   gs      fp32 [E]                 (NVFP4)
+//   bias    bf16 [E][N]              (optional)
+// Output row n of a gate/up pair: gate j = n for n < I_pad, up j = n - I_pad otherwise; source
+// row j (contiguous halves) or 2j / 2j+1 (interleaved).  Rows j >= I and columns k >= K are
+// padding: zero codes, unit scales, zero bias.
+#include "moe_internal.h"
+
+namespace moe {
+
+struct PrepGeom {
+  int q, E, N, K, Nout, Kout, I, Ip;
+  uint32_t flags;
+};
+
+// source row of output row n, or -1 for a padding row
+__device__ __forceinline__ int src_row(const PrepGeom& g, int n) {
+  if (!(g.flags & MOE_PREP_GATE_UP)) return n;
+  const int half = n >= g.Ip, j = n - half * g.Ip;
+  if (j >= g.I) return -1;
+  return (g.flags & MOE_PREP_INTERLEAVED) ? 2 * j + half : half * g.I + j;
+}
+
+// one thread per output dword of codes
+__global__ void prep_codes_kernel(const uint8_t* __restrict__ src, uint32_t* __restrict__ dst, PrepGeom g) {
+  const int NT = g.Nout / kTileN, KT = g.Kout / kTileK;
+  const int64_t total = (int64_t)g.E * NT * KT * 128;
+  const uint32_t zero = g.q == MOE_Q_INT4_G128 ? 0x88888888u : 0u;
+  for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < total;
+       d += (int64_t)gridDim.x * blockDim.x) {
+    const int i = (int)(d & 1), lane = (int)((d >> 1) & 63);
+    const int64_t tile = d >> 7;
+    const int kt = (int)(tile % KT);
+    const int64_t et = tile / KT;
+    const int nt = (int)(et % NT), e = (int)(et / NT);
+    const int n = nt * kTileN + (lane & 15);
+    const int k = kt * kTileK + 32 * i + 8 * (lane >> 4);
+    const int r = src_row(g, n);
+    uint32_t v = zero;
+    if (r >= 0 && k < g.K) {
+      const uint8_t* p = src + ((int64_t)e * g.N + r) * (g.K / 2) + k / 2;
+      v = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+    }
+    dst[d] = v;
+  }
+}
+
+// one thread per output scale element
+__global__ void prep_scales_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, PrepGeom g) {
+  const int NT = g.Nout / kTileN, KT = g.Kout / kTileK;
+  const int grp = group_of(g.q);
+  const int ngroups = g.K / grp;  // groups per source row
+  if (g.q == MOE_Q_INT4_G128) {
+    const uint16_t* s16 = reinterpret_cast<const uint16_t*>(src);
+    uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);
+    const int64_t total = (int64_t)g.E * NT * (KT / 2) * 16;
+    for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < total;
+         d += (int64_t)gridDim.x * blockDim.x) {
+      const int row = (int)(d & 15);
+      const int64_t t = d >> 4;
+      const int kp = (int)(t % (KT / 2));
+      const int64_t et = t / (KT / 2);
+      const int nt = (int)(et % NT), e = (int)(et / NT);
+      const int r = src_row(g, nt * kTileN + row);
+      d16[d] = (r >= 0 && kp < ngroups) ? s16[((int64_t)e * g.N + r) * ngroups + kp] : (uint16_t)0x3F80;
+    }
+    return;
+  }
+  const int per_row = kTileK / grp;  // 4 (NVFP4) or 2 (MXFP4)
+  const uint8_t unit = g.q == MOE_Q_NVFP4_G16 ? 0x38 : 127;  // 1.0 in e4m3fn / E8M0
+  const int64_t total = (int64_t)g.E * NT * KT * 16 * per_row;
+  for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < total;
+       d += (int64_t)gridDim.x * blockDim.x) {
+    const int j = (int)(d % per_row);
+    const int64_t t = d / per_row;
+    const int row = (int)(t & 15);
+    const int64_t tile = t >> 4;
+    const int kt = (int)(tile % KT);
+    const int64_t et = tile / KT;
+    const int nt = (int)(et % NT), e = (int)(et / NT);
+    const int r = src_row(g, nt * kTileN + row);
+    const int gi = kt * per_row + j;
+    dst[d] = (r >= 0 && gi < ngroups) ? src[((int64_t)e * g.N + r) * ngroups + gi] : unit;
+  }
+}
+
+__global__ void prep_bias_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, PrepGeom g) {
+  const int64_t total = (int64_t)g.E * g.Nout;
+  for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < total;
+       d += (int64_t)gridDim.x * blockDim.x) {
+    const int n = (int)(d % g.Nout), e = (int)(d / g.Nout);
+    const int r = src_row(g, n);
+    dst[d] = r >= 0 ? src[(int64_t)e * g.N + r] : (uint16_t)0;
+  }
+}
+
+static int grid_for(int64_t n) { return (int)std::min<int64_t>((n + 255) / 256, 16384); }
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_w4a16_prepare(moe_qtype q, const uint8_t* codes, const void* scales,
+                                 const float* global_scale, const uint16_t* bias, int32_t E,
+                                 int32_t N, int32_t K, uint32_t flags, void* out, size_t out_bytes,
+                                 moe_weights* desc, hipStream_t stream) {
+  int32_t Nout = 0, Kout = 0;
+  size_t need = 0;
+  int rc = moe_w4a16_prepared_size(q, E, N, K, flags, bias != nullptr, &Nout, &Kout, &need);
+  if (rc) return rc;
+  MOE_REQUIRE(codes && scales && out && desc, MOE_EINVAL, "moe_w4a16_prepare: null pointer");
+  MOE_REQUIRE((q == MOE_Q_NVFP4_G16) == (global_scale != nullptr), MOE_EINVAL,
+              "moe_w4a16_prepare: a global scale is required for NVFP4 and only for NVFP4");
+  MOE_REQUIRE(out_bytes >= need, MOE_ESIZE, "moe_w4a16_prepare: out has %zu bytes, %zu needed",
+              out_bytes, need);
+  MOE_REQUIRE(((uintptr_t)out & 255) == 0, MOE_EINVAL, "moe_w4a16_prepare: out must be 256-byte aligned");
+  PrepGeom g{(int)q, E, N, K, Nout, Kout, (flags & MOE_PREP_GATE_UP) ? N / 2 : N,
+             (flags & MOE_PREP_GATE_UP) ? Nout / 2 : Nout, flags};
+  const size_t tiles = (size_t)E * (Nout / kTileN) * (Kout / kTileK);
+  uint8_t* base = static_cast<uint8_t*>(out);
+  uint8_t* p_codes = base;
+  uint8_t* p_scales = p_codes + align256(tiles * kTileBytes);
+  uint8_t* p_gs = p_scales + align256(tiles * (size_t)scale_bytes_per_tile(q));
+  uint8_t* p_bias = p_gs + (q == MOE_Q_NVFP4_G16 ? align256((size_t)E * 4) : 0);
+
+  hipLaunchKernelGGL(prep_codes_kernel, dim3(grid_for((int64_t)tiles * 128)), dim3(256), 0, stream,
+                     codes, reinterpret_cast<uint32_t*>(p_codes), g);
+  hipLaunchKernelGGL(prep_scales_kernel, dim3(grid_for((int64_t)tiles * 64)), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(scales), p_scales, g);
+  if (q == MOE_Q_NVFP4_G16) {
+    hipError_t e = hipMemcpyAsync(p_gs, global_scale, (size_t)E * 4, hipMemcpyDeviceToDevice, stream);
+    MOE_REQUIRE(e == hipSuccess, MOE_EHIP, "moe_w4a16_prepare: copy of the global scales: %s",
+                hipGetErrorString(e));
+  }
+  if (bias)
+    hipLaunchKernelGGL(prep_bias_kernel, dim3(grid_for((int64_t)E * Nout)), dim3(256), 0, stream,
+                       bias, reinterpret_cast<uint16_t*>(p_bias), g);
+  rc = check_launch("moe_w4a16_prepare");
+  if (rc) return rc;
+  moe_weights d{};
+  d.qtype = q;
+  d.n_experts = E;
+  d.N = Nout;
+  d.K = Kout;
+  d.N_logical = N;
+  d.K_logical = K;
+  d.flags = flags;
+  d.codes = p_codes;
+  d.scales = p_scales;
+  d.global_scale = q == MOE_Q_NVFP4_G16 ? reinterpret_cast<const float*>(p_gs) : nullptr;
+  d.bias = bias ? reinterpret_cast<const uint16_t*>(p_bias) : nullptr;
+  *desc = d;
+  return ok();
+}

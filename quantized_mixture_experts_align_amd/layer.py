@@ -1,0 +1,94 @@
+"""The expert layer as the five C-ABI calls: align -> GEMM1 -> act -> GEMM2 -> combine.
+
+Everything runs on torch's current stream without host synchronisation, so a forward can be
+captured in a HIP graph when a Workspace is passed (no allocation inside).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+from . import ops
+
+
+@dataclass
+class Workspace:
+    """Buffers of one forward for M tokens.  The GEMM1 output h [numel, 2I] and the GEMM2
+    output y [numel, H] share one allocation (h is dead once the activation has run), the
+    same plan as the experiment's cache13."""
+    M: int
+    block_m: int
+    sorted_ids: torch.Tensor
+    expert_ids: torch.Tensor
+    ntpp: torch.Tensor
+    slot_local: torch.Tensor
+    buf13: torch.Tensor
+    a: torch.Tensor
+    out: torch.Tensor
+
+
+class MoELayer:
+    """One GPU's slice of a W4A16 MoE expert layer (experts [expert_start, expert_start + n_local)).
+
+    ``w13`` / ``w2``: dicts of device tensors in the canonical layouts: ``codes`` uint8
+    [E, N, K/2], ``scales`` [E, N, K/g], optional ``gs`` fp32 [E] (NVFP4) and ``bias`` bf16 [E, N].
+    """
+
+    def __init__(self, qtype: str, w13: dict, w2: dict, *, expert_start: int, n_local: int,
+                 top_k: int, act: str = "silu_mul", alpha: float = 1.702,
+                 limit: float = float("inf"), post_norm_w: Optional[torch.Tensor] = None,
+                 eps: float = 1e-8, interleaved_w13: bool = False, pad: bool = False):
+        self.qtype, self.expert_start, self.n_local, self.top_k = qtype, expert_start, n_local, top_k
+        self.act, self.alpha, self.limit, self.eps = act, alpha, limit, eps
+        f13 = L.PREP_GATE_UP | (L.PREP_INTERLEAVED if interleaved_w13 else 0) | (L.PREP_PAD if pad else 0)
+        f2 = L.PREP_PAD if pad else 0
+        self.W13 = ops.moe_w4a16_prepare(qtype, w13["codes"], w13["scales"], w13.get("gs"),
+                                         w13.get("bias"), f13)
+        self.W2 = ops.moe_w4a16_prepare(qtype, w2["codes"], w2["scales"], w2.get("gs"),
+                                        w2.get("bias"), f2)
+        if self.W2.K != self.W13.N // 2:
+            raise ValueError(f"down projection K={self.W2.K} != intermediate {self.W13.N // 2}")
+        if self.W2.n_experts != n_local or self.W13.n_experts != n_local:
+            raise ValueError("weights must hold exactly the n_local local experts")
+        self.I = self.W13.N // 2
+        self.H = self.W2.N
+        self.norm_w = None if post_norm_w is None else ops.moe_norm_weight(post_norm_w)
+
+    def block_m(self, M: int) -> int:
+        return ops.choose_block_m(M * self.top_k, self.n_local)
+
+    def workspace(self, M: int, block_m: Optional[int] = None, device=None) -> Workspace:
+        device = device or self.W13.buffer.device
+        B = block_m or self.block_m(M)
+        s_len, b_len = ops.align_capacity(M, self.top_k, self.n_local, B)
+        numel = M * self.top_k
+        i32 = dict(dtype=torch.int32, device=device)
+        bf = dict(dtype=torch.bfloat16, device=device)
+        return Workspace(M, B, torch.empty(s_len, **i32), torch.empty(b_len, **i32),
+                         torch.empty(1, **i32), torch.empty((M, self.top_k), **i32),
+                         torch.empty(numel * max(2 * self.I, self.H), **bf),
+                         torch.empty((numel, self.I), **bf), torch.empty((M, self.H), **bf))
+
+    def forward(self, x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                ws: Optional[Workspace] = None, cfg13=None, cfg2=None) -> torch.Tensor:
+        M = x.shape[0]
+        if ws is None:
+            ws = self.workspace(M, device=x.device)
+        if ws.M != M:
+            raise ValueError(f"workspace is for M={ws.M}, got {M}")
+        numel = M * self.top_k
+        B = ws.block_m
+        sorted_ids, eids, ntpp, loc = ops.moe_align(
+            topk_ids, self.expert_start, self.n_local, B,
+            out=(ws.sorted_ids, ws.expert_ids, ws.ntpp, ws.slot_local))
+        h = ws.buf13[: numel * 2 * self.I].view(numel, 2 * self.I)
+        ops.moe_w4a16_gemm(x, self.W13, sorted_ids, eids, ntpp, numel, self.top_k, B, out=h, cfg=cfg13)
+        ops.moe_act(self.act, h, self.I, loc.view(-1), self.alpha, self.limit, out=ws.a)
+        y = ws.buf13[: numel * self.H].view(numel, self.H)
+        ops.moe_w4a16_gemm(ws.a, self.W2, sorted_ids, eids, ntpp, numel, 1, B, out=y, cfg=cfg2)
+        return ops.moe_combine(y, topk_weights, loc, self.norm_w, self.eps, out=ws.out)
+
+    __call__ = forward

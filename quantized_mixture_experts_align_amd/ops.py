@@ -1,0 +1,181 @@
+"""Torch-tensor wrappers of the C ABI, one per entry point and with the same names.
+
+Argument marshalling only: tensors are checked for device/dtype/contiguity, outputs are
+allocated with torch when not given, and every computation runs in libmoe_w4a16.  Streams
+are torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, dtype, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def align_capacity(M: int, top_k: int, n_local: int, block_m: int):
+    s, b = C.c_int64(), C.c_int64()
+    L.check(L.lib().moe_align_capacity(M, top_k, n_local, block_m, C.byref(s), C.byref(b)),
+            "moe_align_capacity")
+    return s.value, b.value
+
+
+def choose_block_m(numel: int, n_local: int) -> int:
+    b = C.c_int32()
+    L.check(L.lib().moe_choose_block_m(numel, n_local, C.byref(b)), "moe_choose_block_m")
+    return b.value
+
+
+def moe_align(topk_ids: torch.Tensor, expert_start: int, n_local: int, block_m: int,
+              slot_local_ids: bool = True, out=None):
+    """-> (sorted_token_ids, expert_ids, num_tokens_post_padded, slot_local_ids or None)."""
+    _need(topk_ids, torch.int32, "topk_ids")
+    M, k = topk_ids.shape
+    s_len, b_len = align_capacity(M, k, n_local, block_m)
+    dev = topk_ids.device
+    if out is None:
+        out = (torch.empty(s_len, dtype=torch.int32, device=dev),
+               torch.empty(b_len, dtype=torch.int32, device=dev),
+               torch.empty(1, dtype=torch.int32, device=dev),
+               torch.empty((M, k), dtype=torch.int32, device=dev) if slot_local_ids else None)
+    sorted_ids, eids, ntpp, loc = out
+    L.check(L.lib().moe_align(_ptr(topk_ids), M, k, expert_start, n_local, block_m, _ptr(sorted_ids),
+                              _ptr(eids), _ptr(ntpp), _ptr(loc), _stream()), "moe_align")
+    return sorted_ids, eids, ntpp, loc
+
+
+@dataclass
+class PreparedWeights:
+    """Device buffer written by moe_w4a16_prepare and the descriptor pointing into it."""
+    buffer: torch.Tensor
+    desc: L.MoeWeights
+
+    @property
+    def N(self) -> int:
+        return self.desc.N
+
+    @property
+    def K(self) -> int:
+        return self.desc.K
+
+    @property
+    def n_experts(self) -> int:
+        return self.desc.n_experts
+
+    @property
+    def weight_bytes(self) -> int:
+        return self.buffer.numel()
+
+
+def prepared_size(qtype: str, E: int, N: int, K: int, flags: int, has_bias: bool):
+    n, k, b = C.c_int32(), C.c_int32(), C.c_size_t()
+    L.check(L.lib().moe_w4a16_prepared_size(L.QTYPE[qtype], E, N, K, flags, int(has_bias),
+                                            C.byref(n), C.byref(k), C.byref(b)),
+            "moe_w4a16_prepared_size")
+    return n.value, k.value, b.value
+
+
+def moe_w4a16_prepare(qtype: str, codes: torch.Tensor, scales: torch.Tensor,
+                      global_scale: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                      flags: int = 0) -> PreparedWeights:
+    """Repack canonical [E, N, K/2] codes and [E, N, K/g] scales into the tiled layout."""
+    _need(codes, torch.uint8, "codes")
+    if not scales.is_cuda or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous device tensor")
+    E, N, Kh = codes.shape
+    K = Kh * 2
+    if global_scale is not None:
+        _need(global_scale, torch.float32, "global_scale")
+    if bias is not None:
+        if bias.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+            raise ValueError("bias must hold bf16 values")
+        if not bias.is_cuda or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous device tensor")
+    _, _, nbytes = prepared_size(qtype, E, N, K, flags, bias is not None)
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    desc = L.MoeWeights()
+    L.check(L.lib().moe_w4a16_prepare(L.QTYPE[qtype], _ptr(codes), _ptr(scales), _ptr(global_scale),
+                                      _ptr(bias), E, N, K, flags, _ptr(buf), nbytes, C.byref(desc),
+                                      _stream()), "moe_w4a16_prepare")
+    return PreparedWeights(buf, desc)
+
+
+def moe_norm_weight(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _need(w, torch.bfloat16, "post_norm_w")
+    out = torch.empty_like(w) if out is None else out
+    L.check(L.lib().moe_norm_weight(_ptr(w), w.numel(), _ptr(out), _stream()), "moe_norm_weight")
+    return out
+
+
+def gemm_config(kernel: int = L.GEMM_AUTO, ng: int = 0, ksplit: int = 0, gemv_rows: int = 0):
+    return L.MoeGemmConfig(kernel, ng, ksplit, gemv_rows)
+
+
+def gemm_choose(W: PreparedWeights, numel: int, block_m: int, num_cus: int = 0) -> L.MoeGemmConfig:
+    c = L.MoeGemmConfig()
+    L.check(L.lib().moe_gemm_choose(C.byref(W.desc), numel, block_m, num_cus, C.byref(c)),
+            "moe_gemm_choose")
+    return c
+
+
+def moe_w4a16_gemm(A: torch.Tensor, W: PreparedWeights, sorted_token_ids: torch.Tensor,
+                   expert_ids: torch.Tensor, num_tokens_post_padded: torch.Tensor, numel: int,
+                   top_k: int, block_m: int, out: Optional[torch.Tensor] = None,
+                   cfg: Optional[L.MoeGemmConfig] = None) -> torch.Tensor:
+    """C[slot] = dequant(W[e]) . A[slot // top_k] (+ bias) for the live slots; C is [numel, N]."""
+    _need(A, torch.bfloat16, "A")
+    if out is None:
+        out = torch.empty((numel, W.N), dtype=torch.bfloat16, device=A.device)
+    _need(out, torch.bfloat16, "out")
+    L.check(L.lib().moe_w4a16_gemm(_ptr(A), A.shape[0], A.stride(0), _ptr(out), out.stride(0),
+                                   C.byref(W.desc), _ptr(sorted_token_ids), _ptr(expert_ids),
+                                   _ptr(num_tokens_post_padded), numel, top_k, block_m,
+                                   None if cfg is None else C.byref(cfg), _stream()),
+            "moe_w4a16_gemm")
+    return out
+
+
+def moe_act(kind: str, h: torch.Tensor, I: int, slot_local_ids: Optional[torch.Tensor] = None,
+            alpha: float = 1.702, limit: float = float("inf"),
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _need(h, torch.bfloat16, "h")
+    R = h.shape[0]
+    if out is None:
+        out = torch.empty((R, I), dtype=torch.bfloat16, device=h.device)
+    L.check(L.lib().moe_act(L.ACT[kind], _ptr(h), h.stride(0), _ptr(out), out.stride(0), R, I,
+                            _ptr(slot_local_ids), alpha, limit, _stream()), "moe_act")
+    return out
+
+
+def moe_combine(y: torch.Tensor, topk_weights: torch.Tensor, slot_local_ids: torch.Tensor,
+                norm_w: Optional[torch.Tensor] = None, eps: float = 1e-8,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _need(y, torch.bfloat16, "y")
+    _need(topk_weights, torch.float32, "topk_weights")
+    _need(slot_local_ids, torch.int32, "slot_local_ids")
+    M, k = topk_weights.shape
+    H = y.shape[-1]
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.bfloat16, device=y.device)
+    L.check(L.lib().moe_combine(_ptr(y), _ptr(topk_weights), _ptr(slot_local_ids), _ptr(norm_w), eps,
+                                M, k, H, _ptr(out), _stream()), "moe_combine")
+    return out

@@ -1,0 +1,43 @@
+"""Shared helpers of the GPU parity tests (tolerances and oracle calls)."""
+import numpy as np
+import torch
+
+import workloads as W
+from oracle import moe as O
+
+LAYER_ATOL, LAYER_RTOL = 0.06, 0.04   # the layer bar: |d| <= 0.06 + 0.04 |ref|
+
+
+def layer_violations(got: np.ndarray, ref: np.ndarray) -> int:
+    return int(np.sum(np.abs(got - ref) > LAYER_ATOL + LAYER_RTOL * np.abs(ref)))
+
+
+def gemm_tolerance(ref: np.ndarray) -> np.ndarray:
+    """Per-element bound for one GEMM against the float64 product: the bf16 rounding of the
+    result (2^-9 |ref|, doubled) plus 1% of the RMS for the bf16 rounding of int4 weights
+    (exact for the fp4 formats)."""
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    return 2.0 ** -8 * np.abs(ref) + 0.01 * rms + 1e-30
+
+
+def rel_rms(got: np.ndarray, ref: np.ndarray) -> float:
+    return float(np.sqrt(np.mean((got - ref) ** 2)) / max(np.sqrt(np.mean(ref * ref)), 1e-30))
+
+
+def oracle_layer(wl: W.Workload, lw, inp, tokens=None):
+    return O.moe_layer(wl.qtype, inp.x, inp.topk_ids, inp.topk_weights, lw.w13, lw.w2,
+                       expert_start=wl.expert_start, n_local=wl.n_local, act=wl.act, alpha=wl.alpha,
+                       limit=wl.limit, norm_w_bits=lw.norm_w, eps=wl.eps,
+                       interleaved_w13=wl.interleaved_w13, tokens=tokens)
+
+
+def make_layer(wl: W.Workload, lw, pad: bool = False):
+    from quantized_mixture_experts_align_amd import MoELayer
+    w13, w2, nw = W.device_weights(lw)
+    return MoELayer(wl.qtype, w13, w2, expert_start=wl.expert_start, n_local=wl.n_local,
+                    top_k=wl.top_k, act=wl.act, alpha=wl.alpha, limit=wl.limit, post_norm_w=nw,
+                    eps=wl.eps, interleaved_w13=wl.interleaved_w13, pad=pad)
+
+
+def announce(msg: str) -> None:
+    print(msg, flush=True)

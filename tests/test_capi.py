@@ -1,0 +1,117 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry point, and its
+host-side logic (size queries, validation, launch heuristics) behaves.  No kernel runs here."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import quantized_mixture_experts_align_amd as P
+from quantized_mixture_experts_align_amd import _lib as L
+from oracle import moe as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "moe_w4a16.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    lib = L.lib()
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in L.SIGNATURES, f"{n} has no binding"
+    assert lib.moe_abi_version() == 1
+
+
+@pytest.mark.parametrize("M,k,E,B", [(0, 8, 32, 16), (1, 8, 32, 16), (123, 2, 8, 64), (4096, 8, 32, 128),
+                                     (2048, 4, 128, 64), (5, 3, 512, 256)])
+def test_align_capacity_matches_definition(M, k, E, B):
+    assert P.align_capacity(M, k, E, B) == O.align_capacity(M * k, E, B)
+
+
+def test_prepared_size_validation():
+    n, k, b = P.prepared_size("nvfp4_g16", 32, 8192, 4096, L.PREP_GATE_UP, False)
+    assert (n, k) == (8192, 4096)
+    tiles = 32 * (8192 // 16) * (4096 // 64)
+    assert b == tiles * 512 + tiles * 64 + 256
+    # MXFP4 GPT-OSS: interleaved gate/up, bias; I = 2880 is already a tile multiple
+    n, k, b = P.prepared_size("mxfp4_g32", 128, 5760, 2880, L.PREP_GATE_UP | L.PREP_INTERLEAVED, True)
+    assert (n, k) == (5760, 2880)
+    # padding of the intermediate: I = 2848 -> 2880 per half; K = 2848 -> 2880
+    n, k, _ = P.prepared_size("mxfp4_g32", 4, 2 * 2848, 2880, L.PREP_GATE_UP | L.PREP_PAD, True)
+    assert n == 2 * 2880
+    _, k, _ = P.prepared_size("mxfp4_g32", 4, 2880, 2848, L.PREP_PAD, True)
+    assert k == 2880
+    with pytest.raises(ValueError, match="multiple of 64"):
+        P.prepared_size("mxfp4_g32", 4, 2880, 2848, 0, False)
+    with pytest.raises(ValueError, match="group"):
+        P.prepared_size("int4_g128", 4, 64, 192, 0, False)
+    with pytest.raises(ValueError, match="INTERLEAVED"):
+        P.prepared_size("int4_g128", 4, 64, 256, L.PREP_INTERLEAVED, False)
+    with pytest.raises(ValueError):
+        P.prepared_size("nvfp4_g16", 4, 40, 256, 0, False)   # N not a multiple of 16
+
+
+def test_entry_points_reject_bad_arguments_before_launch():
+    lib = L.lib()
+    s, e, n = C.c_void_p(1), C.c_void_p(1), C.c_void_p(1)
+    assert lib.moe_align(None, 4, 8, 0, 0, 16, s, e, n, None, None) == L.MOE_EUNSUPPORTED
+    assert b"n_local" in lib.moe_last_error()
+    assert lib.moe_align(None, 4, 8, 0, 32, 0, s, e, n, None, None) == L.MOE_EUNSUPPORTED
+    assert lib.moe_align(None, 4, 8, 0, 32, 16, None, e, n, None, None) == L.MOE_EINVAL
+    assert lib.moe_act(7, s, 16, s, 8, 4, 8, None, 1.0, 1.0, None) == L.MOE_EINVAL
+    assert lib.moe_act(0, s, 16, s, 8, 4, 12, None, 1.0, 1.0, None) == L.MOE_EUNSUPPORTED
+    assert lib.moe_combine(s, s, s, None, 1e-8, 4, 17, 64, s, None) == L.MOE_EUNSUPPORTED
+    assert lib.moe_combine(s, s, s, None, 1e-8, 4, 8, 60, s, None) == L.MOE_EUNSUPPORTED
+    W = L.MoeWeights(1, 32, 8192, 4096, 8192, 4096, 1, 0, 256, 256, None, None)  # NVFP4 without gs
+    assert lib.moe_w4a16_gemm(s, 8, 4096, s, 8192, C.byref(W), s, s, s, 8, 8, 16, None, None) == L.MOE_EINVAL
+    W.global_scale = 256
+    # A too short for the slots, lda below K
+    assert lib.moe_w4a16_gemm(s, 0, 4096, s, 8192, C.byref(W), s, s, s, 8, 8, 16, None, None) == L.MOE_EINVAL
+    assert lib.moe_w4a16_gemm(s, 8, 2048, s, 8192, C.byref(W), s, s, s, 8, 8, 16, None, None) == L.MOE_EINVAL
+    cfg = L.MoeGemmConfig(L.GEMM_MFMA, 4, 0, 0)
+    assert lib.moe_w4a16_gemm(s, 8, 4096, s, 8192, C.byref(W), s, s, s, 8, 8, 48, C.byref(cfg), None) \
+        == L.MOE_EUNSUPPORTED
+    cfg = L.MoeGemmConfig(L.GEMM_DECODE, 0, 3, 4)
+    assert lib.moe_w4a16_gemm(s, 8, 4096, s, 8192, C.byref(W), s, s, s, 8, 8, 16, C.byref(cfg), None) \
+        != L.MOE_OK
+    # numel == 0 is a no-op that needs no device
+    assert lib.moe_w4a16_gemm(None, 0, 4096, None, 8192, C.byref(W), None, None, None, 0, 8, 16, None, None) \
+        == L.MOE_OK
+
+
+def test_block_m_heuristic_is_monotone_and_picks_kernels():
+    prev = 0
+    for numel in [1, 8, 64, 256, 512, 1024, 2048, 4096, 8192, 32768, 1 << 20]:
+        b = P.choose_block_m(numel, 32)
+        assert b in (16, 32, 64, 128) and b >= prev
+        prev = b
+    assert P.choose_block_m(8, 32) == 16            # decode slice
+    assert P.choose_block_m(4608, 8) == 128         # int4 prefill
+
+
+def _W(q, E, N, K):
+    return P.PreparedWeights(None, L.MoeWeights(q, E, N, K, N, K, 0, 0, 1, 1, None, None))
+
+
+@pytest.mark.parametrize("N,K,E", [(8192, 4096, 32), (4096, 4096, 32), (5760, 2880, 128), (512, 1024, 8)])
+def test_gemm_choose_contract(N, K, E):
+    W = _W(1, E, N, K)
+    for numel in [1, 8, 64, 512]:
+        c = P.gemm_choose(W, numel, 16, 256)
+        assert c.kernel == L.GEMM_DECODE and c.ksplit in (1, 2, 4) and 0 <= c.gemv_rows <= 4
+        assert c.gemv_rows * K * 2 <= 65536
+    last = 4
+    for numel, B in [(512, 32), (2048, 64), (8192, 128), (32768, 128), (1 << 20, 128)]:
+        c = P.gemm_choose(W, numel, B, 256)
+        assert c.kernel == L.GEMM_MFMA and c.ng in (1, 2, 4)
+    # more work never selects a narrower tile
+    ngs = [P.gemm_choose(W, n, 128, 256).ng for n in (256, 1024, 8192, 65536)]
+    assert ngs == sorted(ngs)

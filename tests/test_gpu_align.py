@@ -1,0 +1,64 @@
+"""GPU align vs the oracle: bit-exact on every output entry (the whole capacity)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import moe as O
+import quantized_mixture_experts_align_amd as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(ids: np.ndarray, start: int, n_local: int, B: int, slot_ids=True):
+    t = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
+    s, e, n, loc = P.moe_align(t, start, n_local, B, slot_local_ids=slot_ids)
+    torch.cuda.synchronize()
+    return (s.cpu().numpy(), e.cpu().numpy(), int(n.cpu().item()),
+            None if loc is None else loc.cpu().numpy())
+
+
+def _check(ids, start, n_local, B):
+    print(f"align M={ids.shape[0]} k={ids.shape[1]} start={start} n_local={n_local} B={B}", flush=True)
+    gs, ge, gn, gl = _run(ids, start, n_local, B)
+    rs, re_, rn, rl = O.moe_align(ids, start, n_local, B)
+    assert gn == rn
+    assert np.array_equal(gs, rs)
+    assert np.array_equal(ge, re_)
+    assert np.array_equal(gl, rl)
+
+
+@pytest.mark.parametrize("cfg,M,B", [(0, 123, 32), (1, 2304, 128), (2, 1, 16), (2, 4, 16), (2, 16, 16),
+                                     (2, 64, 16), (3, 256, 64), (3, 1024, 128), (3, 4096, 128),
+                                     (4, 1, 16), (4, 32, 16), (4, 2048, 64)])
+def test_align_config_routing(cfg, M, B):
+    wl = W.CONFIGS[cfg]
+    inp = W.make_inputs(wl, M)
+    _check(inp.topk_ids, wl.expert_start, wl.n_local, B)
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("B", [1, 7, 16, 256])
+def test_align_random_slices(seed, B):
+    rng = np.random.default_rng(seed)
+    M, k = int(rng.integers(1, 700)), int(rng.integers(1, 9))
+    n_local = int(rng.integers(1, 300))
+    start = int(rng.integers(0, 50))
+    ids = rng.integers(-5, start + n_local + 40, size=(M, k)).astype(np.int32)  # includes junk ids
+    _check(ids, start, n_local, B)
+
+
+def test_align_edge_cases():
+    _check(np.zeros((0, 8), np.int32), 0, 32, 16)                        # no tokens
+    _check(np.full((37, 4), 1000, np.int32), 0, 128, 16)                 # everything off-slice
+    _check(np.full((300, 2), 5, np.int32), 5, 1, 64)                     # one expert
+    rng = np.random.default_rng(9)
+    _check(rng.integers(0, 1024, (513, 8)).astype(np.int32), 256, 512, 32)   # largest n_local
+    _check(rng.integers(0, 256, (16384, 8)).astype(np.int32), 0, 32, 128)    # 131072 slots
+
+
+def test_align_deterministic_and_optional_slot_ids():
+    inp = W.make_inputs(W.CONFIGS[3], 4096)
+    a = _run(inp.topk_ids, 0, 32, 128)
+    b = _run(inp.topk_ids, 0, 32, 128, slot_ids=False)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2] and b[3] is None

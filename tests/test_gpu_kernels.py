@@ -1,0 +1,159 @@
+"""Per-kernel GPU parity: prepare + grouped GEMM (every kernel and tile shape), activation,
+combine and the norm-weight binding, each against the oracle on the same inputs."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import moe as O
+from oracle import formats as F
+import quantized_mixture_experts_align_amd as P
+from quantized_mixture_experts_align_amd import _lib as L
+
+from gpu_util import gemm_tolerance, rel_rms
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_dev(a_bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(a_bits.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _gemm_case(qtype, which, M, B, cfg, wl_kw=None):
+    """Run GEMM1 (which=13) or GEMM2 (which=2) of a small workload on the GPU and return
+    (got, ref) over the live slots, in prepared column order."""
+    wl = W.small_workload(qtype, **(wl_kw or {}))
+    lw = W.make_weights(wl)
+    inp = W.make_inputs(wl, M)
+    w13, w2, _ = W.device_weights(lw)
+    if which == 13:
+        flags = L.PREP_GATE_UP | (L.PREP_INTERLEAVED if wl.interleaved_w13 else 0)
+        Wp = P.moe_w4a16_prepare(qtype, w13["codes"], w13["scales"], w13.get("gs"), w13.get("bias"), flags)
+        proj, top_k = lw.w13, wl.top_k
+        A_bits = inp.x
+    else:
+        Wp = P.moe_w4a16_prepare(qtype, w2["codes"], w2["scales"], w2.get("gs"), w2.get("bias"), 0)
+        proj, top_k = lw.w2, 1
+        rng = np.random.default_rng(M)
+        A_bits = W._to_bf16_bits(rng.standard_normal((M * wl.top_k, wl.I)).astype(np.float32))
+    ids = torch.from_numpy(inp.topk_ids).cuda()
+    s, e, n, loc = P.moe_align(ids, wl.expert_start, wl.n_local, B)
+    numel = M * wl.top_k
+    out = P.moe_w4a16_gemm(_bf16_dev(A_bits), Wp, s, e, n, numel, top_k, B, cfg=cfg)
+    torch.cuda.synchronize()
+    got = W.bf16_to_float(out)
+    local = loc.cpu().numpy().reshape(-1)
+    A = F.decode_bf16(A_bits)
+    rows = np.nonzero(local >= 0)[0]
+    ref = np.zeros((rows.size, Wp.N))
+    for j, slot in enumerate(rows):
+        ex = local[slot]
+        Wd = O.dequant(qtype, proj.codes[ex], proj.scales[ex], None if proj.gs is None else proj.gs[ex])
+        h = Wd @ A[slot // top_k]
+        if proj.bias is not None:
+            h = h + F.decode_bf16(proj.bias[ex])
+        if which == 13:
+            g, u = O.split_gate_up(h, wl.interleaved_w13)
+            h = np.concatenate([g, u])
+        ref[j] = h
+    return got[rows], ref, out[torch.from_numpy(rows).cuda()]   # rows of dead slots are never written
+
+
+CFGS = {
+    "decode_gemv": (16, P.gemm_config(L.GEMM_DECODE, 0, 4, 4)),
+    "decode_mfma": (16, P.gemm_config(L.GEMM_DECODE, 0, 2, 0)),
+    "decode_k1": (16, P.gemm_config(L.GEMM_DECODE, 0, 1, 2)),
+    "mfma16": (16, P.gemm_config(L.GEMM_MFMA, 1, 0, 0)),
+    "mfma32": (32, P.gemm_config(L.GEMM_MFMA, 2, 0, 0)),
+    "mfma64": (64, P.gemm_config(L.GEMM_MFMA, 4, 0, 0)),
+    "mfma128": (128, P.gemm_config(L.GEMM_MFMA, 4, 0, 0)),
+    "auto": (None, None),
+}
+
+
+@pytest.mark.parametrize("which", [13, 2])
+@pytest.mark.parametrize("kind", list(CFGS))
+@pytest.mark.parametrize("qtype", W.QTYPES)
+def test_gemm_matches_oracle(qtype, kind, which):
+    B, cfg = CFGS[kind]
+    M = 5 if kind.startswith("decode") else 61
+    if B is None:
+        B = P.choose_block_m(M * W.small_workload(qtype).top_k, W.small_workload(qtype).n_local)
+    print(f"gemm {qtype} {kind} W{which} M={M} B={B}", flush=True)
+    got, ref, _ = _gemm_case(qtype, which, M, B, cfg)
+    err = np.abs(got - ref)
+    assert np.all(err <= gemm_tolerance(ref)), f"max err {err.max()} rel rms {rel_rms(got, ref)}"
+    assert rel_rms(got, ref) < (4e-3 if qtype == "int4_g128" else 2e-3)
+
+
+@pytest.mark.parametrize("qtype", W.QTYPES)
+def test_mfma_result_is_independent_of_tile_width(qtype):
+    outs = []
+    for ng in (1, 2, 4):
+        print(f"mfma ng={ng} {qtype}", flush=True)
+        _, _, out = _gemm_case(qtype, 13, 200, 64, P.gemm_config(L.GEMM_MFMA, ng, 0, 0))
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def test_decode_is_reproducible():
+    cfg = P.gemm_config(L.GEMM_DECODE, 0, 4, 4)
+    a = _gemm_case("nvfp4_g16", 13, 3, 16, cfg)[2]
+    b = _gemm_case("nvfp4_g16", 13, 3, 16, cfg)[2]
+    assert torch.equal(a, b)
+
+
+def test_gemm_pad_intermediate():
+    # I = 288 is not a multiple of 64: the down projection's K is padded to 320 with zeros
+    wl = W.small_workload("mxfp4_g32", I=288, H=448)
+    lw = W.make_weights(wl)
+    w13, w2, _ = W.device_weights(lw)
+    Wp = P.moe_w4a16_prepare("mxfp4_g32", w2["codes"], w2["scales"], None, w2["bias"], L.PREP_PAD)
+    assert Wp.K == 320 and Wp.N == 448
+    W13 = P.moe_w4a16_prepare("mxfp4_g32", w13["codes"], w13["scales"], None, w13["bias"],
+                              L.PREP_GATE_UP | L.PREP_INTERLEAVED | L.PREP_PAD)
+    assert W13.N == 640
+
+
+@pytest.mark.parametrize("kind,limit", [("silu_mul", math.inf), ("swiglu_alpha", math.inf), ("swiglu_alpha", 7.0)])
+def test_act_matches_oracle(kind, limit):
+    rng = np.random.default_rng(3)
+    R, I = 77, 320
+    h_bits = W._to_bf16_bits((rng.standard_normal((R, 2 * I)) * 3).astype(np.float32))
+    loc = rng.integers(-1, 4, size=R).astype(np.int32)
+    out = torch.full((R, I), float("nan"), dtype=torch.bfloat16, device="cuda")
+    P.moe_act(kind, _bf16_dev(h_bits), I, torch.from_numpy(loc).cuda(), 1.702, limit, out=out)
+    torch.cuda.synchronize()
+    got = W.bf16_to_float(out)
+    h = F.decode_bf16(h_bits)
+    g, u = h[:, :I], h[:, I:]
+    ref = O.act_silu_mul(g, u) if kind == "silu_mul" else O.act_swiglu_alpha(g, u, 1.702, limit)
+    live = loc >= 0
+    assert np.all(np.isnan(got[~live]))                 # dead rows untouched
+    err = np.abs(got[live] - ref[live])
+    assert np.all(err <= 2.0 ** -8 * np.abs(ref[live]) + 1e-6), err.max()
+
+
+@pytest.mark.parametrize("H,norm", [(512, False), (4096, True), (2880, False), (2880, True), (64, True)])
+def test_combine_matches_oracle(H, norm):
+    rng = np.random.default_rng(H)
+    M, k = 45, 8
+    y_bits = W._to_bf16_bits(rng.standard_normal((M * k, H)).astype(np.float32))
+    g = rng.random((M, k)).astype(np.float32)
+    loc = rng.integers(-1, 3, size=(M, k)).astype(np.int32)
+    loc[0] = -1                                            # a token with no live slot
+    y_dev = _bf16_dev(y_bits)
+    y_dev.view(M, k, H)[torch.from_numpy(loc < 0).cuda()] = float("nan")   # dead rows never read
+    nw_bits = W._to_bf16_bits(rng.normal(0, 0.1, H).astype(np.float32)) if norm else None
+    nw_dev = P.moe_norm_weight(_bf16_dev(nw_bits)) if norm else None
+    out = P.moe_combine(y_dev, torch.from_numpy(g).cuda(), torch.from_numpy(loc).cuda(), nw_dev, 1e-8)
+    torch.cuda.synchronize()
+    got = W.bf16_to_float(out)
+    ref = O.combine(F.decode_bf16(y_bits), g, loc, O.norm_weight(nw_bits) if norm else None, 1e-8)
+    assert np.all(got[0] == 0)
+    err = np.abs(got - ref)
+    assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-3 * np.sqrt(np.mean(ref ** 2))), err.max()
+    if norm:
+        assert np.array_equal(W.bf16_to_float(nw_dev), O.norm_weight(nw_bits))

@@ -1,0 +1,114 @@
+"""Whole-layer GPU parity against the oracle: small shapes (several tiles, ragged tails) in
+full, the five workload configurations at full size on sampled tokens, and edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+import quantized_mixture_experts_align_amd as P
+from quantized_mixture_experts_align_amd import _lib as L
+
+from gpu_util import announce, layer_violations, make_layer, oracle_layer, rel_rms
+
+pytestmark = pytest.mark.gpu
+
+
+def _forward(layer, inp, **kw):
+    out = layer(*W.device_inputs(inp), **kw)
+    torch.cuda.synchronize()
+    return W.bf16_to_float(out)
+
+
+@pytest.mark.parametrize("M", [1, 3, 29, 130, 517])
+@pytest.mark.parametrize("qtype", W.QTYPES)
+def test_small_layer_matches_oracle(qtype, M):
+    wl = W.small_workload(qtype)
+    lw = W.make_weights(wl)
+    inp = W.make_inputs(wl, M)
+    announce(f"layer small {qtype} M={M}")
+    got = _forward(make_layer(wl, lw), inp)
+    ref = oracle_layer(wl, lw, inp)
+    assert layer_violations(got, ref) == 0
+    assert rel_rms(got, ref) < 0.01
+
+
+@pytest.mark.parametrize("qtype", W.QTYPES)
+def test_small_layer_every_gemm_kernel(qtype):
+    wl = W.small_workload(qtype)
+    lw = W.make_weights(wl)
+    layer = make_layer(wl, lw)
+    for M, B, cfg in [(7, 16, P.gemm_config(L.GEMM_DECODE, 0, 4, 4)),
+                      (7, 16, P.gemm_config(L.GEMM_DECODE, 0, 1, 0)),
+                      (90, 16, P.gemm_config(L.GEMM_MFMA, 1, 0, 0)),
+                      (90, 32, P.gemm_config(L.GEMM_MFMA, 2, 0, 0)),
+                      (300, 128, P.gemm_config(L.GEMM_MFMA, 4, 0, 0))]:
+        inp = W.make_inputs(wl, M)
+        announce(f"layer kernels {qtype} M={M} B={B} kernel={cfg.kernel}")
+        got = _forward(layer, inp, ws=layer.workspace(M, B), cfg13=cfg, cfg2=cfg)
+        ref = oracle_layer(wl, lw, inp)
+        assert layer_violations(got, ref) == 0
+
+
+def test_padded_intermediate_layer():
+    # I = 288: zero-padded to 320 at prepare (GPT-OSS tile padding); same result as unpadded
+    wl = W.small_workload("mxfp4_g32", I=288)
+    lw = W.make_weights(wl)
+    layer = make_layer(wl, lw, pad=True)
+    assert layer.I == 320
+    inp = W.make_inputs(wl, 77)
+    got = _forward(layer, inp)
+    assert layer_violations(got, oracle_layer(wl, lw, inp)) == 0
+
+
+def test_off_slice_tokens_are_zero_and_runs_repeat_bitwise():
+    wl = W.small_workload("nvfp4_g16")
+    lw = W.make_weights(wl)
+    inp = W.make_inputs(wl, 64)
+    ids = inp.topk_ids.copy()
+    ids[::4] = 60                        # outside the local range [8, 24)
+    inp2 = W.LayerInputs(inp.x, ids, inp.topk_weights, inp.M)
+    layer = make_layer(wl, lw)
+    a = _forward(layer, inp2)
+    b = _forward(layer, inp2)
+    assert np.all(a[::4] == 0.0)
+    assert np.array_equal(a, b)
+    assert layer_violations(a, oracle_layer(wl, lw, inp2)) == 0
+
+
+# ----------------------------------------------------------------------------- full-size configs
+_CACHE = {}
+
+
+def _cfg_layer(cfg):
+    wl = W.CONFIGS[cfg]
+    key = wl.seed
+    if key not in _CACHE:
+        _CACHE.clear()                   # keep one weight set resident at a time
+        lw = W.make_weights(wl)
+        _CACHE[key] = (lw, make_layer(wl, lw))
+    return (wl,) + _CACHE[key]
+
+
+def _sample(M, n, seed=0):
+    if M <= n:
+        return np.arange(M)
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(M, size=n, replace=False))
+
+
+@pytest.mark.parametrize("cfg,M,n_sample", [(0, 123, 123), (1, 2304, 2304), (2, 1, 1), (2, 4, 4), (2, 16, 5),
+                                            (2, 64, 5), (3, 256, 4), (3, 1024, 3), (3, 4096, 3),
+                                            (4, 1, 1), (4, 32, 4), (4, 2048, 4)])
+def test_config_layer_matches_oracle(cfg, M, n_sample):
+    wl, lw, layer = _cfg_layer(cfg)
+    inp = W.make_inputs(wl, M)
+    announce(f"layer config {cfg} M={M} ({wl.name}) sampled tokens={n_sample}")
+    got = _forward(layer, inp)
+    toks = _sample(M, n_sample, seed=M)
+    ref = oracle_layer(wl, lw, inp, tokens=toks)
+    assert layer_violations(got[toks], ref) == 0
+    assert rel_rms(got[toks], ref) < 0.01
+    # every token whose slots all fall off the local slice is exactly zero
+    off = np.all((inp.topk_ids < wl.expert_start) | (inp.topk_ids >= wl.expert_start + wl.n_local), axis=1)
+    assert np.all(got[off] == 0.0)
+    assert np.all(np.isfinite(got))

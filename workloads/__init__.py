@@ -200,3 +200,33 @@ def small_workload(qtype: str, **kw) -> Workload:
                               bias=True, act="swiglu_alpha", interleaved_w13=True, seed=102),
     }[qtype]
     return base.replace(**kw) if kw else base
+
+
+# ----------------------------------------------------------------------------- device copies
+def device_weights(lw: LayerWeights, device="cuda") -> tuple:
+    """(w13, w2, post_norm_w) as device tensors in the canonical layouts (bf16 for bf16 bits)."""
+    def proj(p: ExpertWeights, bf16_scales: bool) -> dict:
+        d = {"codes": torch.from_numpy(p.codes).to(device)}
+        s = torch.from_numpy(p.scales.view(np.int16) if bf16_scales else p.scales).to(device)
+        d["scales"] = s.view(torch.bfloat16) if bf16_scales else s
+        if p.gs is not None:
+            d["gs"] = torch.from_numpy(p.gs).to(device)
+        if p.bias is not None:
+            d["bias"] = torch.from_numpy(p.bias.view(np.int16)).to(device).view(torch.bfloat16)
+        return d
+    int4 = lw.w13.scales.dtype == np.uint16
+    nw = None
+    if lw.norm_w is not None:
+        nw = torch.from_numpy(lw.norm_w.view(np.int16)).to(device).view(torch.bfloat16)
+    return proj(lw.w13, int4), proj(lw.w2, int4), nw
+
+
+def device_inputs(inp: LayerInputs, device="cuda") -> tuple:
+    """(x bf16 [M, H], topk_ids int32 [M, k], topk_weights fp32 [M, k]) on the device."""
+    x = torch.from_numpy(inp.x.view(np.int16)).to(device).view(torch.bfloat16)
+    return x, torch.from_numpy(inp.topk_ids).to(device), torch.from_numpy(inp.topk_weights).to(device)
+
+
+def bf16_to_float(t: torch.Tensor) -> np.ndarray:
+    """A bf16 device tensor as float64 numpy (exact)."""
+    return t.detach().float().cpu().numpy().astype(np.float64)
