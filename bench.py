@@ -1,0 +1,236 @@
+"""Benchmark of the W4A16 MoE expert layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config C] [--M M] [--no-cpu-baseline]
+
+A step is one pass of the whole layer (align -> gate/up GEMM -> activation -> down GEMM ->
+combine) over one batch of seeded synthetic inputs already resident in HBM.  The default
+workload is the int4 layer with biases, M=2304 tokens, E=8, top-2, H=512, I=1024.
+
+Timing: W untimed warm-up steps, then K steps replayed from a HIP graph of one step,
+bracketed by device synchronisation; value = tokens / second.  The roofline entry is for
+the dominant kernel (the largest share of the layer's work): its average duration is taken
+with HIP events recorded around it on its own stream over K eager steps, and its algorithmic
+work per launch is the flops (prefill) or weight bytes (decode) it must process.  The CPU
+baseline is the float64 oracle on a bounded sample of the same workload on the host cores.
+
+Prints one JSON line.  With --sweep, prints one JSON line per configuration cell instead.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s + weight-stream GB/s (decode) and TFLOP/s (prefill) vs roofline"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PROFILES = os.path.join(ROOT, "profiles")
+GEMM_SRC = os.path.join(ROOT, "quantized_mixture_experts_align_amd", "csrc", "moe_gemm.hip")
+
+
+def gemm_source_hash() -> str:
+    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+
+
+def weight_bytes_per_expert(wl, proj: str) -> int:
+    """Algorithmic weight bytes of one expert's projection: codes + scales (+ global scale,
+    + bias), at the unpadded shape."""
+    N, K = (2 * wl.I, wl.H) if proj == "w13" else (wl.H, wl.I)
+    codes = N * K // 2
+    scales = N * (K // wl.group) * (2 if wl.qtype == "int4_g128" else 1)
+    gs = 4 if wl.qtype == "nvfp4_g16" else 0
+    bias = 2 * N if wl.bias else 0
+    return codes + scales + gs + bias
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None if there
+    is none for this kernel/workload or the kernel source changed since it was taken."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("source_sha256_16") != gemm_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, lw, inp, budget_s: float = 12.0) -> dict:
+    from oracle import moe as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    M = inp.M
+    # bounded sample: whole tokens, the first T of the batch, repeated until the budget is used
+    T = M
+    t0 = time.perf_counter()
+    O.moe_layer(wl.qtype, inp.x, inp.topk_ids, inp.topk_weights, lw.w13, lw.w2,
+                expert_start=wl.expert_start, n_local=wl.n_local, act=wl.act, alpha=wl.alpha,
+                limit=wl.limit, norm_w_bits=lw.norm_w, eps=wl.eps,
+                interleaved_w13=wl.interleaved_w13, tokens=np.arange(T))
+    one = time.perf_counter() - t0
+    reps = max(1, int(budget_s / max(one, 1e-3)))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        O.moe_layer(wl.qtype, inp.x, inp.topk_ids, inp.topk_weights, lw.w13, lw.w2,
+                    expert_start=wl.expert_start, n_local=wl.n_local, act=wl.act, alpha=wl.alpha,
+                    limit=wl.limit, norm_w_bits=lw.norm_w, eps=wl.eps,
+                    interleaved_w13=wl.interleaved_w13, tokens=np.arange(T))
+    dt = time.perf_counter() - t0
+    return {"value": round(T * reps / dt, 1), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 oracle, full layer on the first {T} of {M} tokens, {reps} runs, "
+                      f"{dt:.1f} s wall on {threads} BLAS threads"}
+
+
+def run_cell(cfg: int, M: int, steps: int, warmup: int, want_cpu: bool, seed=None) -> dict:
+    import torch
+    import workloads as W
+    from quantized_mixture_experts_align_amd import MoELayer
+    import quantized_mixture_experts_align_amd as P
+
+    wl = W.CONFIGS[cfg]
+    lw = W.make_weights(wl)
+    inp = W.make_inputs(wl, M, seed)
+    dev = torch.device("cuda", 0)
+    w13, w2, nw = W.device_weights(lw, dev)
+    layer = MoELayer(wl.qtype, w13, w2, expert_start=wl.expert_start, n_local=wl.n_local,
+                     top_k=wl.top_k, act=wl.act, alpha=wl.alpha, limit=wl.limit, post_norm_w=nw,
+                     eps=wl.eps, interleaved_w13=wl.interleaved_w13)
+    del w13, w2
+    x, ids, gw = W.device_inputs(inp, dev)
+    ws = layer.workspace(M, device=dev)
+    numel = M * wl.top_k
+    local = (inp.topk_ids >= wl.expert_start) & (inp.topk_ids < wl.expert_start + wl.n_local)
+    live = int(local.sum())
+    touched = len(np.unique(inp.topk_ids[local]))
+    flops_13 = 2.0 * live * (2 * wl.I) * wl.H
+    flops_2 = 2.0 * live * wl.H * wl.I
+    bytes_13 = touched * weight_bytes_per_expert(wl, "w13")
+    bytes_2 = touched * weight_bytes_per_expert(wl, "w2")
+
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        layer(x, ids, gw, ws=ws)
+    torch.cuda.synchronize()
+    # ---- value: graph replay of one step
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer(x, ids, gw, ws=ws)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / steps
+
+    # ---- dominant kernel: HIP events on the launch stream around each GEMM, eager steps
+    import quantized_mixture_experts_align_amd.ops as ops
+    ev = {k: [] for k in ("gemm13", "gemm2")}
+    orig = ops.moe_w4a16_gemm
+
+    def timed_gemm(A, Wt, *a, **kw):
+        key = "gemm13" if Wt is layer.W13 else "gemm2"
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        r = orig(A, Wt, *a, **kw)
+        e.record(stream)
+        ev[key].append((s, e))
+        return r
+    ops.moe_w4a16_gemm = timed_gemm
+    try:
+        # keep the device busy while the host enqueues, so each event pair brackets only
+        # device execution and not host launch latency
+        torch.cuda._sleep(int(2.4e9 * 0.05))
+        for _ in range(steps):
+            layer(x, ids, gw, ws=ws)
+    finally:
+        ops.moe_w4a16_gemm = orig
+    torch.cuda.synchronize()
+    dur = {k: float(np.mean([s.elapsed_time(e) for s, e in v])) * 1e-3 for k, v in ev.items()}
+
+    # dominant kernel: the gate/up GEMM holds 2/3 of the flops and of the weight bytes; it is
+    # compute-bound when its flops per weight byte exceed the machine balance
+    d13 = dur["gemm13"]
+    if flops_13 / bytes_13 > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        ach = flops_13 / d13 / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+    else:
+        ach = bytes_13 / d13 / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4)}
+    roof["kernel"] = "gemm_mfma_kernel" if layer_uses_mfma(layer, M, P) else "gemm_decode_kernel"
+    roof["traffic"] = load_traffic("moe_gemm13", wl.name + f"_m{M}")
+    roof["avg_launch_us"] = round(d13 * 1e6, 2)
+
+    out = {
+        "metric": METRIC, "value": round(M / step_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "qtype": wl.qtype, "M": M, "top_k": wl.top_k,
+                   "n_local": wl.n_local, "n_global": wl.n_global, "H": wl.H, "I": wl.I,
+                   "block_m": ws.block_m, "live_slots": live, "touched_experts": touched},
+        "roofline": roof,
+        "layer": {"weight_GBps": round((bytes_13 + bytes_2) / step_s / 1e9, 1),
+                  "TFLOPs": round((flops_13 + flops_2) / step_s / 1e12, 2),
+                  "gemm13_us": round(d13 * 1e6, 2), "gemm2_us": round(dur["gemm2"] * 1e6, 2),
+                  "weight_bytes": bytes_13 + bytes_2, "flops": flops_13 + flops_2},
+    }
+    if want_cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, lw, inp)
+    return out
+
+
+def layer_uses_mfma(layer, M, P) -> bool:
+    c = P.gemm_choose(layer.W13, M * layer.top_k, layer.block_m(M))
+    return c.kernel == 2
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--M", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="one line per configuration cell")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this layer is one GPU's expert slice and no multi-GPU "
+              "path is built; run with --gpus 1", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X (no GPU visible)", file=sys.stderr)
+        return 1
+    import workloads as W
+    if a.sweep:
+        for cfg, wl in W.CONFIGS.items():
+            for M in wl.Ms:
+                r = run_cell(cfg, M, a.steps, a.warmup, False)
+                print(json.dumps(r), flush=True)
+        return 0
+    M = a.M or W.CONFIGS[a.config].Ms[0]
+    r = run_cell(a.config, M, a.steps, a.warmup, not a.no_cpu_baseline)
+    print(json.dumps(r), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
