@@ -158,23 +158,29 @@ int moe_norm_weight(const uint16_t* w, int32_t H, uint16_t* out, hipStream_t str
 
 typedef enum {
   MOE_GEMM_AUTO = 0,
-  MOE_GEMM_DECODE = 1,    /* block_m <= 16: 16-row weight tiles, K split over waves,
-                             dot-product (GEMV) or one MFMA column of 16 rows per block  */
-  MOE_GEMM_MFMA = 2       /* block_m in {16,32,64,128}: bf16 MFMA 16x16x32 tiles           */
+  MOE_GEMM_DECODE = 1,    /* block_m <= 16: persistent workgroups over (live block, strip of ng
+                             16-row weight tiles), K split over ksplit waves; dot products for
+                             blocks of <= gemv_rows live slots, one 16-slot MFMA column otherwise */
+  MOE_GEMM_MFMA = 2       /* block_m in {16,32,64,128}: 4 waves x ng 16-row tiles x all slots of
+                             the block, bf16 MFMA 16x16x32, activations through an LDS ring   */
 } moe_gemm_kernel;
 
-/* Launch configuration.  Any valid configuration gives the same result bit for bit for a given
- * kernel (the K order of every output is fixed); AUTO picks one from the shapes. */
+/* Launch configuration.  For the MFMA kernel every valid configuration gives the same result bit
+ * for bit (the K order of every output is fixed); for the decode kernel a fixed configuration is
+ * reproducible run to run, and configurations differ only by fp32 summation order.  AUTO
+ * (cfg NULL or kernel 0) picks one from the shapes. */
 typedef struct moe_gemm_config {
   int32_t kernel;         /* moe_gemm_kernel                                               */
-  int32_t ng;             /* MFMA: 16-row n-tiles per wave: 1, 2 or 4 (4 waves per group)  */
+  int32_t ng;             /* 16-row weight tiles per wave: 1, 2 or 4                       */
   int32_t ksplit;         /* DECODE: waves splitting K in one workgroup: 1, 2 or 4         */
-  int32_t gemv_rows;      /* DECODE: blocks with at most this many live rows use the
-                             dot-product path (0..4), others the MFMA column              */
+  int32_t gemv_rows;      /* DECODE: blocks with at most this many live slots use dot
+                             products (0..4, and gemv_rows * K * 2 <= 32 KiB)              */
 } moe_gemm_config;
 
-/* Host heuristic: block_m for the align and the GEMM configuration for a problem of `numel`
- * slots over `n_local` experts with projection (N, K).  Pure host function. */
+/* Host heuristics (pure host functions).  moe_choose_block_m: block_m for the align from the
+ * slot count.  moe_gemm_choose: the GEMM configuration for projection W; `numel` is the number
+ * of slots expected to be live (M * top_k when unknown, or the expected local share of it -- a
+ * launch hint only, never a correctness input), num_cus <= 0 means 256. */
 int moe_choose_block_m(int64_t numel, int32_t n_local, int32_t* block_m);
 int moe_gemm_choose(const moe_weights* W, int64_t numel, int32_t block_m, int32_t num_cus,
                     moe_gemm_config* cfg);
@@ -198,6 +204,22 @@ int moe_w4a16_gemm(const uint16_t* A, int64_t a_rows, int32_t lda, uint16_t* C, 
                    const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
                    int64_t numel, int32_t top_k, int32_t block_m, const moe_gemm_config* cfg,
                    hipStream_t stream);
+
+/*
+ * Gate/up GEMM with the activation fused into its epilogue (one launch instead of
+ * moe_w4a16_gemm + moe_act, and no [numel, 2I] intermediate in memory):
+ *     out[s, j] = act(gate, up),  gate = bf16(h[s, j]), up = bf16(h[s, I + j])
+ * where h is what moe_w4a16_gemm computes for W13 (prepared with MOE_PREP_GATE_UP, N = 2I).
+ * The gate/up values are rounded to bf16 exactly as the stored GEMM output would be, so the
+ * result equals moe_w4a16_gemm followed by moe_act bit for bit.  out: device bf16 [numel, ldo],
+ * ldo >= I, only rows of live slots written.  cfg->ng must be 2 or 4 (gate/up tile pairs).
+ * Other arguments as moe_w4a16_gemm; alpha/limit as moe_act.
+ */
+int moe_w4a16_gemm_act(moe_act_kind kind, float alpha, float limit, const uint16_t* A, int64_t a_rows,
+                       int32_t lda, uint16_t* out, int32_t ldo, const moe_weights* W13,
+                       const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                       const int32_t* num_tokens_post_padded, int64_t numel, int32_t top_k,
+                       int32_t block_m, const moe_gemm_config* cfg, hipStream_t stream);
 
 /* ----------------------------------------------------------------------------- act */
 

@@ -50,6 +50,8 @@ SIGNATURES = {
     "moe_gemm_choose": (C.c_int, [C.POINTER(MoeWeights), _I64, _I32, _I32, C.POINTER(MoeGemmConfig)]),
     "moe_w4a16_gemm": (C.c_int, [_P, _I64, _I32, _P, _I32, C.POINTER(MoeWeights), _P, _P, _P,
                                  _I64, _I32, _I32, C.POINTER(MoeGemmConfig), _P]),
+    "moe_w4a16_gemm_act": (C.c_int, [C.c_int, _F, _F, _P, _I64, _I32, _P, _I32, C.POINTER(MoeWeights), _P,
+                                     _P, _P, _I64, _I32, _I32, C.POINTER(MoeGemmConfig), _P]),
     "moe_act": (C.c_int, [C.c_int, _P, _I32, _P, _I32, _I64, _I32, _P, _F, _F, _P]),
     "moe_combine": (C.c_int, [_P, _P, _P, _P, _F, _I64, _I32, _I32, _P, _P]),
 }

@@ -9,24 +9,6 @@
 
 namespace moe {
 
-__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
-
-// silu(gate) * up -- silu_and_mul of the Muse Spark experiment.
-struct SiluMul {
-  float alpha, limit;
-  __device__ __forceinline__ float operator()(float g, float u) const { return g * sigmoid_f(g) * u; }
-};
-// GPT-OSS: gate clamped from above, up clamped to [-limit, limit], then
-// gate * sigmoid(alpha * gate) * (up + 1)  (swiglu_gpt_oss_sigmoid_alpha_contiguous, sglang PR 28231).
-struct SwigluAlpha {
-  float alpha, limit;
-  __device__ __forceinline__ float operator()(float g, float u) const {
-    g = fminf(g, limit);
-    u = fminf(fmaxf(u, -limit), limit);
-    return g * sigmoid_f(alpha * g) * (u + 1.0f);
-  }
-};
-
 // One thread per 8 output columns of one row; grid-stride over rows x chunks.
 template <class Act>
 __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ in, int32_t ld_in,

@@ -23,6 +23,7 @@ namespace moe {
 constexpr int kAlignWaves = 16;
 constexpr int kAlignThreads = kAlignWaves * 64;
 constexpr int kAlignMaxLocal = 512;
+constexpr int kAlignUnroll = 8;
 
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int32_t* __restrict__ ids, int32_t numel, int32_t start, int32_t n_local, int32_t B,
@@ -42,12 +43,20 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   const int c0 = min(numel, w * per), c1 = min(numel, c0 + per);
   int32_t* my_cnt = cnt + w * n_local;
 
-  for (int base = c0; base < c1; base += 64) {
-    const int i = base + lane;
-    int le = -1;
-    if (i < c1) {
-      const int id = ids[i];
-      le = (id >= start && id - start < n_local) ? id - start : -1;
+  // (ids are read kAlignUnroll batches at a time so their load latencies overlap)
+  for (int base = c0; base < c1; base += 64 * kAlignUnroll) {
+    int idv[kAlignUnroll];
+#pragma unroll
+    for (int u = 0; u < kAlignUnroll; ++u) {
+      const int i = base + 64 * u + lane;
+      idv[u] = i < c1 ? ids[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kAlignUnroll; ++u) {
+      const int i = base + 64 * u + lane;
+      if (i >= c1) break;
+      const int id = idv[u];
+      const int le = (id >= start && id - start < n_local) ? id - start : -1;
       if (slot_local) slot_local[i] = le;
       if (le >= 0) atomicAdd(&my_cnt[le], 1);
     }
@@ -88,27 +97,34 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   int nbits = 0;
   while ((1 << nbits) < n_local) ++nbits;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = c0; base < c1; base += 64) {
-    const int i = base + lane;
-    int le = -1;
-    if (i < c1) {
-      const int id = ids[i];
-      le = (id >= start && id - start < n_local) ? id - start : -1;
+  for (int base = c0; base < c1; base += 64 * kAlignUnroll) {
+    int idv[kAlignUnroll];
+#pragma unroll
+    for (int u = 0; u < kAlignUnroll; ++u) {
+      const int i = base + 64 * u + lane;
+      idv[u] = i < c1 ? ids[i] : -1;
     }
-    const bool live = le >= 0;
-    uint64_t same = __ballot(live);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = live && ((le >> b) & 1);
-      const uint64_t m = __ballot(bit);
-      same &= bit ? m : ~m;
+#pragma unroll
+    for (int u = 0; u < kAlignUnroll; ++u) {
+      const int i = base + 64 * u + lane;
+      if (base + 64 * u >= c1) break;  // uniform: the wave's chunk has ended
+      const int id = idv[u];
+      const int le = (i < c1 && id >= start && id - start < n_local) ? id - start : -1;
+      const bool live = le >= 0;
+      uint64_t same = __ballot(live);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = live && ((le >> b) & 1);
+        const uint64_t m = __ballot(bit);
+        same &= bit ? m : ~m;
+      }
+      if (live) {
+        const int rank = __popcll(same & lt_mask);
+        const int before = my_cnt[le];
+        sorted[seg[le] + before + rank] = i;
+        if ((same >> lane) == 1ull) my_cnt[le] = before + __popcll(same);  // last lane of the group
+      }
+      __builtin_amdgcn_wave_barrier();
     }
-    if (live) {
-      const int rank = __popcll(same & lt_mask);
-      const int before = my_cnt[le];
-      sorted[seg[le] + before + rank] = i;
-      if ((same >> lane) == 1ull) my_cnt[le] = before + __popcll(same);  // last lane of the group
-    }
-    __builtin_amdgcn_wave_barrier();
   }
 
   // padding of each expert's last block, then the tail

@@ -90,16 +90,17 @@ extern "C" int moe_w4a16_prepared_size(moe_qtype q, int32_t E, int32_t N, int32_
 }
 
 // BLOCK_SIZE_M for the align.  The Muse Spark experiment picks from (8, 16, 32, 48, 64) by the
-// expected rows per expert; here the choice also selects the kernel: up to 16 expected rows per
-// local expert go to the decode kernel (one 16-row block), larger counts to MFMA tiles of
-// 32/64/128 rows so that the padding of the last block of each expert stays a small fraction.
+// expected rows per expert; here the choice also selects the kernel: up to 16 rows per local
+// expert (if every slot were local) go to the decode kernel, larger counts to MFMA tiles of
+// 32/64/128 rows.  Counting every slot (not only the expected local share) keeps skewed routing,
+// where a few local experts take most slots, on the MFMA tiles that share weight reads.
 extern "C" int moe_choose_block_m(int64_t numel, int32_t n_local, int32_t* block_m) {
   MOE_REQUIRE(block_m && numel >= 0 && n_local >= 1, MOE_EINVAL, "moe_choose_block_m: bad arguments");
   const double rows = (double)numel / n_local;
   int b = 16;
   if (rows > 16) b = 32;
   if (rows > 48) b = 64;
-  if (rows > 160) b = 128;
+  if (rows >= 1024) b = 128;
   *block_m = b;
   return ok();
 }
@@ -112,18 +113,25 @@ extern "C" int moe_gemm_choose(const moe_weights* W, int64_t numel, int32_t bloc
   moe_gemm_config c{};
   const int nt = W->N / kTileN;
   if (block_m <= 16) {
+    // decode: stream the touched experts' weights.  Enough waves to keep every CU streaming
+    // (about 8 per CU) even if only min(numel, E) blocks are live, K split over the waves of a
+    // workgroup, and as many 16-row tiles per wave as that allows (activations are reused
+    // across a wave's tiles).
     c.kernel = MOE_GEMM_DECODE;
-    c.gemv_rows = 4;
-    // enough waves to keep every CU streaming: split K when there are few n-tiles x blocks
-    const int64_t blocks = std::min<int64_t>(std::max<int64_t>(numel, 1), W->n_experts);
-    const int64_t groups = (int64_t)nt * blocks;
     const int kt = W->K / kTileK;
-    c.ksplit = (groups >= 8 * num_cus || kt < 8) ? 1 : (groups >= 2 * num_cus || kt < 16 ? 2 : 4);
+    c.ksplit = kt >= 16 ? 4 : (kt >= 4 ? 2 : 1);
+    c.gemv_rows = 0;  // measured: the one-column MFMA path streams faster than dot products
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(numel, W->n_experts));
+    const int64_t want = 8ll * num_cus;
+    c.ng = 4;
+    while (c.ng > 1 && blocks * ((nt + c.ng - 1) / c.ng) * c.ksplit < want) c.ng /= 2;
   } else {
+    // prefill: two 16-row tiles per wave (measured faster than four, whose register use
+    // leaves one wave per SIMD); one tile when the grid would not cover the CUs twice
     c.kernel = MOE_GEMM_MFMA;
     const int64_t mblocks = numel / block_m + std::min<int64_t>(numel, W->n_experts);
-    c.ng = 4;
-    while (c.ng > 1 && ((int64_t)(nt + 4 * c.ng - 1) / (4 * c.ng)) * mblocks < 2 * num_cus) c.ng /= 2;
+    c.ng = 2;
+    if (((int64_t)(nt + 7) / 8) * mblocks < 2 * num_cus) c.ng = 1;
   }
   *cfg = c;
   return ok();

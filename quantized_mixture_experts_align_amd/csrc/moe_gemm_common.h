@@ -1,0 +1,166 @@
+// Shared pieces of the grouped W4A16 GEMM kernels: arguments, group-scale loading and the
+// in-register dequantisation of one dword of codes (not part of the ABI).
+//
+// Weights are in the tiled layout written by moe_w4a16_prepare: 16 rows x 64 columns = 512
+// bytes per tile; lane l of a wave reads 8 contiguous bytes, which are the
+// v_mfma_f32_16x16x32_bf16 A operand of row l%16 for two k-steps (k = 32 i + 8 (l/16) + 0..7).
+#pragma once
+
+#include <algorithm>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+struct GemmArgs {
+  const uint16_t* A;
+  int64_t lda;
+  uint16_t* C;
+  int64_t ldc;
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* gs;
+  const uint16_t* bias;
+  const int32_t* sorted;
+  const int32_t* eids;
+  const int32_t* ntpp;
+  int32_t numel, top_k, block_m, N, K, E;
+  float alpha, limit;  // activation parameters of the fused gate/up epilogue
+};
+
+// Fused gate/up epilogue: the GEMM's output tiles come in (gate, up) pairs held by the same lane;
+// both are rounded to bf16 as the stored GEMM output would be, then the activation is applied
+// exactly as moe_act does, so the fused result equals GEMM + moe_act bit for bit.
+enum { kActNone = 0, kActSilu = 1, kActSwiglu = 2 };
+template <int ACT>
+__device__ __forceinline__ float fused_act(float gate, float up, const GemmArgs& a) {
+  const float g = bf16_to_f32(f32_to_bf16(gate)), u = bf16_to_f32(f32_to_bf16(up));
+  if constexpr (ACT == kActSilu) return SiluMul{a.alpha, a.limit}(g, u);
+  else return SwigluAlpha{a.alpha, a.limit}(g, u);
+}
+
+// ---------------------------------------------------------------------------- dequant
+// Group scales of one 64-column tile for this lane, kept as raw bits (they sit in prefetch
+// rings) and converted to fp32 at use: s(i, lane) is the scale of k-step i (k = 32 i + 8 (lane/16)
+// + 0..7 of the tile).
+template <int QT> struct TileScale;
+
+// NVFP4: the row's four e4m3 codes of the tile; k-step i of this lane is group 2 i + lane/32.
+template <> struct TileScale<MOE_Q_NVFP4_G16> {
+  uint32_t raw;
+  static constexpr int kRowBytes = 4;  // scale bytes per row and tile
+  __device__ __forceinline__ void load(const uint8_t* tile_scales, int kt, int lane) {
+    raw = reinterpret_cast<const uint32_t*>(tile_scales)[(int64_t)kt * 16 + (lane & 15)];
+  }
+  __device__ __forceinline__ float s(int i, int lane) const {
+    return __builtin_amdgcn_cvt_f32_fp8((int)(raw >> (8 * (lane >> 5) + 16 * i)), 0);
+  }
+};
+// MXFP4: the row's two E8M0 codes (one per k-step) -> fp32 powers of two (exponent field = code).
+template <> struct TileScale<MOE_Q_MXFP4_G32> {
+  uint32_t raw;
+  static constexpr int kRowBytes = 2;
+  __device__ __forceinline__ void load(const uint8_t* tile_scales, int kt, int lane) {
+    raw = reinterpret_cast<const uint16_t*>(tile_scales)[(int64_t)kt * 16 + (lane & 15)];
+  }
+  __device__ __forceinline__ float s(int i, int) const { return __uint_as_float(((raw >> (8 * i)) & 0xFFu) << 23); }
+};
+// int4: one bf16 scale per group of 128 (a tile pair).
+template <> struct TileScale<MOE_Q_INT4_G128> {
+  uint32_t raw;
+  static constexpr int kRowBytes = 2;  // per tile pair
+  __device__ __forceinline__ void load(const uint8_t* tile_scales, int kt, int lane) {
+    raw = reinterpret_cast<const uint16_t*>(tile_scales)[(int64_t)(kt >> 1) * 16 + (lane & 15)];
+  }
+  __device__ __forceinline__ float s(int, int) const { return __uint_as_float(raw << 16); }
+};
+
+__device__ __forceinline__ uint32_t bits2(bf16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
+
+// Eight codes (one dword, k order) -> eight bf16 weights, scale folded in (the MFMA A operand).
+template <int QT>
+__device__ __forceinline__ u32x4_t dequant8(uint32_t w, float s) {
+  u32x4_t o;
+  if constexpr (QT == MOE_Q_MXFP4_G32) {
+    // the hardware fp4 convert applies a power-of-two scale exactly (its exponent field)
+    o[0] = bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0));
+    o[1] = bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1));
+    o[2] = bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2));
+    o[3] = bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3));
+  } else if constexpr (QT == MOE_Q_NVFP4_G16) {
+    // e2m1 * e4m3 has at most 5 significant bits: exact in fp32 and in bf16
+    f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    o[0] = pack_bf16x2(p0[0] * s, p0[1] * s);
+    o[1] = pack_bf16x2(p1[0] * s, p1[1] * s);
+    o[2] = pack_bf16x2(p2[0] * s, p2[1] * s);
+    o[3] = pack_bf16x2(p3[0] * s, p3[1] * s);
+  } else {
+    // uint4b8: (u - 8) * s, exact in fp32 (4 x 8 significant bits), rounded once to bf16
+    const uint32_t t0 = w & 0x0F0F0F0Fu, t1 = (w >> 4) & 0x0F0F0F0Fu;
+    const float m8s = -8.0f * s;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = pack_bf16x2(fmaf((float)((t0 >> (8 * j)) & 0xFFu), s, m8s),
+                         fmaf((float)((t1 >> (8 * j)) & 0xFFu), s, m8s));
+  }
+  return o;
+}
+
+// Raw codes for the dot-product path: the group scale is applied to the partial sum instead
+// (NVFP4), or folded into the exact power-of-two convert (MXFP4), or into the weight (int4).
+template <int QT>
+__device__ __forceinline__ u32x4_t dequant8_raw(uint32_t w, float s) {
+  if constexpr (QT == MOE_Q_NVFP4_G16) {
+    u32x4_t o;
+    o[0] = bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0));
+    o[1] = bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1));
+    o[2] = bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2));
+    o[3] = bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3));
+    return o;
+  } else {
+    return dequant8<QT>(w, s);
+  }
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b),
+                                         c, false);
+}
+// (vector elements are copied to scalars first: a bit_cast of a subscripted vector element
+// is not an element-wise read)
+__device__ __forceinline__ float dot8(u32x4_t a, u32x4_t b, float c) {
+  const uint32_t a0 = a.x, a1 = a.y, a2 = a.z, a3 = a.w, b0 = b.x, b1 = b.y, b2 = b.z, b3 = b.w;
+  return dot2(a3, b3, dot2(a2, b2, dot2(a1, b1, dot2(a0, b0, c))));
+}
+
+__device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+template <int QT, bool BIAS>
+__device__ __forceinline__ float epilogue(float v, const GemmArgs& a, int e, int n) {
+  if constexpr (QT == MOE_Q_NVFP4_G16) v *= a.gs[e];
+  if constexpr (BIAS) v += bf16_to_f32(a.bias[(int64_t)e * a.N + n]);
+  return v;
+}
+
+// launchers, one explicit instantiation per weight format (moe_gemm_q*.hip)
+template <int QT>
+int launch_gemm_decode(bool bias, int act, const GemmArgs& a, const moe_gemm_config& c, int cap_blocks,
+                       int num_cus, hipStream_t st);
+template <int QT>
+int launch_gemm_mfma(bool bias, int act, const GemmArgs& a, const moe_gemm_config& c, int cap_blocks,
+                     hipStream_t st);
+int device_cu_count();
+
+}  // namespace moe

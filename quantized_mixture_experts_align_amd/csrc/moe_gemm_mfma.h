@@ -1,0 +1,268 @@
+// gemm_mfma: grouped W4A16 GEMM for align blocks of 16/32/64/128 slots (prefill batches).
+//
+// Workgroup = 4 waves over one align block (16*MG slots of one expert) x 4*NG 16-row weight
+// tiles; wave w owns tiles w*NG .. w*NG+NG-1 and all MG 16-slot groups, so every dequantised
+// weight fragment feeds MG v_mfma_f32_16x16x32_bf16 (weights = A operand, rows = output
+// features; activations = B operand, columns = slots).
+//
+// Pipeline over K in steps of 64 columns, kStages deep, every operand through LDS:
+//   * each stage holds the step's activations (in B-operand order: contiguous ds_read_b128
+//     per lane), the wave's NG weight tiles (512 B each, ds_read_b64 per lane) and their group
+//     scales, all written by global_load_lds (direct global -> LDS, no register staging);
+//   * step kt + kStages - 1 is issued while step kt computes; rows of padding slots read row 0
+//     of A (those MFMA columns are never stored);
+//   * one barrier per step: each wave waits (s_waitcnt vmcnt) until only the later steps' loads
+//     are pending -- every load is one instruction, so the count is exact -- then all waves
+//     meet at s_barrier.  __syncthreads() would wait for every prefetch in flight.
+// With ACT (fused gate/up epilogue) the wave's NG tiles are NG/2 gate tiles and the matching up
+// tiles I/16 tiles further down, so each lane holds gate and up of the same (slot, column).
+#pragma once
+
+#include "moe_gemm_common.h"
+
+namespace moe {
+
+constexpr int kStages = 3;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt[3:0] and
+// vmcnt[5:4] at bits 15:14; expcnt and lgkmcnt left at their maximum).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Direct global -> LDS load of BYTES (4 or 16) per lane: lane l's data lands at lds + l*BYTES.
+// Written as inline assembly so that the compiler's own wait insertion, which cannot tell which
+// LDS bytes such a load writes, does not add a full vmcnt(0) before every LDS read; the waits
+// for these loads are the explicit wait_vm<> calls.  (m0 holds the LDS address; one wait state
+// is required between writing m0 and the load.)
+template <int BYTES>
+__device__ __forceinline__ void dma_to_lds(const void* g, void* lds) {
+  const uint32_t off = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(off);
+  if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(g) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(g) : "memory", "m0");
+}
+
+template <int QT, bool BIAS, int MG, int NG, int ACT>
+__global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
+  static_assert(ACT == kActNone || NG % 2 == 0, "the fused epilogue pairs gate and up tiles");
+  constexpr int NGA = ACT == kActNone ? NG : NG / 2;     // tiles per wave in the assigned range
+  constexpr int BM = 16 * MG;
+  constexpr int FRAGS = 2 * MG * 64;                      // 16-B activation fragments per step
+  constexpr int XL = FRAGS >= 256 ? FRAGS / 256 : 1;      // fragment loads per thread and step
+  constexpr int XWAVES = FRAGS >= 256 ? 4 : FRAGS / 64;   // waves that load activations
+  constexpr int SROW = TileScale<QT>::kRowBytes;          // scale bytes per tile row
+  constexpr int SLANES = 16 * SROW / 4;                    // lanes loading a tile's scales (dwords)
+  constexpr int XB = FRAGS * 16;                           // stage layout: activations,
+  constexpr int WB = 4 * NG * kTileBytes;                  //   weight tiles of the 4 waves,
+  constexpr int SB = 4 * NG * 64;                          //   scales (64-B slot per tile)
+  constexpr int STAGE = XB + WB + SB;
+  constexpr int LW = 3 * NG;                               // weight + scale loads per wave and step
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * STAGE];
+  __shared__ int s_crow[BM];
+  auto stage_ptr = [&](int stage) -> uint8_t* { return smem + stage * STAGE; };
+
+  const int NT = a.N / kTileN, KT = a.K / kTileK;
+  const int NTA = ACT == kActNone ? NT : NT / 2;          // tiles to assign (gate tiles if fused)
+  const int nblk = (NTA + 4 * NGA - 1) / (4 * NGA);
+  const int mb = blockIdx.x / nblk, nb = blockIdx.x - mb * nblk;
+  if (mb * BM >= *a.ntpp) return;
+  const int e = a.eids[mb];
+  if (e < 0 || e >= a.E) return;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+
+  if (tid < BM) {
+    const int s = a.sorted[(int64_t)mb * BM + tid];
+    s_crow[tid] = (s >= 0 && s < a.numel) ? s : -1;
+  }
+  __syncthreads();
+
+  // activation fragment f = l*256 + tid -> k-step i, m-group g, MFMA lane fl: row g*16 + fl%16,
+  // columns 32 i + 8 (fl/16) + 0..7 of the step; stage slot f (wave-contiguous for the DMA)
+  const bool xwave = w < XWAVES;
+  const uint16_t* xsrc[XL];
+#pragma unroll
+  for (int l = 0; l < XL; ++l) {
+    const int f = l * 256 + tid;
+    const int fl = f & 63, g = (f >> 6) % MG, i = (f >> 6) / MG;
+    const int row = xwave ? s_crow[g * 16 + (fl & 15)] : -1;
+    xsrc[l] = a.A + (int64_t)(row >= 0 ? row / a.top_k : 0) * a.lda + 32 * i + 8 * (fl >> 4);
+  }
+  // weights: NG consecutive 16-row tiles of this wave (clamped at the N edge, not stored)
+  int ntile[NG];
+  bool nok[NG];
+  const uint8_t* wsrc[NG];
+  const uint8_t* ssrc[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    if (g < NGA) {
+      const int t = nb * 4 * NGA + w * NGA + g;
+      nok[g] = t < NTA;
+      ntile[g] = nok[g] ? t : NTA - 1;
+    } else {  // up tile of gate tile g - NGA
+      nok[g] = nok[g - NGA];
+      ntile[g] = ntile[g - NGA] + NTA;
+    }
+    const int64_t tile0 = ((int64_t)e * NT + ntile[g]) * KT;
+    wsrc[g] = a.codes + tile0 * kTileBytes + lane * 4;
+    ssrc[g] = a.scales + (QT == MOE_Q_INT4_G128 ? ((int64_t)e * NT + ntile[g]) * (KT / 2) * 32
+                                                : tile0 * scale_bytes_per_tile(QT)) + lane * 4;
+  }
+  auto issue = [&](int kt, int stage) {
+    uint8_t* st = stage_ptr(stage);
+    if (xwave) {
+#pragma unroll
+      for (int l = 0; l < XL; ++l)
+        dma_to_lds<16>(xsrc[l] + kt * kTileK, st + (l * 256 + w * 64) * 16);
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      uint8_t* wt = st + XB + (w * NG + g) * kTileBytes;
+      const uint8_t* src = wsrc[g] + (int64_t)kt * kTileBytes;
+      dma_to_lds<4>(src, wt);
+      dma_to_lds<4>(src + 256, wt + 256);
+      const int64_t soff = QT == MOE_Q_INT4_G128 ? (int64_t)(kt >> 1) * 32 : (int64_t)kt * scale_bytes_per_tile(QT);
+      if (lane < SLANES)
+        dma_to_lds<4>(ssrc[g] + soff, st + XB + WB + (w * NG + g) * 64);
+    }
+  };
+
+  f32x4_t acc[NG][MG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int h = 0; h < MG; ++h) acc[g][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < KT) issue(s, s);
+
+  for (int kt0 = 0; kt0 < KT; kt0 += kStages) {
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) {
+      const int kt = kt0 + u;
+      if (kt >= KT) break;
+      // this wave's loads of step kt have landed once only later steps' loads are pending
+      static_assert(kStages == 3, "wait counts below assume three stages");
+      if (kt + 1 < KT) {
+        if (xwave) wait_vm<XL + LW>(); else wait_vm<LW>();
+      } else {
+        wait_vm<0>();
+      }
+      block_barrier();  // everyone's step kt is in LDS, and everyone is done with step kt-1
+      if (kt + kStages - 1 < KT) issue(kt + kStages - 1, (u + kStages - 1) % kStages);
+      const uint8_t* st = stage_ptr(u);
+      const u32x4_t* xs = reinterpret_cast<const u32x4_t*>(st);
+      u32x2_t wq[NG];
+      TileScale<QT> sc[NG];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        wq[g] = reinterpret_cast<const u32x2_t*>(st + XB + (w * NG + g) * kTileBytes)[lane];
+        const uint8_t* sb = st + XB + WB + (w * NG + g) * 64 + (lane & 15) * SROW;
+        sc[g].raw = SROW == 4 ? *reinterpret_cast<const uint32_t*>(sb) : *reinterpret_cast<const uint16_t*>(sb);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        u32x4_t af[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) af[g] = dequant8<QT>(wq[g][i], sc[g].s(i, lane));
+#pragma unroll
+        for (int h = 0; h < MG; ++h) {
+          const u32x4_t bf = xs[(i * MG + h) * 64 + lane];
+#pragma unroll
+          for (int g = 0; g < NG; ++g) acc[g][h] = mfma(af[g], bf, acc[g][h]);
+        }
+      }
+    }
+  }
+
+  // epilogue: lane holds D[n = 4 (lane/16) + q][m = lane % 16] of each (n-tile, m-group)
+  float gsv = 1.f;
+  if constexpr (QT == MOE_Q_NVFP4_G16) gsv = a.gs[e];
+  float bv[NG][4];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int n0 = ntile[g] * kTileN + 4 * (lane >> 4);
+    bv[g][0] = bv[g][1] = bv[g][2] = bv[g][3] = 0.f;
+    if constexpr (BIAS) {
+      const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(a.bias + (int64_t)e * a.N + n0);
+      bv[g][0] = bf16_lo(bb[0]); bv[g][1] = bf16_hi(bb[0]); bv[g][2] = bf16_lo(bb[1]); bv[g][3] = bf16_hi(bb[1]);
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < NGA; ++g) {
+    if (!nok[g]) continue;
+    const int n0 = ntile[g] * kTileN + 4 * (lane >> 4);
+#pragma unroll
+    for (int h = 0; h < MG; ++h) {
+      const int row = s_crow[h * 16 + (lane & 15)];
+      if (row < 0) continue;
+      float o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        o[q] = acc[g][h][q] * gsv + bv[g][q];
+        if constexpr (ACT != kActNone) o[q] = fused_act<ACT>(o[q], acc[g + NGA][h][q] * gsv + bv[g + NGA][q], a);
+      }
+      *reinterpret_cast<u32x2_t*>(a.C + (int64_t)row * a.ldc + n0) =
+          u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    }
+  }
+}
+
+template <int QT, bool BIAS, int MG, int ACT>
+static int launch_mg(const GemmArgs& a, int ng, int blocks, hipStream_t st) {
+  const int NT = a.N / kTileN;
+  const int nta = ACT == kActNone ? NT : NT / 2, nga = ACT == kActNone ? ng : ng / 2;
+  const int nblk = (nta + 4 * nga - 1) / (4 * nga);
+  const dim3 grid((unsigned)((int64_t)nblk * blocks));
+  if constexpr (ACT == kActNone) {
+    if (ng == 1) {
+      hipLaunchKernelGGL((gemm_mfma_kernel<QT, BIAS, MG, 1, ACT>), grid, dim3(256), 0, st, a);
+      return check_launch("moe_w4a16_gemm (mfma)");
+    }
+  }
+  switch (ng) {
+    case 2: hipLaunchKernelGGL((gemm_mfma_kernel<QT, BIAS, MG, 2, ACT>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((gemm_mfma_kernel<QT, BIAS, MG, 4, ACT>), grid, dim3(256), 0, st, a); break;
+    default:
+      return fail(MOE_EINVAL, "moe_w4a16_gemm: ng=%d (1, 2 or 4; 2 or 4 with a fused activation)", ng);
+  }
+  return check_launch("moe_w4a16_gemm (mfma)");
+}
+
+template <int QT, bool BIAS, int ACT>
+static int launch_mfma_b(const GemmArgs& a, int ng, int blocks, hipStream_t st) {
+  switch (a.block_m) {
+    case 16: return launch_mg<QT, BIAS, 1, ACT>(a, ng, blocks, st);
+    case 32: return launch_mg<QT, BIAS, 2, ACT>(a, ng, blocks, st);
+    case 64: return launch_mg<QT, BIAS, 4, ACT>(a, ng, blocks, st);
+    case 128: return launch_mg<QT, BIAS, 8, ACT>(a, ng, blocks, st);
+    default:
+      return fail(MOE_EUNSUPPORTED, "moe_w4a16_gemm: MFMA kernel needs block_m 16/32/64/128, got %d",
+                  a.block_m);
+  }
+}
+
+template <int QT>
+int launch_gemm_mfma(bool bias, int act, const GemmArgs& a, const moe_gemm_config& c, int cap_blocks,
+                     hipStream_t st) {
+  switch (act) {
+    case kActNone:
+      return bias ? launch_mfma_b<QT, true, kActNone>(a, c.ng, cap_blocks, st)
+                  : launch_mfma_b<QT, false, kActNone>(a, c.ng, cap_blocks, st);
+    case kActSilu:
+      return bias ? launch_mfma_b<QT, true, kActSilu>(a, c.ng, cap_blocks, st)
+                  : launch_mfma_b<QT, false, kActSilu>(a, c.ng, cap_blocks, st);
+    default:
+      return bias ? launch_mfma_b<QT, true, kActSwiglu>(a, c.ng, cap_blocks, st)
+                  : launch_mfma_b<QT, false, kActSwiglu>(a, c.ng, cap_blocks, st);
+  }
+}
+
+}  // namespace moe

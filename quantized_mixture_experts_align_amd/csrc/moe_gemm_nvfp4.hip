@@ -1,0 +1,9 @@
+// Instantiation of the grouped GEMM kernels for nvfp4 weights (one translation unit per format
+// so the kernel variants compile in parallel).
+#include "moe_gemm_decode.h"
+#include "moe_gemm_mfma.h"
+
+namespace moe {
+template int launch_gemm_decode<MOE_Q_NVFP4_G16>(bool, int, const GemmArgs&, const moe_gemm_config&, int, int, hipStream_t);
+template int launch_gemm_mfma<MOE_Q_NVFP4_G16>(bool, int, const GemmArgs&, const moe_gemm_config&, int, hipStream_t);
+}  // namespace moe

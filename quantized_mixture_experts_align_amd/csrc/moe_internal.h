@@ -60,4 +60,23 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(__builtin_bit_cast(uint16_t, (__bf16)f));
 }
 
+// ---------------------------------------------------------------------------- activations
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+// silu(gate) * up -- silu_and_mul of the Muse Spark experiment.
+struct SiluMul {
+  float alpha, limit;
+  __device__ __forceinline__ float operator()(float g, float u) const { return g * sigmoid_f(g) * u; }
+};
+// GPT-OSS: gate clamped from above, up clamped to [-limit, limit], then
+// gate * sigmoid(alpha * gate) * (up + 1)  (swiglu_gpt_oss_sigmoid_alpha_contiguous, sglang PR 28231).
+struct SwigluAlpha {
+  float alpha, limit;
+  __device__ __forceinline__ float operator()(float g, float u) const {
+    g = fminf(g, limit);
+    u = fminf(fmaxf(u, -limit), limit);
+    return g * sigmoid_f(alpha * g) * (u + 1.0f);
+  }
+};
+
 }  // namespace moe

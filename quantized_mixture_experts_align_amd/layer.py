@@ -28,6 +28,7 @@ class Workspace:
     buf13: torch.Tensor
     a: torch.Tensor
     out: torch.Tensor
+    cfgs: Optional[tuple] = None    # (gate/up, down) GEMM launch configurations
 
 
 class MoELayer:
@@ -40,8 +41,10 @@ class MoELayer:
     def __init__(self, qtype: str, w13: dict, w2: dict, *, expert_start: int, n_local: int,
                  top_k: int, act: str = "silu_mul", alpha: float = 1.702,
                  limit: float = float("inf"), post_norm_w: Optional[torch.Tensor] = None,
-                 eps: float = 1e-8, interleaved_w13: bool = False, pad: bool = False):
+                 eps: float = 1e-8, interleaved_w13: bool = False, pad: bool = False,
+                 n_global: Optional[int] = None):
         self.qtype, self.expert_start, self.n_local, self.top_k = qtype, expert_start, n_local, top_k
+        self.n_global = n_global
         self.act, self.alpha, self.limit, self.eps = act, alpha, limit, eps
         f13 = L.PREP_GATE_UP | (L.PREP_INTERLEAVED if interleaved_w13 else 0) | (L.PREP_PAD if pad else 0)
         f2 = L.PREP_PAD if pad else 0
@@ -57,8 +60,21 @@ class MoELayer:
         self.H = self.W2.N
         self.norm_w = None if post_norm_w is None else ops.moe_norm_weight(post_norm_w)
 
+    def expected_local_slots(self, M: int) -> int:
+        """Launch hint: slots expected on this slice (all of them when n_global is unknown).
+        Only launch shapes depend on it, never results."""
+        numel = M * self.top_k
+        if not self.n_global or self.n_global <= self.n_local:
+            return numel
+        return max(1, -(-numel * self.n_local // self.n_global))
+
     def block_m(self, M: int) -> int:
         return ops.choose_block_m(M * self.top_k, self.n_local)
+
+    def configs(self, M: int, block_m: int):
+        """GEMM launch configurations (gate/up, down) for a batch of M tokens."""
+        hint = self.expected_local_slots(M)
+        return ops.gemm_choose(self.W13, hint, block_m), ops.gemm_choose(self.W2, hint, block_m)
 
     def workspace(self, M: int, block_m: Optional[int] = None, device=None) -> Workspace:
         device = device or self.W13.buffer.device
@@ -70,10 +86,15 @@ class MoELayer:
         return Workspace(M, B, torch.empty(s_len, **i32), torch.empty(b_len, **i32),
                          torch.empty(1, **i32), torch.empty((M, self.top_k), **i32),
                          torch.empty(numel * max(2 * self.I, self.H), **bf),
-                         torch.empty((numel, self.I), **bf), torch.empty((M, self.H), **bf))
+                         torch.empty((numel, self.I), **bf), torch.empty((M, self.H), **bf),
+                         self.configs(M, B))
 
     def forward(self, x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
-                ws: Optional[Workspace] = None, cfg13=None, cfg2=None) -> torch.Tensor:
+                ws: Optional[Workspace] = None, cfg13=None, cfg2=None,
+                fused_act: bool = True) -> torch.Tensor:
+        """align -> gate/up GEMM -> activation -> down GEMM -> combine.  With fused_act the
+        activation runs in the gate/up GEMM's epilogue (bitwise the same result, one launch
+        and one [numel, 2I] round trip less); cfg13 must then have ng 2 or 4."""
         M = x.shape[0]
         if ws is None:
             ws = self.workspace(M, device=x.device)
@@ -81,12 +102,22 @@ class MoELayer:
             raise ValueError(f"workspace is for M={ws.M}, got {M}")
         numel = M * self.top_k
         B = ws.block_m
+        if cfg13 is None or cfg2 is None:
+            c13, c2 = ws.cfgs if ws.cfgs is not None else self.configs(M, B)
+            cfg13 = cfg13 or c13
+            cfg2 = cfg2 or c2
         sorted_ids, eids, ntpp, loc = ops.moe_align(
             topk_ids, self.expert_start, self.n_local, B,
             out=(ws.sorted_ids, ws.expert_ids, ws.ntpp, ws.slot_local))
-        h = ws.buf13[: numel * 2 * self.I].view(numel, 2 * self.I)
-        ops.moe_w4a16_gemm(x, self.W13, sorted_ids, eids, ntpp, numel, self.top_k, B, out=h, cfg=cfg13)
-        ops.moe_act(self.act, h, self.I, loc.view(-1), self.alpha, self.limit, out=ws.a)
+        if fused_act:
+            if cfg13.ng < 2:
+                cfg13 = ops.gemm_config(cfg13.kernel, 2, cfg13.ksplit, cfg13.gemv_rows)
+            ops.moe_w4a16_gemm_act(self.act, x, self.W13, sorted_ids, eids, ntpp, numel, self.top_k, B,
+                                   self.alpha, self.limit, out=ws.a, cfg=cfg13)
+        else:
+            h = ws.buf13[: numel * 2 * self.I].view(numel, 2 * self.I)
+            ops.moe_w4a16_gemm(x, self.W13, sorted_ids, eids, ntpp, numel, self.top_k, B, out=h, cfg=cfg13)
+            ops.moe_act(self.act, h, self.I, loc.view(-1), self.alpha, self.limit, out=ws.a)
         y = ws.buf13[: numel * self.H].view(numel, self.H)
         ops.moe_w4a16_gemm(ws.a, self.W2, sorted_ids, eids, ntpp, numel, 1, B, out=y, cfg=cfg2)
         return ops.moe_combine(y, topk_weights, loc, self.norm_w, self.eps, out=ws.out)

@@ -154,6 +154,25 @@ def moe_w4a16_gemm(A: torch.Tensor, W: PreparedWeights, sorted_token_ids: torch.
     return out
 
 
+def moe_w4a16_gemm_act(kind: str, A: torch.Tensor, W13: PreparedWeights, sorted_token_ids: torch.Tensor,
+                       expert_ids: torch.Tensor, num_tokens_post_padded: torch.Tensor, numel: int,
+                       top_k: int, block_m: int, alpha: float = 1.702, limit: float = float("inf"),
+                       out: Optional[torch.Tensor] = None,
+                       cfg: Optional[L.MoeGemmConfig] = None) -> torch.Tensor:
+    """out[slot] = act(gate, up) of the gate/up GEMM, fused into one launch; out is [numel, I]."""
+    _need(A, torch.bfloat16, "A")
+    if out is None:
+        out = torch.empty((numel, W13.N // 2), dtype=torch.bfloat16, device=A.device)
+    _need(out, torch.bfloat16, "out")
+    L.check(L.lib().moe_w4a16_gemm_act(L.ACT[kind], alpha, limit, _ptr(A), A.shape[0], A.stride(0),
+                                       _ptr(out), out.stride(0), C.byref(W13.desc),
+                                       _ptr(sorted_token_ids), _ptr(expert_ids),
+                                       _ptr(num_tokens_post_padded), numel, top_k, block_m,
+                                       None if cfg is None else C.byref(cfg), _stream()),
+            "moe_w4a16_gemm_act")
+    return out
+
+
 def moe_act(kind: str, h: torch.Tensor, I: int, slot_local_ids: Optional[torch.Tensor] = None,
             alpha: float = 1.702, limit: float = float("inf"),
             out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -36,7 +36,8 @@ def make_layer(wl: W.Workload, lw, pad: bool = False):
     w13, w2, nw = W.device_weights(lw)
     return MoELayer(wl.qtype, w13, w2, expert_start=wl.expert_start, n_local=wl.n_local,
                     top_k=wl.top_k, act=wl.act, alpha=wl.alpha, limit=wl.limit, post_norm_w=nw,
-                    eps=wl.eps, interleaved_w13=wl.interleaved_w13, pad=pad)
+                    eps=wl.eps, interleaved_w13=wl.interleaved_w13, pad=pad,
+                    n_global=wl.n_global)
 
 
 def announce(msg: str) -> None:

@@ -94,7 +94,8 @@ def test_block_m_heuristic_is_monotone_and_picks_kernels():
         assert b in (16, 32, 64, 128) and b >= prev
         prev = b
     assert P.choose_block_m(8, 32) == 16            # decode slice
-    assert P.choose_block_m(4608, 8) == 128         # int4 prefill
+    assert P.choose_block_m(4608, 8) == 64          # int4 prefill, 576 rows per expert
+    assert P.choose_block_m(32768, 32) == 128       # NVFP4 slice, 1024 rows per expert
 
 
 def _W(q, E, N, K):

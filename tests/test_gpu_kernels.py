@@ -62,9 +62,9 @@ def _gemm_case(qtype, which, M, B, cfg, wl_kw=None):
 
 
 CFGS = {
-    "decode_gemv": (16, P.gemm_config(L.GEMM_DECODE, 0, 4, 4)),
-    "decode_mfma": (16, P.gemm_config(L.GEMM_DECODE, 0, 2, 0)),
-    "decode_k1": (16, P.gemm_config(L.GEMM_DECODE, 0, 1, 2)),
+    "decode_gemv": (16, P.gemm_config(L.GEMM_DECODE, 4, 4, 4)),
+    "decode_mfma": (16, P.gemm_config(L.GEMM_DECODE, 2, 2, 0)),
+    "decode_k1": (16, P.gemm_config(L.GEMM_DECODE, 1, 1, 2)),
     "mfma16": (16, P.gemm_config(L.GEMM_MFMA, 1, 0, 0)),
     "mfma32": (32, P.gemm_config(L.GEMM_MFMA, 2, 0, 0)),
     "mfma64": (64, P.gemm_config(L.GEMM_MFMA, 4, 0, 0)),
@@ -99,7 +99,7 @@ def test_mfma_result_is_independent_of_tile_width(qtype):
 
 
 def test_decode_is_reproducible():
-    cfg = P.gemm_config(L.GEMM_DECODE, 0, 4, 4)
+    cfg = P.gemm_config(L.GEMM_DECODE, 2, 4, 4)
     a = _gemm_case("nvfp4_g16", 13, 3, 16, cfg)[2]
     b = _gemm_case("nvfp4_g16", 13, 3, 16, cfg)[2]
     assert torch.equal(a, b)
@@ -157,3 +157,27 @@ def test_combine_matches_oracle(H, norm):
     assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-3 * np.sqrt(np.mean(ref ** 2))), err.max()
     if norm:
         assert np.array_equal(W.bf16_to_float(nw_dev), O.norm_weight(nw_bits))
+
+
+@pytest.mark.parametrize("kind", ["decode", "mfma"])
+@pytest.mark.parametrize("qtype", W.QTYPES)
+def test_fused_activation_equals_gemm_then_act(qtype, kind):
+    """The gate/up GEMM with the activation in its epilogue gives the same bytes as
+    moe_w4a16_gemm followed by moe_act (both round gate/up to bf16 before the activation)."""
+    wl = W.small_workload(qtype)
+    lw = W.make_weights(wl)
+    M, B, cfg = (5, 16, P.gemm_config(L.GEMM_DECODE, 2, 4, 0)) if kind == "decode" else \
+        (150, 64, P.gemm_config(L.GEMM_MFMA, 2, 0, 0))
+    inp = W.make_inputs(wl, M)
+    w13, _, _ = W.device_weights(lw)
+    flags = L.PREP_GATE_UP | (L.PREP_INTERLEAVED if wl.interleaved_w13 else 0)
+    W13 = P.moe_w4a16_prepare(qtype, w13["codes"], w13["scales"], w13.get("gs"), w13.get("bias"), flags)
+    s, e, n, loc = P.moe_align(torch.from_numpy(inp.topk_ids).cuda(), wl.expert_start, wl.n_local, B)
+    x = _bf16_dev(inp.x)
+    numel = M * wl.top_k
+    h = P.moe_w4a16_gemm(x, W13, s, e, n, numel, wl.top_k, B, cfg=cfg)
+    a_ref = P.moe_act(wl.act, h, W13.N // 2, loc.view(-1), wl.alpha, 7.0)
+    a = P.moe_w4a16_gemm_act(wl.act, x, W13, s, e, n, numel, wl.top_k, B, wl.alpha, 7.0, cfg=cfg)
+    torch.cuda.synchronize()
+    live = torch.from_numpy(np.nonzero(loc.cpu().numpy().reshape(-1) >= 0)[0]).cuda()
+    assert torch.equal(a[live], a_ref[live])

@@ -37,8 +37,8 @@ def test_small_layer_every_gemm_kernel(qtype):
     wl = W.small_workload(qtype)
     lw = W.make_weights(wl)
     layer = make_layer(wl, lw)
-    for M, B, cfg in [(7, 16, P.gemm_config(L.GEMM_DECODE, 0, 4, 4)),
-                      (7, 16, P.gemm_config(L.GEMM_DECODE, 0, 1, 0)),
+    for M, B, cfg in [(7, 16, P.gemm_config(L.GEMM_DECODE, 4, 4, 4)),
+                      (7, 16, P.gemm_config(L.GEMM_DECODE, 1, 1, 0)),
                       (90, 16, P.gemm_config(L.GEMM_MFMA, 1, 0, 0)),
                       (90, 32, P.gemm_config(L.GEMM_MFMA, 2, 0, 0)),
                       (300, 128, P.gemm_config(L.GEMM_MFMA, 4, 0, 0))]:
@@ -112,3 +112,14 @@ def test_config_layer_matches_oracle(cfg, M, n_sample):
     off = np.all((inp.topk_ids < wl.expert_start) | (inp.topk_ids >= wl.expert_start + wl.n_local), axis=1)
     assert np.all(got[off] == 0.0)
     assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("qtype", W.QTYPES)
+def test_small_layer_unfused_activation(qtype):
+    wl = W.small_workload(qtype)
+    lw = W.make_weights(wl)
+    layer = make_layer(wl, lw)
+    inp = W.make_inputs(wl, 130)
+    got = _forward(layer, inp, fused_act=False)
+    assert layer_violations(got, oracle_layer(wl, lw, inp)) == 0
+    assert np.array_equal(got, _forward(layer, inp))      # fused and unfused give the same bytes
