@@ -23,6 +23,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
     # no packed fp32 instructions (v_pk_*_f32) are generated for device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: otherwise the loop-carried accumulators are copied
+    # into AGPRs before every MFMA
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

@@ -83,6 +83,18 @@ template <> struct TileScale<MOE_Q_INT4_G128> {
 
 __device__ __forceinline__ uint32_t bits2(bf16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
 
+// Byte B of x as a float (v_cvt_f32_ubyteB).  Written out because the compiler otherwise folds
+// the nibble mask into a bit-field extract followed by a byte-0 convert, one instruction more.
+template <int B>
+__device__ __forceinline__ float ubyte_to_f32(uint32_t x) {
+  float r;
+  if constexpr (B == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x));
+  else if constexpr (B == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x));
+  else if constexpr (B == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x));
+  else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
 // Eight codes (one dword, k order) -> eight bf16 weights, scale folded in (the MFMA A operand).
 template <int QT>
 __device__ __forceinline__ u32x4_t dequant8(uint32_t w, float s) {
@@ -104,13 +116,14 @@ __device__ __forceinline__ u32x4_t dequant8(uint32_t w, float s) {
     o[2] = pack_bf16x2(p2[0] * s, p2[1] * s);
     o[3] = pack_bf16x2(p3[0] * s, p3[1] * s);
   } else {
-    // uint4b8: (u - 8) * s, exact in fp32 (4 x 8 significant bits), rounded once to bf16
+    // uint4b8: (u - 8) * s, exact in fp32 (4 x 8 significant bits), rounded once to bf16;
+    // even-k nibbles are the low nibbles of the four bytes, odd-k the high ones
     const uint32_t t0 = w & 0x0F0F0F0Fu, t1 = (w >> 4) & 0x0F0F0F0Fu;
     const float m8s = -8.0f * s;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      o[j] = pack_bf16x2(fmaf((float)((t0 >> (8 * j)) & 0xFFu), s, m8s),
-                         fmaf((float)((t1 >> (8 * j)) & 0xFFu), s, m8s));
+    o[0] = pack_bf16x2(fmaf(ubyte_to_f32<0>(t0), s, m8s), fmaf(ubyte_to_f32<0>(t1), s, m8s));
+    o[1] = pack_bf16x2(fmaf(ubyte_to_f32<1>(t0), s, m8s), fmaf(ubyte_to_f32<1>(t1), s, m8s));
+    o[2] = pack_bf16x2(fmaf(ubyte_to_f32<2>(t0), s, m8s), fmaf(ubyte_to_f32<2>(t1), s, m8s));
+    o[3] = pack_bf16x2(fmaf(ubyte_to_f32<3>(t0), s, m8s), fmaf(ubyte_to_f32<3>(t1), s, m8s));
   }
   return o;
 }

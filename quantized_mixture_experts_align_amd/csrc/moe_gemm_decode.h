@@ -30,7 +30,8 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode_kernel(GemmArgs a, int ge
   __shared__ int s_cnt, s_e;
   __shared__ f32x4_t red[KS > 1 ? KS - 1 : 1][NG][64];
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  // the wave index is uniform: keep it (and every LDS address derived from it) in scalar registers
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int NT = a.N / kTileN, KT = a.K / kTileK, kc = a.K / 8;
   const int NTA = ACT == kActNone ? NT : NT / 2;  // tiles to assign (gate tiles if fused)
   const int NS = (NTA + NGA - 1) / NGA;

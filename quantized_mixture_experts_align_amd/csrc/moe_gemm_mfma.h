@@ -22,14 +22,28 @@
 
 namespace moe {
 
-constexpr int kStages = 3;
-
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt[3:0] and
 // vmcnt[5:4] at bits 15:14; expcnt and lgkmcnt left at their maximum).
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt out of range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Pipeline depth: four stages where the LDS allows two or more workgroups per CU, three for the
+// 128-slot tile.
+template <int MG>
+constexpr int stages_for() { return MG >= 8 ? 3 : 4; }
+
+// Wait until this wave's loads of the current step have landed, given how many later steps'
+// loads (LPER instructions each) it has already issued.
+template <int LPER, int ST>
+__device__ __forceinline__ void wait_step(int later) {
+  if constexpr (ST >= 4) {
+    if (later >= 2) { wait_vm<2 * LPER>(); return; }
+  }
+  if (later >= 1) { wait_vm<LPER>(); return; }
+  wait_vm<0>();
 }
 
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -64,6 +78,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
   constexpr int SB = 4 * NG * 64;                          //   scales (64-B slot per tile)
   constexpr int STAGE = XB + WB + SB;
   constexpr int LW = 3 * NG;                               // weight + scale loads per wave and step
+  constexpr int kStages = stages_for<MG>();
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * STAGE];
   __shared__ int s_crow[BM];
   auto stage_ptr = [&](int stage) -> uint8_t* { return smem + stage * STAGE; };
@@ -75,7 +90,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
   if (mb * BM >= *a.ntpp) return;
   const int e = a.eids[mb];
   if (e < 0 || e >= a.E) return;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  // the wave index is uniform: keep it (and every LDS address derived from it) in scalar registers
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 
   if (tid < BM) {
     const int s = a.sorted[(int64_t)mb * BM + tid];
@@ -149,12 +165,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
       const int kt = kt0 + u;
       if (kt >= KT) break;
       // this wave's loads of step kt have landed once only later steps' loads are pending
-      static_assert(kStages == 3, "wait counts below assume three stages");
-      if (kt + 1 < KT) {
-        if (xwave) wait_vm<XL + LW>(); else wait_vm<LW>();
-      } else {
-        wait_vm<0>();
-      }
+      const int later = min(kStages - 2, KT - 1 - kt);
+      if (xwave) wait_step<XL + LW, kStages>(later); else wait_step<LW, kStages>(later);
       block_barrier();  // everyone's step kt is in LDS, and everyone is done with step kt-1
       if (kt + kStages - 1 < KT) issue(kt + kStages - 1, (u + kStages - 1) % kStages);
       const uint8_t* st = stage_ptr(u);
