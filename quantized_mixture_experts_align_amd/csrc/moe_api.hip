@@ -94,13 +94,16 @@ extern "C" int moe_w4a16_prepared_size(moe_qtype q, int32_t E, int32_t N, int32_
 // expert (if every slot were local) go to the decode kernel, larger counts to MFMA tiles of
 // 32/64/128 rows.  Counting every slot (not only the expected local share) keeps skewed routing,
 // where a few local experts take most slots, on the MFMA tiles that share weight reads.
+// 128-row tiles halve the dequantisation per flop against 64-row ones but leave half as many
+// workgroups; measured, they pay once an expert averages 256 rows and there are at least 8192
+// slots (64 full blocks), below that the smaller grid and the padding cost more.
 extern "C" int moe_choose_block_m(int64_t numel, int32_t n_local, int32_t* block_m) {
   MOE_REQUIRE(block_m && numel >= 0 && n_local >= 1, MOE_EINVAL, "moe_choose_block_m: bad arguments");
   const double rows = (double)numel / n_local;
   int b = 16;
   if (rows > 16) b = 32;
   if (rows > 48) b = 64;
-  if (rows >= 1024) b = 128;
+  if (rows >= 256 && numel >= 8192) b = 128;
   *block_m = b;
   return ok();
 }
@@ -126,11 +129,13 @@ extern "C" int moe_gemm_choose(const moe_weights* W, int64_t numel, int32_t bloc
     c.ng = 4;
     while (c.ng > 1 && blocks * ((nt + c.ng - 1) / c.ng) * c.ksplit < want) c.ng /= 2;
   } else {
-    // prefill: two 16-row tiles per wave (measured faster than four, whose register use
-    // leaves one wave per SIMD); one tile when the grid would not cover the CUs twice
+    // prefill: with 128-row blocks four 16-row tiles per wave (the dequantised weights then
+    // feed 32 MFMAs per k-step), else two; one when the grid would not cover the CUs twice.
+    // Measured on the int4, NVFP4 and MXFP4 prefill shapes.
     c.kernel = MOE_GEMM_MFMA;
     const int64_t mblocks = numel / block_m + std::min<int64_t>(numel, W->n_experts);
     c.ng = 2;
+    if (block_m >= 128 && ((int64_t)(nt + 15) / 16) * mblocks >= 2 * num_cus) c.ng = 4;
     if (((int64_t)(nt + 7) / 8) * mblocks < 2 * num_cus) c.ng = 1;
   }
   *cfg = c;
