@@ -7,7 +7,9 @@ combine) over one batch of seeded synthetic inputs already resident in HBM.  The
 workload is the int4 layer with biases, M=2304 tokens, E=8, top-2, H=512, I=1024.
 
 Timing: W untimed warm-up steps, then K steps replayed from a HIP graph of one step,
-bracketed by device synchronisation; value = tokens / second.  The roofline entry is for
+bracketed by device synchronisation; value = tokens / second.  "cold" repeats the replay with
+1 GiB streamed through the caches before each one (so the weights come from HBM, not from L2
+or the memory-side cache) and reports the median replay time.  The roofline entry is for
 the dominant kernel (the largest share of the layer's work): its average duration is taken
 with HIP events recorded around it on its own stream over K eager steps, and its algorithmic
 work per launch is the flops (prefill) or weight bytes (decode) it must process.  The CPU
@@ -33,11 +35,18 @@ METRIC = "MoE layer tokens/s + weight-stream GB/s (decode) and TFLOP/s (prefill)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
-GEMM_SRC = os.path.join(ROOT, "quantized_mixture_experts_align_amd", "csrc", "moe_gemm.hip")
+CSRC = os.path.join(ROOT, "quantized_mixture_experts_align_amd", "csrc")
+# every source the GEMM kernels are compiled from: a change to any of them voids old counters
+GEMM_SRCS = ["moe_gemm.hip", "moe_gemm_common.h", "moe_gemm_mfma.h", "moe_gemm_decode.h",
+             "moe_gemm_int4.hip", "moe_gemm_nvfp4.hip", "moe_gemm_mxfp4.hip", "moe_internal.h"]
+FLUSH_BYTES = 1 << 30          # streamed between cold steps: more than L2 + MALL
 
 
 def gemm_source_hash() -> str:
-    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in GEMM_SRCS:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def weight_bytes_per_expert(wl, proj: str) -> int:
@@ -146,6 +155,21 @@ def run_cell(cfg: int, M: int, steps: int, warmup: int, want_cpu: bool, seed=Non
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - t0) / steps
 
+    # ---- cold: before each replay stream 1 GiB through the caches, events around the replay
+    # only; the median over the replays
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(max(50, min(steps, 200))):
+        flush.zero_()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        g.replay()
+        s1.record(stream)
+        cold.append((s0, s1))
+    torch.cuda.synchronize()
+    cold_s = float(np.median([a.elapsed_time(b) for a, b in cold])) * 1e-3
+    del flush
+
     # ---- dominant kernel: HIP events on the launch stream around each GEMM, eager steps
     import quantized_mixture_experts_align_amd.ops as ops
     ev = {k: [] for k in ("gemm13", "gemm2")}
@@ -198,14 +222,28 @@ def run_cell(cfg: int, M: int, steps: int, warmup: int, want_cpu: bool, seed=Non
                    "n_local": wl.n_local, "n_global": wl.n_global, "H": wl.H, "I": wl.I,
                    "block_m": ws.block_m, "live_slots": live, "touched_experts": touched},
         "roofline": roof,
-        "layer": {"weight_GBps": round((bytes_13 + bytes_2) / step_s / 1e9, 1),
+        "layer": {**layer_fracs(bytes_13 + bytes_2, flops_13 + flops_2, step_s),
+                  "weight_GBps": round((bytes_13 + bytes_2) / step_s / 1e9, 1),
                   "TFLOPs": round((flops_13 + flops_2) / step_s / 1e12, 2),
                   "gemm13_us": round(d13 * 1e6, 2), "gemm2_us": round(dur["gemm2"] * 1e6, 2),
                   "weight_bytes": bytes_13 + bytes_2, "flops": flops_13 + flops_2},
+        "cold": {"ms_per_step": round(cold_s * 1e3, 4), "tokens_per_s": round(M / cold_s, 1),
+                 "replays": len(cold), "note": "median graph replay after streaming 1 GiB",
+                 **layer_fracs(bytes_13 + bytes_2, flops_13 + flops_2, cold_s)},
     }
     if want_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, lw, inp)
     return out
+
+
+def layer_fracs(nbytes: float, flops: float, t: float) -> dict:
+    """Fractions of the MI355X roofline reached by a whole step: of HBM peak on the touched
+    weight bytes, of dense bf16 MFMA peak on the live-slot flops, and of the binding bound
+    max(t_hbm, t_mfma) (1.0 = on the roofline)."""
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    return {"hbm_frac": round(t_hbm / t, 4), "mfma_frac": round(t_mfma / t, 4),
+            "roof_frac": round(max(t_hbm, t_mfma) / t, 4)}
 
 
 def layer_uses_mfma(layer, M, P) -> bool:
@@ -221,6 +259,9 @@ def main() -> int:
     ap.add_argument("--M", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="one line per configuration cell")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only copy a buffer of this many MiB 10 times (reference kernel of known "
+                         "traffic for calibrating the HBM byte counters)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this layer is one GPU's expert slice and no multi-GPU "
@@ -230,6 +271,15 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X (no GPU visible)", file=sys.stderr)
         return 1
+    if a.copy_mib:
+        n = a.copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 10}), flush=True)
+        return 0
     import workloads as W
     if a.sweep:
         for cfg, wl in W.CONFIGS.items():

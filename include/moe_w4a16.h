@@ -175,6 +175,9 @@ typedef struct moe_gemm_config {
   int32_t ksplit;         /* DECODE: waves splitting K in one workgroup: 1, 2 or 4         */
   int32_t gemv_rows;      /* DECODE: blocks with at most this many live slots use dot
                              products (0..4, and gemv_rows * K * 2 <= 32 KiB)              */
+  int32_t group_m;        /* MFMA: align blocks per workgroup group, 0..64 (0 = chosen from
+                             the shapes); a group's workgroups run on one XCD, sharing its
+                             L2.  Launch order only: results do not depend on it             */
 } moe_gemm_config;
 
 /* Host heuristics (pure host functions).  moe_choose_block_m: block_m for the align from the

@@ -28,7 +28,7 @@ class MoeWeights(C.Structure):
 
 class MoeGemmConfig(C.Structure):
     _fields_ = [("kernel", C.c_int32), ("ng", C.c_int32), ("ksplit", C.c_int32),
-                ("gemv_rows", C.c_int32)]
+                ("gemv_rows", C.c_int32), ("group_m", C.c_int32)]
 
 
 class MoeError(RuntimeError):

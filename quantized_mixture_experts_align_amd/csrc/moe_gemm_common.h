@@ -32,6 +32,7 @@ struct GemmArgs {
   const int32_t* ntpp;
   int32_t numel, top_k, block_m, N, K, E;
   float alpha, limit;  // activation parameters of the fused gate/up epilogue
+  int32_t group_m;     // MFMA: align blocks per XCD workgroup group
 };
 
 // Fused gate/up epilogue: the GEMM's output tiles come in (gate, up) pairs held by the same lane;

@@ -30,10 +30,12 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Pipeline depth: four stages where the LDS allows two or more workgroups per CU, three for the
-// 128-slot tile.
+// Pipeline depth.  Measured on all prefill shapes: two stages (double buffering) beat three and
+// four, because the smaller LDS footprint lets more workgroups share a CU and hide each other's
+// load latency (a workgroup runs only K/64 steps, 8 for K = 512), which deeper per-workgroup
+// prefetch does not.
 template <int MG>
-constexpr int stages_for() { return MG >= 8 ? 3 : 4; }
+constexpr int stages_for() { return 2; }
 
 // Wait until this wave's loads of the current step have landed, given how many later steps'
 // loads (LPER instructions each) it has already issued.
@@ -63,6 +65,28 @@ __device__ __forceinline__ void dma_to_lds(const void* g, void* lds) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(g) : "memory", "m0");
 }
 
+// Workgroups go to the 8 XCDs round-robin by launch index, and each XCD has its own L2.  The
+// launch index is mapped to a logical (align block, column block) so that workgroups sharing
+// data run on one XCD: a group is GM consecutive align blocks x all nblk column blocks (column
+// block outer, so the GM workgroups reading the same weight tiles are adjacent; all of them read
+// the group's activation rows), and whole groups go round-robin over the XCDs.  The map is a
+// bijection on [0, gridDim.x): a trailing partial round keeps the identity.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void grouped_block(int nblk, int gm_max, int& mb, int& nb) {
+  const int G = (int)gridDim.x, P = (int)blockIdx.x;
+  const int C = gm_max * nblk;
+  const int full = (G / (kXcds * C)) * (kXcds * C);
+  int L = P;
+  if (P < full) {
+    const int x = P % kXcds, j = P / kXcds;
+    L = ((j / C) * kXcds + x) * C + j % C;
+  }
+  const int g = L / C, r = L - g * C;
+  const int gm = min(gm_max, G / nblk - g * gm_max);
+  mb = g * gm_max + r % gm;
+  nb = r / gm;
+}
+
 template <int QT, bool BIAS, int MG, int NG, int ACT>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
   static_assert(ACT == kActNone || NG % 2 == 0, "the fused epilogue pairs gate and up tiles");
@@ -86,7 +110,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
   const int NT = a.N / kTileN, KT = a.K / kTileK;
   const int NTA = ACT == kActNone ? NT : NT / 2;          // tiles to assign (gate tiles if fused)
   const int nblk = (NTA + 4 * NGA - 1) / (4 * NGA);
-  const int mb = blockIdx.x / nblk, nb = blockIdx.x - mb * nblk;
+  int mb, nb;
+  grouped_block(nblk, a.group_m, mb, nb);
   if (mb * BM >= *a.ntpp) return;
   const int e = a.eids[mb];
   if (e < 0 || e >= a.E) return;

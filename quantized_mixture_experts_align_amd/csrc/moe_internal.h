@@ -42,6 +42,13 @@ inline __host__ __device__ int scale_bytes_per_tile(int q) {
 
 inline __host__ __device__ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// MFMA GEMM: align blocks per XCD workgroup group (launch order only, never results)
+inline int default_group_m(int64_t numel, int block_m) {
+  (void)numel;
+  (void)block_m;
+  return 1;
+}
+
 // ---------------------------------------------------------------------------- device math
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

@@ -111,7 +111,7 @@ class MoELayer:
             out=(ws.sorted_ids, ws.expert_ids, ws.ntpp, ws.slot_local))
         if fused_act:
             if cfg13.ng < 2:
-                cfg13 = ops.gemm_config(cfg13.kernel, 2, cfg13.ksplit, cfg13.gemv_rows)
+                cfg13 = ops.gemm_config(cfg13.kernel, 2, cfg13.ksplit, cfg13.gemv_rows, cfg13.group_m)
             ops.moe_w4a16_gemm_act(self.act, x, self.W13, sorted_ids, eids, ntpp, numel, self.top_k, B,
                                    self.alpha, self.limit, out=ws.a, cfg=cfg13)
         else:

@@ -126,8 +126,9 @@ def moe_norm_weight(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> torc
     return out
 
 
-def gemm_config(kernel: int = L.GEMM_AUTO, ng: int = 0, ksplit: int = 0, gemv_rows: int = 0):
-    return L.MoeGemmConfig(kernel, ng, ksplit, gemv_rows)
+def gemm_config(kernel: int = L.GEMM_AUTO, ng: int = 0, ksplit: int = 0, gemv_rows: int = 0,
+                group_m: int = 0):
+    return L.MoeGemmConfig(kernel, ng, ksplit, gemv_rows, group_m)
 
 
 def gemm_choose(W: PreparedWeights, numel: int, block_m: int, num_cus: int = 0) -> L.MoeGemmConfig:
