@@ -159,8 +159,11 @@ int moe_norm_weight(const uint16_t* w, int32_t H, uint16_t* out, hipStream_t str
 typedef enum {
   MOE_GEMM_AUTO = 0,
   MOE_GEMM_DECODE = 1,    /* block_m <= 16: persistent workgroups over (live block, strip of ng
-                             16-row weight tiles), K split over ksplit waves; dot products for
-                             blocks of <= gemv_rows live slots, one 16-slot MFMA column otherwise */
+                             16-row weight tiles), K split over ksplit waves.  gemv_rows = 0:
+                             the streaming kernel (one 16-slot MFMA column per tile, one
+                             uninterrupted prefetch ring per wave across its items);
+                             gemv_rows > 0: dot products for blocks of <= gemv_rows live slots,
+                             the MFMA column otherwise                                        */
   MOE_GEMM_MFMA = 2       /* block_m in {16,32,64,128}: 4 waves x ng 16-row tiles x all slots of
                              the block, bf16 MFMA 16x16x32, activations through an LDS ring   */
 } moe_gemm_kernel;
@@ -172,7 +175,8 @@ typedef enum {
 typedef struct moe_gemm_config {
   int32_t kernel;         /* moe_gemm_kernel                                               */
   int32_t ng;             /* 16-row weight tiles per wave: 1, 2 or 4                       */
-  int32_t ksplit;         /* DECODE: waves splitting K in one workgroup: 1, 2 or 4         */
+  int32_t ksplit;         /* DECODE: waves splitting K in one workgroup: 1, 2, 4 (or 8 when
+                             gemv_rows = 0); capped at K/64 by the streaming kernel           */
   int32_t gemv_rows;      /* DECODE: blocks with at most this many live slots use dot
                              products (0..4, and gemv_rows * K * 2 <= 32 KiB)              */
   int32_t group_m;        /* MFMA: align blocks per workgroup group, 0..64 (0 = chosen from

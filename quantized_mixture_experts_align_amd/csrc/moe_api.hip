@@ -116,18 +116,17 @@ extern "C" int moe_gemm_choose(const moe_weights* W, int64_t numel, int32_t bloc
   moe_gemm_config c{};
   const int nt = W->N / kTileN;
   if (block_m <= 16) {
-    // decode: stream the touched experts' weights.  Enough waves to keep every CU streaming
-    // (about 8 per CU) even if only min(numel, E) blocks are live, K split over the waves of a
-    // workgroup, and as many 16-row tiles per wave as that allows (activations are reused
-    // across a wave's tiles).
+    // decode: the streaming kernel over min(numel, E) live blocks.  Measured (cold weights, NVFP4
+    // and MXFP4 slices): four 16-row tiles per wave once about 8 blocks are live, else two; then
+    // the smallest K split that gives at least 24 waves per CU.  The one-column MFMA streams
+    // faster than the dot-product path (gemv_rows > 0), which stays available.
     c.kernel = MOE_GEMM_DECODE;
-    const int kt = W->K / kTileK;
-    c.ksplit = kt >= 16 ? 4 : (kt >= 4 ? 2 : 1);
-    c.gemv_rows = 0;  // measured: the one-column MFMA path streams faster than dot products
+    c.gemv_rows = 0;
     const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(numel, W->n_experts));
-    const int64_t want = 8ll * num_cus;
-    c.ng = 4;
-    while (c.ng > 1 && blocks * ((nt + c.ng - 1) / c.ng) * c.ksplit < want) c.ng /= 2;
+    c.ng = blocks >= 8 ? 4 : 2;
+    const int64_t items = blocks * ((nt + c.ng - 1) / c.ng);
+    c.ksplit = 1;
+    while (c.ksplit < 8 && items * c.ksplit < 24ll * num_cus) c.ksplit *= 2;
   } else {
     // prefill: with 128-row blocks four 16-row tiles per wave (the dequantised weights then
     // feed 32 MFMAs per k-step), else two; one when the grid would not cover the CUs twice.

@@ -76,6 +76,13 @@ static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64
                 c.gemv_rows);
     MOE_REQUIRE((int64_t)c.gemv_rows * W->K * 2 <= 32768, MOE_EUNSUPPORTED,
                 "moe_w4a16_gemm: gemv_rows=%d x K=%d exceeds the 32 KiB activation stage", c.gemv_rows, W->K);
+    if (c.gemv_rows == 0) {  // one-column MFMA on every block: the streaming kernel
+      switch (W->qtype) {
+        case MOE_Q_INT4_G128: return launch_gemm_stream<MOE_Q_INT4_G128>(bias, act, a, c, (int)cap_blocks, cus, stream);
+        case MOE_Q_NVFP4_G16: return launch_gemm_stream<MOE_Q_NVFP4_G16>(bias, act, a, c, (int)cap_blocks, cus, stream);
+        default: return launch_gemm_stream<MOE_Q_MXFP4_G32>(bias, act, a, c, (int)cap_blocks, cus, stream);
+      }
+    }
     switch (W->qtype) {
       case MOE_Q_INT4_G128: return launch_gemm_decode<MOE_Q_INT4_G128>(bias, act, a, c, (int)cap_blocks, cus, stream);
       case MOE_Q_NVFP4_G16: return launch_gemm_decode<MOE_Q_NVFP4_G16>(bias, act, a, c, (int)cap_blocks, cus, stream);

@@ -173,6 +173,9 @@ template <int QT>
 int launch_gemm_decode(bool bias, int act, const GemmArgs& a, const moe_gemm_config& c, int cap_blocks,
                        int num_cus, hipStream_t st);
 template <int QT>
+int launch_gemm_stream(bool bias, int act, const GemmArgs& a, const moe_gemm_config& c, int cap_blocks,
+                       int num_cus, hipStream_t st);
+template <int QT>
 int launch_gemm_mfma(bool bias, int act, const GemmArgs& a, const moe_gemm_config& c, int cap_blocks,
                      hipStream_t st);
 int device_cu_count();

@@ -1,0 +1,253 @@
+// gemm_stream: grouped W4A16 GEMM for align blocks of at most 16 slots (decode batches), whose
+// cost is streaming the touched experts' weights from HBM.  Built to keep an uninterrupted
+// stream of weight loads in flight.
+//
+// Work item = (live align block, strip of NG 16-row weight tiles).  A persistent workgroup walks
+// a contiguous range of items; its KS waves split K (wave w owns k-tiles [KT w/KS, KT (w+1)/KS)).
+// Each wave runs ONE flat sequence of k-steps over all of its items with a register ring D steps
+// deep (per step: the NG tiles' codes -- 8 B per lane, one 512-B wave load per tile --, their
+// group scales and the step's 16-slot activation column), so the next item's first loads are in
+// flight while the previous item finishes: there is no per-item pipeline drain.  Everything an
+// item needs besides the streamed operands (expert, slot rows, NVFP4 global scale, bias) is
+// staged in LDS when the workgroup starts (the launch gives no workgroup more than kWin items),
+// so inside the stream nothing waits on a vector-memory load other than the ring's own (a load
+// of bias in the epilogue would wait for every weight load issued before it).
+//
+// Per step and tile each lane feeds one v_mfma_f32_16x16x32_bf16 per k-substep: weights as the A
+// operand (rows = output features), the 16 slots of the block as the B operand (columns; dead
+// columns read token 0 and are never stored).  At an item's last step the waves' partial sums are
+// added through LDS in a fixed wave order (double-buffered by item parity: one barrier per item)
+// and wave 0 applies global scale, bias and (fused gate/up) the activation, and writes the
+// block's live rows.
+#pragma once
+
+#include "moe_gemm_common.h"
+
+namespace moe {
+
+constexpr int kWin = 32;  // most items per workgroup (their metadata is staged in LDS)
+
+// LDS-only barrier: waits for this wave's LDS traffic, not for its vector-memory loads (the ring).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int QT, bool BIAS, int NG, int KS, int ACT>
+__global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
+  static_assert(ACT == kActNone || NG % 2 == 0, "the fused epilogue pairs gate and up tiles");
+  constexpr int NGA = ACT == kActNone ? NG : NG / 2;
+  constexpr int D = NG >= 4 ? 4 : 8;  // ring depth (k-steps): about 9 KB of weights per wave
+  __shared__ int t_e[kWin];
+  __shared__ float t_gs[kWin];
+  __shared__ int t_row[kWin][16];                  // slot of each column of the block, -1 = dead
+  __shared__ uint16_t t_bias[BIAS ? kWin : 1][NG][16];
+  __shared__ f32x4_t red[2][KS > 1 ? KS - 1 : 1][NG][64];
+
+  // the wave index is uniform: keep it (and everything derived from it) in scalar registers
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int NT = a.N / kTileN, KT = a.K / kTileK;
+  const int NTA = ACT == kActNone ? NT : NT / 2;  // tiles to assign (gate tiles if fused)
+  const int NS = (NTA + NGA - 1) / NGA;           // strips per block
+  const int B = a.block_m;
+  const int items = (*a.ntpp / B) * NS;
+  const int per = (items + (int)gridDim.x - 1) / (int)gridDim.x;  // <= kWin by the launch
+  const int i0 = (int)blockIdx.x * per, i1 = min(items, i0 + per);
+  if (i0 >= i1) return;
+  const int kt0 = KT * w / KS, kt1 = KT * (w + 1) / KS, L = kt1 - kt0;  // L >= 1: KT >= KS
+  const int m = lane & 15, j8 = 8 * (lane >> 4);
+
+  auto tile_of = [&](int strip, int g) {
+    const int t = min(strip * NGA + (g < NGA ? g : g - NGA), NTA - 1);
+    return g < NGA ? t : t + NTA;
+  };
+
+  int par = 0;
+  {
+    const int wb = i0, wn = min(kWin, i1 - i0);  // (the min only guards the LDS table)
+    for (int t = tid; t < wn * 16; t += 64 * KS) {
+      const int q = t >> 4, mm = t & 15, b = (wb + q) / NS;
+      int s = -1;
+      if (mm < B) {
+        s = a.sorted[(int64_t)b * B + mm];
+        if (s < 0 || s >= a.numel) s = -1;
+      }
+      t_row[q][mm] = s;
+      if (mm == 0) {
+        const int e = a.eids[b];
+        const bool ok = e >= 0 && e < a.E;
+        t_e[q] = ok ? e : -1;
+        t_gs[q] = (QT == MOE_Q_NVFP4_G16 && ok) ? a.gs[e] : 1.0f;
+      }
+    }
+    if constexpr (BIAS) {
+      for (int t = tid; t < wn * NG * 16; t += 64 * KS) {
+        const int q = t / (NG * 16), g = (t >> 4) % NG, r = t & 15;
+        const int it = wb + q, b = it / NS, e = a.eids[b];
+        t_bias[q][g][r] = (e >= 0 && e < a.E) ? a.bias[(int64_t)e * a.N + tile_of(it - b * NS, g) * kTileN + r] : 0;
+      }
+    }
+    __syncthreads();
+
+    // ---- issue side: the step (iq, ikt) whose operands are loaded next
+    int iq = 0, ikt = kt0;
+    const u32x2_t* wp[NG];
+    const uint8_t* sp[NG];
+    const uint16_t* xp;
+    auto enter = [&](int q) {
+      const int it = wb + q, b = it / NS, strip = it - b * NS;
+      const int e = max(t_e[q], 0);  // a dead item still loads valid memory; nothing is stored
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int64_t tile = (int64_t)e * NT + tile_of(strip, g);
+        wp[g] = reinterpret_cast<const u32x2_t*>(a.codes + tile * KT * kTileBytes) + lane;
+        sp[g] = a.scales + (QT == MOE_Q_INT4_G128 ? tile * (KT / 2) * 32 : tile * KT * scale_bytes_per_tile(QT));
+      }
+      const int s = t_row[q][m];
+      xp = a.A + (int64_t)(s >= 0 ? s / a.top_k : 0) * a.lda + j8;
+    };
+    u32x2_t rq[D][NG];
+    TileScale<QT> rs[D][NG];
+    u32x4_t rx[D][2];
+    // load the issue step into ring slot u, then advance; past the wave's last step the last step
+    // is loaded again (valid addresses, unused), which keeps every slot's load count the same
+    auto issue = [&](int u) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        rq[u][g] = wp[g][(int64_t)ikt * 64];
+        rs[u][g].load(sp[g], ikt, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) rx[u][i] = *reinterpret_cast<const u32x4_t*>(xp + ikt * kTileK + 32 * i);
+      if (++ikt == kt1) {
+        if (iq + 1 < wn) {
+          ++iq;
+          ikt = kt0;
+          enter(iq);
+        } else {
+          ikt = kt1 - 1;
+        }
+      }
+    };
+
+    // ---- compute side
+    f32x4_t acc[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    int cq = 0, cs = 0;
+    auto finish = [&](int q) {  // the item's partial sums are complete in every wave
+      if constexpr (KS > 1) {
+        if (w > 0)
+#pragma unroll
+          for (int g = 0; g < NG; ++g) red[par][w - 1][g][lane] = acc[g];
+        lds_barrier();
+        if (w == 0)
+          for (int v = 0; v < KS - 1; ++v)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) acc[g] += red[par][v][g][lane];
+        par ^= 1;
+      }
+      const int e = t_e[q], s = t_row[q][m];
+      if (w == 0 && e >= 0 && s >= 0) {
+        const int strip = (wb + q) % NS;
+        const float gs = t_gs[q];
+        const int r0 = 4 * (lane >> 4);  // D[n][m]: this lane holds rows r0 .. r0+3 of column m
+        auto fin = [&](float v, int g, int r) {
+          if constexpr (QT == MOE_Q_NVFP4_G16) v *= gs;
+          if constexpr (BIAS) v += bf16_to_f32(t_bias[q][g][r]);
+          return v;
+        };
+#pragma unroll
+        for (int g = 0; g < NGA; ++g) {
+          if (strip * NGA + g >= NTA) break;
+          float v[4];
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            v[qq] = fin(acc[g][qq], g, r0 + qq);
+            if constexpr (ACT != kActNone) v[qq] = fused_act<ACT>(v[qq], fin(acc[g + NGA][qq], g + NGA, r0 + qq), a);
+          }
+          *reinterpret_cast<u32x2_t*>(a.C + (int64_t)s * a.ldc + tile_of(strip, g) * kTileN + r0) =
+              u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < NG; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    };
+    auto compute = [&](int u) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+          acc[g] = mfma(dequant8<QT>(rq[u][g][i], rs[u][g].s(i, lane)), rx[u][i], acc[g]);
+      if (++cs == L) {
+        finish(cq);
+        cs = 0;
+        ++cq;
+      }
+    };
+
+    enter(0);
+#pragma unroll
+    for (int u = 0; u < D; ++u) issue(u);
+    const int total = wn * L;
+    for (int j0 = 0; j0 < total; j0 += D) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        if (j0 + u < total) {
+          compute(u);
+          issue(u);
+        }
+      }
+    }
+  }
+}
+
+template <int QT, bool BIAS, int NG, int ACT>
+static int launch_stream_ng(const GemmArgs& a, int ks, int grid, hipStream_t st) {
+  switch (ks) {
+    case 1: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 1, ACT>), dim3(grid), dim3(64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 2, ACT>), dim3(grid), dim3(128), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 4, ACT>), dim3(grid), dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 8, ACT>), dim3(grid), dim3(512), 0, st, a); break;
+    default: return fail(MOE_EINVAL, "moe_w4a16_gemm: ksplit=%d (1, 2, 4 or 8)", ks);
+  }
+  return check_launch("moe_w4a16_gemm (decode stream)");
+}
+
+template <int QT, bool BIAS, int ACT>
+static int launch_stream_b(const GemmArgs& a, const moe_gemm_config& c, int grid, hipStream_t st) {
+  if constexpr (ACT == kActNone) {
+    if (c.ng == 1) return launch_stream_ng<QT, BIAS, 1, ACT>(a, c.ksplit, grid, st);
+  }
+  switch (c.ng) {
+    case 2: return launch_stream_ng<QT, BIAS, 2, ACT>(a, c.ksplit, grid, st);
+    case 4: return launch_stream_ng<QT, BIAS, 4, ACT>(a, c.ksplit, grid, st);
+    default: return fail(MOE_EINVAL, "moe_w4a16_gemm: decode ng=%d (1, 2 or 4; 2 or 4 with a fused activation)", c.ng);
+  }
+}
+
+// Persistent grid: about 8 waves per CU and never more workgroups than items, but at least
+// enough that no workgroup gets more than kWin items.
+template <int QT>
+int launch_gemm_stream(bool bias, int act, const GemmArgs& a, const moe_gemm_config& c, int cap_blocks,
+                       int num_cus, hipStream_t st) {
+  const int NT = a.N / kTileN, KT = a.K / kTileK;
+  moe_gemm_config cc = c;  // every wave needs at least one k-tile: ksplit is capped at K/64
+  while (cc.ksplit > 1 && cc.ksplit > KT) cc.ksplit /= 2;
+  const int nta = act == kActNone ? NT : NT / 2, nga = act == kActNone ? c.ng : c.ng / 2;
+  const int ns = (nta + nga - 1) / std::max(nga, 1);
+  const int64_t max_items = (int64_t)cap_blocks * ns;
+  const int64_t want = (int64_t)num_cus * std::max(1, 8 / std::max(cc.ksplit, 1));
+  const int64_t grid64 = std::max<int64_t>({1, std::min<int64_t>(max_items, want), (max_items + kWin - 1) / kWin});
+  if (grid64 >= (1ll << 31)) return fail(MOE_EUNSUPPORTED, "moe_w4a16_gemm: decode grid too large");
+  const int grid = (int)grid64;
+  switch (act) {
+    case kActNone:
+      return bias ? launch_stream_b<QT, true, kActNone>(a, cc, grid, st) : launch_stream_b<QT, false, kActNone>(a, cc, grid, st);
+    case kActSilu:
+      return bias ? launch_stream_b<QT, true, kActSilu>(a, cc, grid, st) : launch_stream_b<QT, false, kActSilu>(a, cc, grid, st);
+    default:
+      return bias ? launch_stream_b<QT, true, kActSwiglu>(a, cc, grid, st) : launch_stream_b<QT, false, kActSwiglu>(a, cc, grid, st);
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,7 @@
+// Instantiation of the streaming decode GEMM for nvfp4 weights (one translation unit per format so
+// the kernel variants compile in parallel).
+#include "moe_gemm_stream.h"
+
+namespace moe {
+template int launch_gemm_stream<MOE_Q_NVFP4_G16>(bool, int, const GemmArgs&, const moe_gemm_config&, int, int, hipStream_t);
+}  // namespace moe

@@ -107,7 +107,7 @@ def test_gemm_choose_contract(N, K, E):
     W = _W(1, E, N, K)
     for numel in [1, 8, 64, 512]:
         c = P.gemm_choose(W, numel, 16, 256)
-        assert c.kernel == L.GEMM_DECODE and c.ksplit in (1, 2, 4) and 0 <= c.gemv_rows <= 4
+        assert c.kernel == L.GEMM_DECODE and c.ksplit in (1, 2, 4, 8) and 0 <= c.gemv_rows <= 4
         assert c.gemv_rows * K * 2 <= 65536
     last = 4
     for numel, B in [(512, 32), (2048, 64), (8192, 128), (32768, 128), (1 << 20, 128)]:

@@ -65,6 +65,9 @@ CFGS = {
     "decode_gemv": (16, P.gemm_config(L.GEMM_DECODE, 4, 4, 4)),
     "decode_mfma": (16, P.gemm_config(L.GEMM_DECODE, 2, 2, 0)),
     "decode_k1": (16, P.gemm_config(L.GEMM_DECODE, 1, 1, 2)),
+    "decode_stream_ks8": (16, P.gemm_config(L.GEMM_DECODE, 2, 8, 0)),
+    "decode_stream_ng4": (16, P.gemm_config(L.GEMM_DECODE, 4, 1, 0)),
+    "decode_stream_ng1": (16, P.gemm_config(L.GEMM_DECODE, 1, 4, 0)),
     "mfma16": (16, P.gemm_config(L.GEMM_MFMA, 1, 0, 0)),
     "mfma32": (32, P.gemm_config(L.GEMM_MFMA, 2, 0, 0)),
     "mfma64": (64, P.gemm_config(L.GEMM_MFMA, 4, 0, 0)),
@@ -98,8 +101,9 @@ def test_mfma_result_is_independent_of_tile_width(qtype):
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
-def test_decode_is_reproducible():
-    cfg = P.gemm_config(L.GEMM_DECODE, 2, 4, 4)
+@pytest.mark.parametrize("gemv_rows", [4, 0])
+def test_decode_is_reproducible(gemv_rows):
+    cfg = P.gemm_config(L.GEMM_DECODE, 2, 4, gemv_rows)
     a = _gemm_case("nvfp4_g16", 13, 3, 16, cfg)[2]
     b = _gemm_case("nvfp4_g16", 13, 3, 16, cfg)[2]
     assert torch.equal(a, b)
