@@ -117,6 +117,118 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   }
 }
 
+// Single pass for top_k <= TK and rows of at most CP * blockDim.x chunks of 8 columns.  Every
+// operand of the token is requested up front -- slot flags, weights, norm weight and the slots'
+// y chunks (with `spec`, also the chunks of slots that may be dead, so that nothing waits for
+// the flags; their values are never used) -- so a token costs one round trip to memory, and y
+// stays in registers between the norm's reduction and the weighted sum (read once).  The fp32
+// operations and their order per output are those of combine_kernel.
+template <bool NORM, int TK, int CP>
+__global__ __launch_bounds__(256) void combine1_kernel(
+    const uint16_t* __restrict__ y, const float* __restrict__ gw, const int32_t* __restrict__ slot_local,
+    const uint16_t* __restrict__ nw, float eps, int32_t top_k, int32_t H, int32_t spec,
+    uint16_t* __restrict__ out) {
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, T = blockDim.x;
+  __shared__ float red[4][TK];
+  __shared__ float fac[TK], gl[TK];
+  const int chunks = H >> 3;
+  uint32_t live = 0;
+  float g[TK];
+#pragma unroll
+  for (int s = 0; s < TK; ++s) {
+    g[s] = 0.f;
+    if (s < top_k) {
+      g[s] = gw[t * top_k + s];
+      if (slot_local[t * top_k + s] >= 0) live |= 1u << s;
+    }
+  }
+  uint4 v[TK][CP], nv[CP];
+#pragma unroll
+  for (int c = 0; c < CP; ++c) {
+    const int col = tid + c * T;
+    nv[c] = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+    if (NORM && col < chunks) nv[c] = *reinterpret_cast<const uint4*>(nw + col * 8);
+#pragma unroll
+    for (int s = 0; s < TK; ++s) {
+      v[s][c] = make_uint4(0u, 0u, 0u, 0u);
+      if (s < top_k && col < chunks && (spec || ((live >> s) & 1)))
+        v[s][c] = *reinterpret_cast<const uint4*>(y + (t * top_k + s) * (int64_t)H + col * 8);
+    }
+  }
+  float f[TK];
+  if (NORM) {
+#pragma unroll
+    for (int s = 0; s < TK; ++s) {
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < CP; ++c) {
+        if (tid + c * T >= chunks || !((live >> s) & 1)) continue;
+        const uint32_t v4[4] = {v[s][c].x, v[s][c].y, v[s][c].z, v[s][c].w};
+        const uint32_t n4[4] = {nv[c].x, nv[c].y, nv[c].z, nv[c].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float a = bf16_lo(v4[j]) * bf16_lo(n4[j]), b = bf16_hi(v4[j]) * bf16_hi(n4[j]);
+          ss = fmaf(a, a, ss);
+          ss = fmaf(b, b, ss);
+        }
+      }
+      for (int d = 32; d >= 1; d >>= 1) ss += __shfl_xor(ss, d);
+      if (lane == 0 && s < top_k) red[w][s] = ss;
+      if (tid == 0) gl[s] = g[s];
+    }
+    __syncthreads();
+    if (tid < top_k) {
+      float ssum = 0.f;
+      for (int i = 0; i < T / 64; ++i) ssum += red[i][tid];
+      fac[tid] = ((live >> tid) & 1) ? gl[tid] / sqrtf(ssum / (float)H + eps) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < TK; ++s) f[s] = s < top_k ? fac[s] : 0.f;
+  } else {
+#pragma unroll
+    for (int s = 0; s < TK; ++s) f[s] = g[s];
+  }
+#pragma unroll
+  for (int c = 0; c < CP; ++c) {
+    const int col = tid + c * T;
+    if (col >= chunks) break;
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+    const uint32_t n4[4] = {nv[c].x, nv[c].y, nv[c].z, nv[c].w};
+#pragma unroll
+    for (int s = 0; s < TK; ++s) {
+      if (s >= top_k || !((live >> s) & 1)) continue;
+      const uint32_t v4[4] = {v[s][c].x, v[s][c].y, v[s][c].z, v[s][c].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (NORM) {
+          acc[2 * j] = fmaf(f[s], bf16_lo(v4[j]) * bf16_lo(n4[j]), acc[2 * j]);
+          acc[2 * j + 1] = fmaf(f[s], bf16_hi(v4[j]) * bf16_hi(n4[j]), acc[2 * j + 1]);
+        } else {
+          acc[2 * j] = fmaf(f[s], bf16_lo(v4[j]), acc[2 * j]);
+          acc[2 * j + 1] = fmaf(f[s], bf16_hi(v4[j]), acc[2 * j + 1]);
+        }
+      }
+    }
+    *reinterpret_cast<uint4*>(out + t * H + col * 8) =
+        make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                   pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+  }
+}
+
+template <bool NORM, int TK>
+static void launch_combine1(int CP, int T, int64_t M, const uint16_t* y, const float* gw, const int32_t* sl,
+                            const uint16_t* nw, float eps, int top_k, int H, int spec, uint16_t* out,
+                            hipStream_t st) {
+  if (CP == 1)
+    hipLaunchKernelGGL((combine1_kernel<NORM, TK, 1>), dim3((unsigned)M), dim3(T), 0, st, y, gw, sl, nw, eps, top_k, H, spec, out);
+  else
+    hipLaunchKernelGGL((combine1_kernel<NORM, TK, 2>), dim3((unsigned)M), dim3(T), 0, st, y, gw, sl, nw, eps, top_k, H, spec, out);
+}
+
 __global__ void norm_weight_kernel(const uint16_t* __restrict__ w, int32_t H, uint16_t* __restrict__ out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < H) out[i] = f32_to_bf16(1.0f + bf16_to_f32(w[i]));
@@ -163,6 +275,22 @@ extern "C" int moe_combine(const uint16_t* y, const float* topk_weights, const i
   MOE_REQUIRE(y && topk_weights && slot_local_ids && out, MOE_EINVAL, "moe_combine: null pointer");
   MOE_REQUIRE(aligned16(y) && aligned16(out) && (!norm_w || aligned16(norm_w)), MOE_EUNSUPPORTED,
               "moe_combine: bf16 tensors must be 16-byte aligned");
+  // single pass when a token's slots fit in registers: top_k <= 8, H <= 2 * 256 * 8
+  const int chunks = H / 8;
+  if (top_k <= 8 && chunks <= 512) {
+    const int T = std::min(256, (chunks + 63) / 64 * 64), CP = (chunks + T - 1) / T;
+    const int spec = M <= 256;  // small batches: do not wait for the slot flags before reading y
+    if (norm_w) {
+      if (top_k <= 2) launch_combine1<true, 2>(CP, T, M, y, topk_weights, slot_local_ids, norm_w, eps, top_k, H, spec, out, stream);
+      else if (top_k <= 4) launch_combine1<true, 4>(CP, T, M, y, topk_weights, slot_local_ids, norm_w, eps, top_k, H, spec, out, stream);
+      else launch_combine1<true, 8>(CP, T, M, y, topk_weights, slot_local_ids, norm_w, eps, top_k, H, spec, out, stream);
+    } else {
+      if (top_k <= 2) launch_combine1<false, 2>(CP, T, M, y, topk_weights, slot_local_ids, norm_w, eps, top_k, H, spec, out, stream);
+      else if (top_k <= 4) launch_combine1<false, 4>(CP, T, M, y, topk_weights, slot_local_ids, norm_w, eps, top_k, H, spec, out, stream);
+      else launch_combine1<false, 8>(CP, T, M, y, topk_weights, slot_local_ids, norm_w, eps, top_k, H, spec, out, stream);
+    }
+    return check_launch("moe_combine");
+  }
   if (norm_w)
     hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)M), dim3(kCombineThreads), 0, stream, y,
                        topk_weights, slot_local_ids, norm_w, eps, top_k, H, out);

@@ -140,10 +140,14 @@ def test_act_matches_oracle(kind, limit):
     assert np.all(err <= 2.0 ** -8 * np.abs(ref[live]) + 1e-6), err.max()
 
 
-@pytest.mark.parametrize("H,norm", [(512, False), (4096, True), (2880, False), (2880, True), (64, True)])
-def test_combine_matches_oracle(H, norm):
-    rng = np.random.default_rng(H)
-    M, k = 45, 8
+# single-pass kernel (top_k <= 8, H <= 4096; M <= 256 also reads y of dead slots, unused) and
+# the two-pass kernel beyond that
+@pytest.mark.parametrize("H,norm,M,k", [(512, False, 45, 8), (4096, True, 45, 8), (2880, False, 45, 8),
+                                        (2880, True, 45, 8), (64, True, 45, 8), (4096, True, 300, 8),
+                                        (512, False, 300, 2), (2880, True, 45, 4), (8192, True, 20, 8),
+                                        (512, True, 20, 16)])
+def test_combine_matches_oracle(H, norm, M, k):
+    rng = np.random.default_rng(H + M + k)
     y_bits = W._to_bf16_bits(rng.standard_normal((M * k, H)).astype(np.float32))
     g = rng.random((M, k)).astype(np.float32)
     loc = rng.integers(-1, 3, size=(M, k)).astype(np.int32)
