@@ -8,11 +8,12 @@ workload is the int4 layer with biases, M=2304 tokens, E=8, top-2, H=512, I=1024
 
 Timing: W untimed warm-up steps, then K steps replayed from a HIP graph of one step,
 bracketed by device synchronisation; value = tokens / second.  "cold" repeats the replay with
-1 GiB streamed through the caches before each one (so the weights come from HBM, not from L2
-or the memory-side cache) and reports the median replay time.  The roofline entry is for
+1 GiB read through the caches before each one (so the weights come from HBM, not from L2 or
+the memory-side cache) and reports the median replay time.  The roofline entry is for
 the dominant kernel (the largest share of the layer's work): its average duration is taken
-with HIP events recorded around it on its own stream over K eager steps, and its algorithmic
-work per launch is the flops (prefill) or weight bytes (decode) it must process.  The CPU
+with HIP events on its launch stream around replays of a graph of back-to-back launches with the
+arguments of a real step, and its algorithmic work per launch is the flops (prefill) or weight
+bytes (decode) it must process.  The CPU
 baseline is the float64 oracle on a bounded sample of the same workload on the host cores.
 
 Prints one JSON line.  With --sweep, prints one JSON line per configuration cell instead.
@@ -39,7 +40,8 @@ CSRC = os.path.join(ROOT, "quantized_mixture_experts_align_amd", "csrc")
 # every source the GEMM kernels are compiled from: a change to any of them voids old counters
 GEMM_SRCS = ["moe_gemm.hip", "moe_gemm_common.h", "moe_gemm_mfma.h", "moe_gemm_decode.h",
              "moe_gemm_int4.hip", "moe_gemm_nvfp4.hip", "moe_gemm_mxfp4.hip", "moe_internal.h"]
-FLUSH_BYTES = 1 << 30          # streamed between cold steps: more than L2 + MALL
+FLUSH_BYTES = 1 << 30          # read between cold steps: more than L2 + MALL
+LAUNCHES = 20                  # back-to-back launches per graph when timing one GEMM
 
 
 def gemm_source_hash() -> str:
@@ -155,12 +157,14 @@ def run_cell(cfg: int, M: int, steps: int, warmup: int, want_cpu: bool, seed=Non
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - t0) / steps
 
-    # ---- cold: before each replay stream 1 GiB through the caches, events around the replay
-    # only; the median over the replays
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    # ---- cold: before each replay read 1 GiB through the caches (as the other layers' weights
+    # would be read between two calls of this one), events around the replay only; the median
+    # over the replays.  A read, not a write: a write would leave the memory-side cache full of
+    # dirty lines whose write-back then slows the replay's reads (measured: about 3x on 128 MB).
+    flush = torch.ones(FLUSH_BYTES // 8, dtype=torch.int64, device=dev)
     cold = []
     for _ in range(max(50, min(steps, 200))):
-        flush.zero_()
+        flush.sum()
         s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s0.record(stream)
         g.replay()
@@ -170,33 +174,43 @@ def run_cell(cfg: int, M: int, steps: int, warmup: int, want_cpu: bool, seed=Non
     cold_s = float(np.median([a.elapsed_time(b) for a, b in cold])) * 1e-3
     del flush
 
-    # ---- dominant kernel: HIP events on the launch stream around each GEMM, eager steps
+    # ---- the two GEMMs alone: the arguments of a real step are recorded, then a HIP graph of
+    # LAUNCHES back-to-back launches of each is replayed between HIP events on the launch stream
+    # (the average per launch is the kernel's duration plus the graph's small launch gap)
     import quantized_mixture_experts_align_amd.ops as ops
-    ev = {k: [] for k in ("gemm13", "gemm2")}
+    calls = {}
     orig, orig_act = ops.moe_w4a16_gemm, ops.moe_w4a16_gemm_act
 
-    def timed(fn, key):
+    def record(fn, key):
         def wrapper(*a, **kw):
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record(stream)
-            r = fn(*a, **kw)
-            e.record(stream)
-            ev[key].append((s, e))
-            return r
+            calls[key] = (fn, a, kw)
+            return fn(*a, **kw)
         return wrapper
     # gate/up GEMM (with the activation fused into it) and down GEMM
-    ops.moe_w4a16_gemm_act = timed(orig_act, "gemm13")
-    ops.moe_w4a16_gemm = timed(orig, "gemm2")
+    ops.moe_w4a16_gemm_act = record(orig_act, "gemm13")
+    ops.moe_w4a16_gemm = record(orig, "gemm2")
     try:
-        # keep the device busy while the host enqueues, so each event pair brackets only
-        # device execution and not host launch latency
-        torch.cuda._sleep(int(2.4e9 * 0.05))
-        for _ in range(steps):
-            layer(x, ids, gw, ws=ws)
+        layer(x, ids, gw, ws=ws)
     finally:
         ops.moe_w4a16_gemm, ops.moe_w4a16_gemm_act = orig, orig_act
     torch.cuda.synchronize()
-    dur = {k: float(np.mean([s.elapsed_time(e) for s, e in v])) * 1e-3 for k, v in ev.items()}
+    dur = {}
+    for key, (fn, a, kw) in calls.items():
+        gk = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gk):
+            for _ in range(LAUNCHES):
+                fn(*a, **kw)
+        gk.replay()
+        torch.cuda.synchronize()
+        reps = max(5, steps // LAUNCHES)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            gk.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dur[key] = e0.elapsed_time(e1) * 1e-3 / (reps * LAUNCHES)
+        del gk
 
     # dominant kernel: the gate/up GEMM holds 2/3 of the flops and of the weight bytes; it is
     # compute-bound when its flops per weight byte exceed the machine balance
@@ -228,7 +242,7 @@ def run_cell(cfg: int, M: int, steps: int, warmup: int, want_cpu: bool, seed=Non
                   "gemm13_us": round(d13 * 1e6, 2), "gemm2_us": round(dur["gemm2"] * 1e6, 2),
                   "weight_bytes": bytes_13 + bytes_2, "flops": flops_13 + flops_2},
         "cold": {"ms_per_step": round(cold_s * 1e3, 4), "tokens_per_s": round(M / cold_s, 1),
-                 "replays": len(cold), "note": "median graph replay after streaming 1 GiB",
+                 "replays": len(cold), "note": "median graph replay after reading 1 GiB",
                  **layer_fracs(bytes_13 + bytes_2, flops_13 + flops_2, cold_s)},
     }
     if want_cpu:

@@ -7,15 +7,18 @@
 // assignments are dropped, and the order inside an expert is ascending slot id, so the result
 // is unique and reproducible.
 //
-// One workgroup of 16 waves.  Wave w owns a contiguous chunk of slots.
+// One workgroup of 16 waves; wave w owns a contiguous chunk of slots, a multiple of 64 long.
 //   1. count:   LDS histogram cnt[w][e] (atomics only add; the totals do not depend on order)
-//   2. scan:    per expert, exclusive scan over waves (ordered) -> offset of wave w inside the
-//               expert's segment; padded totals scanned over experts -> segment starts
+//   2. scan:    per expert, exclusive scan over the waves (a 16-lane segmented shuffle scan per
+//               expert) -> offset of wave w inside the expert's segment and the expert's total;
+//               padded totals scanned over experts -> segment starts
 //   3. scatter: each wave walks its chunk in order, 64 slots at a time; the rank of a lane among
 //               the lanes of its batch with the same expert comes from ballots over the bits of
 //               the expert id (a wave multi-split), so the write position is
-//               seg[e] + off[w][e] + rank, strictly in slot order
-//   4. fill:    padding entries and the tail get the sentinel, block -> expert by binary search
+//               seg[e] + off[w][e] + rank, strictly in slot order.  A chunk of up to
+//               64 * kAlignUnroll slots keeps its ids in registers from step 1 (one read of ids)
+//   4. fill:    padding entries (in parallel over expert x position) and the tail get the
+//               sentinel, block -> expert by binary search over the segment starts
 #include "moe_internal.h"
 
 namespace moe {
@@ -35,17 +38,22 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   __shared__ int32_t wave_sum[kAlignWaves];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  for (int i = tid; i < kAlignWaves * n_local; i += kAlignThreads) cnt[i] = 0;
+  // every wave owns a chunk (the scatter is serial per 64-slot batch within a wave, so short
+  // chunks are faster even when most waves are idle)
+  const int nwv = kAlignWaves;
+  for (int i = tid; i < nwv * n_local; i += kAlignThreads) cnt[i] = 0;
   __syncthreads();
 
-  // chunk of wave w: [c0, c1), a multiple of 64 slots long
-  const int per = ((numel + kAlignWaves - 1) / kAlignWaves + 63) & ~63;
-  const int c0 = min(numel, w * per), c1 = min(numel, c0 + per);
+  // chunk of wave w: [c0, c1), a multiple of 64 slots long (empty for waves >= nwv)
+  const int per = ((numel + nwv - 1) / nwv + 63) & ~63;
+  const int c0 = w < nwv ? min(numel, w * per) : numel, c1 = w < nwv ? min(numel, c0 + per) : numel;
+  const bool keep = per <= 64 * kAlignUnroll;  // the chunk's ids stay in registers
   int32_t* my_cnt = cnt + w * n_local;
 
+  auto local_of = [&](int id) { return (id >= start && id - start < n_local) ? id - start : -1; };
   // (ids are read kAlignUnroll batches at a time so their load latencies overlap)
+  int idv[kAlignUnroll];
   for (int base = c0; base < c1; base += 64 * kAlignUnroll) {
-    int idv[kAlignUnroll];
 #pragma unroll
     for (int u = 0; u < kAlignUnroll; ++u) {
       const int i = base + 64 * u + lane;
@@ -55,23 +63,28 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     for (int u = 0; u < kAlignUnroll; ++u) {
       const int i = base + 64 * u + lane;
       if (i >= c1) break;
-      const int id = idv[u];
-      const int le = (id >= start && id - start < n_local) ? id - start : -1;
+      const int le = local_of(idv[u]);
       if (slot_local) slot_local[i] = le;
       if (le >= 0) atomicAdd(&my_cnt[le], 1);
     }
   }
   __syncthreads();
 
-  // per expert: offsets of each wave inside the expert's run, and the total
-  for (int e = tid; e < n_local; e += kAlignThreads) {
-    int run = 0;
-    for (int v = 0; v < kAlignWaves; ++v) {
-      const int c = cnt[v * n_local + e];
-      cnt[v * n_local + e] = run;
-      run += c;
+  // per expert: exclusive scan of the waves' counts (wave order) and the total; lanes
+  // 16 j .. 16 j + 15 of a wave hold waves 0..15 of one expert
+  for (int base = 0; base < n_local * 16; base += kAlignThreads) {
+    const int i = base + tid, e = i >> 4, v = i & 15;
+    const int c = (e < n_local && v < nwv) ? cnt[v * n_local + e] : 0;
+    int x = c;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int o = __shfl_up(x, d, 16);
+      if (v >= d) x += o;
     }
-    tot[e] = run;
+    if (e < n_local) {
+      if (v < nwv) cnt[v * n_local + e] = x - c;
+      if (v == 15) tot[e] = x;
+    }
   }
   __syncthreads();
 
@@ -98,18 +111,18 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   while ((1 << nbits) < n_local) ++nbits;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int base = c0; base < c1; base += 64 * kAlignUnroll) {
-    int idv[kAlignUnroll];
+    if (!keep) {
 #pragma unroll
-    for (int u = 0; u < kAlignUnroll; ++u) {
-      const int i = base + 64 * u + lane;
-      idv[u] = i < c1 ? ids[i] : -1;
+      for (int u = 0; u < kAlignUnroll; ++u) {
+        const int i = base + 64 * u + lane;
+        idv[u] = i < c1 ? ids[i] : -1;
+      }
     }
 #pragma unroll
     for (int u = 0; u < kAlignUnroll; ++u) {
       const int i = base + 64 * u + lane;
       if (base + 64 * u >= c1) break;  // uniform: the wave's chunk has ended
-      const int id = idv[u];
-      const int le = (i < c1 && id >= start && id - start < n_local) ? id - start : -1;
+      const int le = i < c1 ? local_of(idv[u]) : -1;
       const bool live = le >= 0;
       uint64_t same = __ballot(live);
       for (int b = 0; b < nbits; ++b) {
@@ -127,9 +140,11 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     }
   }
 
-  // padding of each expert's last block, then the tail
-  for (int e = tid; e < n_local; e += kAlignThreads)
-    for (int p = seg[e] + tot[e]; p < seg[e + 1]; ++p) sorted[p] = numel;
+  // padding of each expert's last block (expert x position in parallel), then the tail
+  for (int i = tid; i < n_local * B; i += kAlignThreads) {
+    const int e = i / B, p = seg[e] + tot[e] + (i - e * B);
+    if (p < seg[e + 1]) sorted[p] = numel;
+  }
   const int total = seg[n_local];
   for (int p = total + tid; p < cap; p += kAlignThreads) sorted[p] = numel;
   for (int b = tid; b < cap_blocks; b += kAlignThreads) {

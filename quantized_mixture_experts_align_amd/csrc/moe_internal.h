@@ -68,7 +68,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // ---------------------------------------------------------------------------- activations
-__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// (hardware reciprocal, within 1 ulp: the result is rounded to bf16)
+__device__ __forceinline__ float sigmoid_f(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // silu(gate) * up -- silu_and_mul of the Muse Spark experiment.
 struct SiluMul {
