@@ -124,13 +124,13 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 // stays in registers between the norm's reduction and the weighted sum (read once).  The fp32
 // operations and their order per output are those of combine_kernel.
 template <bool NORM, int TK, int CP>
-__global__ __launch_bounds__(256) void combine1_kernel(
+__global__ __launch_bounds__(512) void combine1_kernel(
     const uint16_t* __restrict__ y, const float* __restrict__ gw, const int32_t* __restrict__ slot_local,
     const uint16_t* __restrict__ nw, float eps, int32_t top_k, int32_t H, int32_t spec,
     uint16_t* __restrict__ out) {
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, T = blockDim.x;
-  __shared__ float red[4][TK];
+  __shared__ float red[8][TK];
   __shared__ float fac[TK], gl[TK];
   const int chunks = H >> 3;
   uint32_t live = 0;
@@ -275,10 +275,11 @@ extern "C" int moe_combine(const uint16_t* y, const float* topk_weights, const i
   MOE_REQUIRE(y && topk_weights && slot_local_ids && out, MOE_EINVAL, "moe_combine: null pointer");
   MOE_REQUIRE(aligned16(y) && aligned16(out) && (!norm_w || aligned16(norm_w)), MOE_EUNSUPPORTED,
               "moe_combine: bf16 tensors must be 16-byte aligned");
-  // single pass when a token's slots fit in registers: top_k <= 8, H <= 2 * 256 * 8
+  // single pass when a token's slots fit in registers: top_k <= 8, H <= 2 * 512 * 8; one
+  // 16-B chunk per thread up to 512 threads (more loads in flight per token)
   const int chunks = H / 8;
-  if (top_k <= 8 && chunks <= 512) {
-    const int T = std::min(256, (chunks + 63) / 64 * 64), CP = (chunks + T - 1) / T;
+  if (top_k <= 8 && chunks <= 1024) {
+    const int T = std::min(512, (chunks + 63) / 64 * 64), CP = (chunks + T - 1) / T;
     const int spec = M <= 256;  // small batches: do not wait for the slot flags before reading y
     if (norm_w) {
       if (top_k <= 2) launch_combine1<true, 2>(CP, T, M, y, topk_weights, slot_local_ids, norm_w, eps, top_k, H, spec, out, stream);

@@ -186,9 +186,8 @@ extern "C" int moe_align(const int32_t* topk_ids, int64_t M, int32_t top_k, int3
   MOE_REQUIRE(num_tokens_post_padded && ((sorted_token_ids && expert_ids) || cap == 0), MOE_EINVAL,
               "moe_align: null output pointer");
   MOE_REQUIRE(topk_ids || M == 0, MOE_EINVAL, "moe_align: null topk_ids");
-  hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, stream, topk_ids,
-                     (int32_t)(M * top_k), expert_start, n_local, block_m, (int32_t)cap,
-                     (int32_t)cap_blocks, sorted_token_ids, expert_ids, num_tokens_post_padded,
-                     slot_local_ids);
+  hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, stream, topk_ids, (int32_t)(M * top_k),
+                     expert_start, n_local, block_m, (int32_t)cap, (int32_t)cap_blocks, sorted_token_ids,
+                     expert_ids, num_tokens_post_padded, slot_local_ids);
   return check_launch("moe_align");
 }

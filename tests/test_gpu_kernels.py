@@ -140,12 +140,12 @@ def test_act_matches_oracle(kind, limit):
     assert np.all(err <= 2.0 ** -8 * np.abs(ref[live]) + 1e-6), err.max()
 
 
-# single-pass kernel (top_k <= 8, H <= 4096; M <= 256 also reads y of dead slots, unused) and
+# single-pass kernel (top_k <= 8, H <= 8192; M <= 256 also reads y of dead slots, unused) and
 # the two-pass kernel beyond that
 @pytest.mark.parametrize("H,norm,M,k", [(512, False, 45, 8), (4096, True, 45, 8), (2880, False, 45, 8),
                                         (2880, True, 45, 8), (64, True, 45, 8), (4096, True, 300, 8),
                                         (512, False, 300, 2), (2880, True, 45, 4), (8192, True, 20, 8),
-                                        (512, True, 20, 16)])
+                                        (512, True, 20, 16), (16384, True, 5, 8)])
 def test_combine_matches_oracle(H, norm, M, k):
     rng = np.random.default_rng(H + M + k)
     y_bits = W._to_bf16_bits(rng.standard_normal((M * k, H)).astype(np.float32))
