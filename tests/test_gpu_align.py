@@ -48,6 +48,19 @@ def test_align_random_slices(seed, B):
     _check(ids, start, n_local, B)
 
 
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("B", [1, 16, 64, 256])
+def test_align_small_batches(seed, B):
+    # up to 64 slots: junk and repeated ids, up to 512 local experts, block sizes 1..256
+    rng = np.random.default_rng(100 + seed)
+    M, k = int(rng.integers(1, 9)), int(rng.integers(1, 9))
+    n_local = int(rng.choice([1, 5, 32, 128, 512]))
+    start = int(rng.integers(0, 50))
+    ids = rng.integers(-5, start + n_local + 40, size=(M, k)).astype(np.int32)
+    _check(ids, start, n_local, B)
+    _check(np.full((1, 8), start, np.int32), start, n_local, B)   # one expert, all slots
+
+
 def test_align_edge_cases():
     _check(np.zeros((0, 8), np.int32), 0, 32, 16)                        # no tokens
     _check(np.full((37, 4), 1000, np.int32), 0, 128, 16)                 # everything off-slice
