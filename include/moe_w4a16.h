@@ -57,8 +57,10 @@ typedef enum {
 } moe_qtype;
 
 typedef enum {
-  MOE_ACT_SILU_MUL = 0,      /* silu(gate) * up                                     */
-  MOE_ACT_SWIGLU_ALPHA = 1   /* min(g,L) * sigmoid(alpha * min(g,L)) * (clamp(u,-L,L) + 1) */
+  MOE_ACT_SILU_MUL = 0,      /* gated: silu(gate) * up                                      */
+  MOE_ACT_SWIGLU_ALPHA = 1,  /* gated: min(g,L) * sigmoid(alpha * min(g,L)) * (clamp(u,-L,L) + 1) */
+  MOE_ACT_RELU2 = 2          /* non-gated: relu(h)^2 (the sglang PR 31552 test's activation,
+                                is_gated=False; GEMM1 then has I rows, no gate/up halves)  */
 } moe_act_kind;
 
 /* ----------------------------------------------------------------------------- errors */
@@ -213,14 +215,15 @@ int moe_w4a16_gemm(const uint16_t* A, int64_t a_rows, int32_t lda, uint16_t* C, 
                    hipStream_t stream);
 
 /*
- * Gate/up GEMM with the activation fused into its epilogue (one launch instead of
- * moe_w4a16_gemm + moe_act, and no [numel, 2I] intermediate in memory):
+ * GEMM1 with the activation fused into its epilogue (one launch instead of moe_w4a16_gemm +
+ * moe_act, and no [numel, 2I] intermediate in memory).  Gated kinds:
  *     out[s, j] = act(gate, up),  gate = bf16(h[s, j]), up = bf16(h[s, I + j])
- * where h is what moe_w4a16_gemm computes for W13 (prepared with MOE_PREP_GATE_UP, N = 2I).
- * The gate/up values are rounded to bf16 exactly as the stored GEMM output would be, so the
- * result equals moe_w4a16_gemm followed by moe_act bit for bit.  out: device bf16 [numel, ldo],
- * ldo >= I, only rows of live slots written.  cfg->ng must be 2 or 4 (gate/up tile pairs).
- * Other arguments as moe_w4a16_gemm; alpha/limit as moe_act.
+ * where h is what moe_w4a16_gemm computes for W13 (prepared with MOE_PREP_GATE_UP, N = 2I);
+ * cfg->ng must be 2 or 4 (gate/up tile pairs).  MOE_ACT_RELU2: W13 is a plain projection (not
+ * MOE_PREP_GATE_UP, N = I) and out[s, j] = relu(bf16(h[s, j]))^2.  The GEMM values are rounded
+ * to bf16 exactly as the stored GEMM output would be, so the result equals moe_w4a16_gemm
+ * followed by moe_act bit for bit.  out: device bf16 [numel, ldo], ldo >= I, only rows of live
+ * slots written.  Other arguments as moe_w4a16_gemm; alpha/limit as moe_act.
  */
 int moe_w4a16_gemm_act(moe_act_kind kind, float alpha, float limit, const uint16_t* A, int64_t a_rows,
                        int32_t lda, uint16_t* out, int32_t ldo, const moe_weights* W13,
@@ -231,9 +234,10 @@ int moe_w4a16_gemm_act(moe_act_kind kind, float alpha, float limit, const uint16
 /* ----------------------------------------------------------------------------- act */
 
 /*
- * Gated activation over rows of the GEMM1 output (silu_and_mul of the experiment; GPT-OSS
- * swiglu_gpt_oss_sigmoid_alpha_contiguous of sglang PR 28231):
- *   in   device bf16 [R, ld_in]: gate = columns [0, I), up = [I, 2I)
+ * Activation over rows of the GEMM1 output (silu_and_mul of the experiment; GPT-OSS
+ * swiglu_gpt_oss_sigmoid_alpha_contiguous of sglang PR 28231; the non-gated relu2):
+ *   in   device bf16 [R, ld_in]: gated kinds gate = columns [0, I), up = [I, 2I) (ld_in >= 2I);
+ *        MOE_ACT_RELU2 the I columns of h (ld_in >= I)
  *   out  device bf16 [R, ld_out]: I columns
  *   slot_local_ids  device int32 [R] or NULL: rows whose id is < 0 are skipped (not written)
  *   alpha, limit    SWIGLU_ALPHA only; limit = +inf disables the clamps
@@ -251,15 +255,16 @@ int moe_act(moe_act_kind kind, const uint16_t* in, int32_t ld_in, uint16_t* out,
  *   y               device bf16 [M * top_k, H]: GEMM2 output, row t*top_k+s
  *   topk_weights    device fp32 [M, top_k]
  *   slot_local_ids  device int32 [M, top_k]: slots with id < 0 are dead and contribute 0
- *                   (their y rows are never read)
+ *                   (their y rows may be read but their values are never used)
  *   norm_w          device bf16 [H] = bf16(1 + w) (moe_norm_weight), or NULL for no norm
+ *   routed_scaling_factor  multiplies every output (1 = none; the sglang PR 31552 argument)
  *   out             device bf16 [M, H], every row written (zeros for tokens with no live slot)
- * With norm: z = y * norm_w, factor = g / sqrt(sum(z^2) / H + eps), out = sum factor * z.
- * Without:   out = sum g * y.   fp32 accumulation, one bf16 rounding at the end.
+ * With norm: z = y * norm_w, factor = g / sqrt(sum(z^2) / H + eps), out = rsf * sum factor * z.
+ * Without:   out = rsf * sum g * y.   fp32 accumulation, one bf16 rounding at the end.
  */
 int moe_combine(const uint16_t* y, const float* topk_weights, const int32_t* slot_local_ids,
-                const uint16_t* norm_w, float eps, int64_t M, int32_t top_k, int32_t H,
-                uint16_t* out, hipStream_t stream);
+                const uint16_t* norm_w, float eps, float routed_scaling_factor, int64_t M,
+                int32_t top_k, int32_t H, uint16_t* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,11 @@ design notes of the repository):
 * the post-expert RMSNorm is weight-first: ``z = y * bf16(1 + w)``, then
   ``z * (mean(z^2) + eps)^-1/2`` -- the order of ``_expert_norm_factors``;
 * biases are added to the matmul output before the activation / before the
-  top-k weighting, as in the sglang PR 31552 reference loop.
+  top-k weighting, as in the sglang PR 31552 reference loop;
+* ``relu2`` is the non-gated activation of that loop: GEMM1 has I rows (no
+  gate/up halves) and ``a = relu(h)^2``;
+* ``routed_scaling_factor`` (passed as 1.0 in that test, not defined on the
+  pages) multiplies the combined output of each token.
 """
 from __future__ import annotations
 
@@ -157,6 +161,16 @@ def act_swiglu_alpha(gate: np.ndarray, up: np.ndarray, alpha: float, limit: floa
     return g * _sigmoid(alpha * g) * (u + 1.0)
 
 
+def act_relu2(h: np.ndarray) -> np.ndarray:
+    """Non-gated ``relu(h)^2`` of the sglang PR 31552 reference loop
+    (``torch.square(torch.relu(intermediate))``, ``activation="relu2"``,
+    ``is_gated=False``).  Pinned by hand values."""
+    return np.square(np.maximum(h, 0.0))
+
+
+GATED = {"silu_mul": True, "swiglu_alpha": True, "relu2": False}
+
+
 # ----------------------------------------------------------------------------- experts
 def expert_forward(xrows: np.ndarray, W13: np.ndarray, b13: Optional[np.ndarray],
                    W2: np.ndarray, b2: Optional[np.ndarray], act: str, alpha: float,
@@ -169,13 +183,16 @@ def expert_forward(xrows: np.ndarray, W13: np.ndarray, b13: Optional[np.ndarray]
     if b13 is not None:
         h = h + b13[None, :]
     h = rnd(h)
-    gate, up = split_gate_up(h, interleaved)
-    if act == "silu_mul":
-        a = act_silu_mul(gate, up)
-    elif act == "swiglu_alpha":
-        a = act_swiglu_alpha(gate, up, alpha, limit)
+    if act == "relu2":
+        a = act_relu2(h)
     else:
-        raise ValueError(act)
+        gate, up = split_gate_up(h, interleaved)
+        if act == "silu_mul":
+            a = act_silu_mul(gate, up)
+        elif act == "swiglu_alpha":
+            a = act_swiglu_alpha(gate, up, alpha, limit)
+        else:
+            raise ValueError(act)
     a = rnd(a)
     y = a @ W2.T
     if b2 is not None:
@@ -192,7 +209,7 @@ def norm_weight(post_norm_w_bits: np.ndarray) -> np.ndarray:
 
 
 def combine(Y: np.ndarray, topk_weights: np.ndarray, slot_local: np.ndarray,
-            norm_w: Optional[np.ndarray], eps: float) -> np.ndarray:
+            norm_w: Optional[np.ndarray], eps: float, routed_scaling_factor: float = 1.0) -> np.ndarray:
     """Top-k weighted sum over the live slots of each token.
 
     Without a norm: ``out[t] = sum_s g[t, s] * y[t, s]`` (the reference loop's
@@ -200,7 +217,8 @@ def combine(Y: np.ndarray, topk_weights: np.ndarray, slot_local: np.ndarray,
     (``_expert_norm_factors`` then ``_expert_norm_sum``):
     ``z = y * norm_w``, ``factor = g * (sum(z^2) / H + eps)^-1/2`` and
     ``out[t] = sum_s factor * z``.  Dead slots (local id -1) contribute
-    nothing.  Pinned by the RMSNorm special case and hand values.
+    nothing.  ``routed_scaling_factor`` multiplies the sum.  Pinned by the
+    RMSNorm special case and hand values.
     """
     M, k = np.shape(topk_weights)
     H = Y.shape[-1]
@@ -216,14 +234,14 @@ def combine(Y: np.ndarray, topk_weights: np.ndarray, slot_local: np.ndarray,
             z = y * norm_w[None, :]
             inv = 1.0 / np.sqrt(np.sum(z * z, axis=1) / H + eps)
             out[live] += (g[live, s] * inv)[:, None] * z
-    return out
+    return out * routed_scaling_factor
 
 
 # ----------------------------------------------------------------------------- layer
 def moe_layer(qtype: str, x_bits: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarray,
               w13, w2, *, expert_start: int, n_local: int, act: str = "silu_mul",
               alpha: float = 1.702, limit: float = math.inf, norm_w_bits=None,
-              eps: float = 1e-8, interleaved_w13: bool = False,
+              eps: float = 1e-8, interleaved_w13: bool = False, routed_scaling_factor: float = 1.0,
               bf16_intermediates: bool = True, tokens=None, return_intermediates: bool = False):
     """The whole expert layer for one GPU's expert slice.
 
@@ -258,7 +276,7 @@ def moe_layer(qtype: str, x_bits: np.ndarray, topk_ids: np.ndarray, topk_weights
                 for j, row in enumerate(rows):
                     inter[name][int(tok[row // k] * k + row % k)] = r[name][j]
     nw = None if norm_w_bits is None else norm_weight(norm_w_bits)
-    out = combine(Y, np.asarray(topk_weights)[tok], sub_local, nw, eps)
+    out = combine(Y, np.asarray(topk_weights)[tok], sub_local, nw, eps, routed_scaling_factor)
     if return_intermediates:
         return out, inter
     return out

@@ -12,7 +12,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe_w4a16.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ESIZE, MOE_EHIP = 0, -1, -2, -3, -4
 QTYPE = {"int4_g128": 0, "nvfp4_g16": 1, "mxfp4_g32": 2}
-ACT = {"silu_mul": 0, "swiglu_alpha": 1}
+ACT = {"silu_mul": 0, "swiglu_alpha": 1, "relu2": 2}
+GATED = {"silu_mul": True, "swiglu_alpha": True, "relu2": False}
 PREP_GATE_UP, PREP_INTERLEAVED, PREP_PAD = 0x1, 0x2, 0x4
 GEMM_AUTO, GEMM_DECODE, GEMM_MFMA = 0, 1, 2
 
@@ -53,7 +54,7 @@ SIGNATURES = {
     "moe_w4a16_gemm_act": (C.c_int, [C.c_int, _F, _F, _P, _I64, _I32, _P, _I32, C.POINTER(MoeWeights), _P,
                                      _P, _P, _I64, _I32, _I32, C.POINTER(MoeGemmConfig), _P]),
     "moe_act": (C.c_int, [C.c_int, _P, _I32, _P, _I32, _I64, _I32, _P, _F, _F, _P]),
-    "moe_combine": (C.c_int, [_P, _P, _P, _P, _F, _I64, _I32, _I32, _P, _P]),
+    "moe_combine": (C.c_int, [_P, _P, _P, _P, _F, _F, _I64, _I32, _I32, _P, _P]),
 }
 
 _lib = None

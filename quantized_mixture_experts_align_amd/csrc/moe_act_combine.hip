@@ -33,6 +33,27 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ i
   }
 }
 
+// Non-gated activation: one thread per 8 columns of one row, out = act(in) element-wise.
+template <class Act>
+__global__ __launch_bounds__(256) void act1_kernel(const uint16_t* __restrict__ in, int32_t ld_in,
+                                                   uint16_t* __restrict__ out, int32_t ld_out, int64_t R,
+                                                   int32_t I, const int32_t* __restrict__ slot_local, Act act) {
+  const int chunks = I >> 3;
+  const int64_t total = R * chunks;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = c / chunks;
+    const int col = (int)(c - r * chunks) << 3;
+    if (slot_local && slot_local[r] < 0) continue;
+    const uint4 h = *reinterpret_cast<const uint4*>(in + r * ld_in + col);
+    const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(act(bf16_lo(hw[j])), act(bf16_hi(hw[j])));
+    *reinterpret_cast<uint4*>(out + r * ld_out + col) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 constexpr int kCombineThreads = 256;
 constexpr int kMaxTopK = 16;
 
@@ -41,7 +62,7 @@ constexpr int kMaxTopK = 16;
 template <bool NORM>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const uint16_t* __restrict__ y, const float* __restrict__ gw, const int32_t* __restrict__ slot_local,
-    const uint16_t* __restrict__ nw, float eps, int32_t top_k, int32_t H, uint16_t* __restrict__ out) {
+    const uint16_t* __restrict__ nw, float eps, float rsf, int32_t top_k, int32_t H, uint16_t* __restrict__ out) {
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   __shared__ float fac[kMaxTopK];
@@ -111,6 +132,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
         }
       }
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= rsf;  // routed scaling factor (1 = none)
     *reinterpret_cast<uint4*>(out + t * H + c * 8) =
         make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                    pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
@@ -126,7 +149,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 template <bool NORM, int TK, int CP>
 __global__ __launch_bounds__(512) void combine1_kernel(
     const uint16_t* __restrict__ y, const float* __restrict__ gw, const int32_t* __restrict__ slot_local,
-    const uint16_t* __restrict__ nw, float eps, int32_t top_k, int32_t H, int32_t spec,
+    const uint16_t* __restrict__ nw, float eps, float rsf, int32_t top_k, int32_t H, int32_t spec,
     uint16_t* __restrict__ out) {
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, T = blockDim.x;
@@ -213,6 +236,8 @@ __global__ __launch_bounds__(512) void combine1_kernel(
         }
       }
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= rsf;  // routed scaling factor (1 = none)
     *reinterpret_cast<uint4*>(out + t * H + col * 8) =
         make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                    pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
@@ -221,12 +246,12 @@ __global__ __launch_bounds__(512) void combine1_kernel(
 
 template <bool NORM, int TK>
 static void launch_combine1(int CP, int T, int64_t M, const uint16_t* y, const float* gw, const int32_t* sl,
-                            const uint16_t* nw, float eps, int top_k, int H, int spec, uint16_t* out,
+                            const uint16_t* nw, float eps, float rsf, int top_k, int H, int spec, uint16_t* out,
                             hipStream_t st) {
   if (CP == 1)
-    hipLaunchKernelGGL((combine1_kernel<NORM, TK, 1>), dim3((unsigned)M), dim3(T), 0, st, y, gw, sl, nw, eps, top_k, H, spec, out);
+    hipLaunchKernelGGL((combine1_kernel<NORM, TK, 1>), dim3((unsigned)M), dim3(T), 0, st, y, gw, sl, nw, eps, rsf, top_k, H, spec, out);
   else
-    hipLaunchKernelGGL((combine1_kernel<NORM, TK, 2>), dim3((unsigned)M), dim3(T), 0, st, y, gw, sl, nw, eps, top_k, H, spec, out);
+    hipLaunchKernelGGL((combine1_kernel<NORM, TK, 2>), dim3((unsigned)M), dim3(T), 0, st, y, gw, sl, nw, eps, rsf, top_k, H, spec, out);
 }
 
 __global__ void norm_weight_kernel(const uint16_t* __restrict__ w, int32_t H, uint16_t* __restrict__ out) {
@@ -243,13 +268,14 @@ using namespace moe;
 extern "C" int moe_act(moe_act_kind kind, const uint16_t* in, int32_t ld_in, uint16_t* out,
                        int32_t ld_out, int64_t R, int32_t I, const int32_t* slot_local_ids,
                        float alpha, float limit, hipStream_t stream) {
-  MOE_REQUIRE(kind == MOE_ACT_SILU_MUL || kind == MOE_ACT_SWIGLU_ALPHA, MOE_EINVAL,
+  MOE_REQUIRE(kind == MOE_ACT_SILU_MUL || kind == MOE_ACT_SWIGLU_ALPHA || kind == MOE_ACT_RELU2, MOE_EINVAL,
               "moe_act: unknown activation %d", (int)kind);
+  const bool gated = kind != MOE_ACT_RELU2;
   MOE_REQUIRE(R >= 0 && I >= 1, MOE_EINVAL, "moe_act: R=%lld I=%d", (long long)R, I);
   MOE_REQUIRE(I % 8 == 0 && ld_in % 8 == 0 && ld_out % 8 == 0, MOE_EUNSUPPORTED,
               "moe_act: I, ld_in and ld_out must be multiples of 8 (I=%d ld_in=%d ld_out=%d)", I,
               ld_in, ld_out);
-  MOE_REQUIRE(ld_in >= 2 * I && ld_out >= I, MOE_EINVAL, "moe_act: leading dims too small");
+  MOE_REQUIRE(ld_in >= (gated ? 2 * I : I) && ld_out >= I, MOE_EINVAL, "moe_act: leading dims too small");
   if (R == 0) return ok();
   MOE_REQUIRE(in && out, MOE_EINVAL, "moe_act: null pointer");
   MOE_REQUIRE(aligned16(in) && aligned16(out), MOE_EUNSUPPORTED, "moe_act: pointers must be 16-byte aligned");
@@ -258,6 +284,9 @@ extern "C" int moe_act(moe_act_kind kind, const uint16_t* in, int32_t ld_in, uin
   if (kind == MOE_ACT_SILU_MUL)
     hipLaunchKernelGGL(act_kernel<SiluMul>, dim3(blocks), dim3(256), 0, stream, in, ld_in, out,
                        ld_out, R, I, slot_local_ids, SiluMul{alpha, limit});
+  else if (kind == MOE_ACT_RELU2)
+    hipLaunchKernelGGL(act1_kernel<Relu2>, dim3(blocks), dim3(256), 0, stream, in, ld_in, out,
+                       ld_out, R, I, slot_local_ids, Relu2{alpha, limit});
   else
     hipLaunchKernelGGL(act_kernel<SwigluAlpha>, dim3(blocks), dim3(256), 0, stream, in, ld_in, out,
                        ld_out, R, I, slot_local_ids, SwigluAlpha{alpha, limit});
@@ -265,8 +294,9 @@ extern "C" int moe_act(moe_act_kind kind, const uint16_t* in, int32_t ld_in, uin
 }
 
 extern "C" int moe_combine(const uint16_t* y, const float* topk_weights, const int32_t* slot_local_ids,
-                           const uint16_t* norm_w, float eps, int64_t M, int32_t top_k, int32_t H,
-                           uint16_t* out, hipStream_t stream) {
+                           const uint16_t* norm_w, float eps, float routed_scaling_factor, int64_t M,
+                           int32_t top_k, int32_t H, uint16_t* out, hipStream_t stream) {
+  const float rsf = routed_scaling_factor;
   MOE_REQUIRE(M >= 0 && top_k >= 1 && top_k <= kMaxTopK, MOE_EUNSUPPORTED,
               "moe_combine: M=%lld top_k=%d (top_k must be 1..%d)", (long long)M, top_k, kMaxTopK);
   MOE_REQUIRE(H >= 8 && H % 8 == 0, MOE_EUNSUPPORTED, "moe_combine: H=%d must be a multiple of 8", H);
@@ -282,22 +312,22 @@ extern "C" int moe_combine(const uint16_t* y, const float* topk_weights, const i
     const int T = std::min(512, (chunks + 63) / 64 * 64), CP = (chunks + T - 1) / T;
     const int spec = M <= 256;  // small batches: do not wait for the slot flags before reading y
     if (norm_w) {
-      if (top_k <= 2) launch_combine1<true, 2>(CP, T, M, y, topk_weights, slot_local_ids, norm_w, eps, top_k, H, spec, out, stream);
-      else if (top_k <= 4) launch_combine1<true, 4>(CP, T, M, y, topk_weights, slot_local_ids, norm_w, eps, top_k, H, spec, out, stream);
-      else launch_combine1<true, 8>(CP, T, M, y, topk_weights, slot_local_ids, norm_w, eps, top_k, H, spec, out, stream);
+      if (top_k <= 2) launch_combine1<true, 2>(CP, T, M, y, topk_weights, slot_local_ids, norm_w, eps, rsf, top_k, H, spec, out, stream);
+      else if (top_k <= 4) launch_combine1<true, 4>(CP, T, M, y, topk_weights, slot_local_ids, norm_w, eps, rsf, top_k, H, spec, out, stream);
+      else launch_combine1<true, 8>(CP, T, M, y, topk_weights, slot_local_ids, norm_w, eps, rsf, top_k, H, spec, out, stream);
     } else {
-      if (top_k <= 2) launch_combine1<false, 2>(CP, T, M, y, topk_weights, slot_local_ids, norm_w, eps, top_k, H, spec, out, stream);
-      else if (top_k <= 4) launch_combine1<false, 4>(CP, T, M, y, topk_weights, slot_local_ids, norm_w, eps, top_k, H, spec, out, stream);
-      else launch_combine1<false, 8>(CP, T, M, y, topk_weights, slot_local_ids, norm_w, eps, top_k, H, spec, out, stream);
+      if (top_k <= 2) launch_combine1<false, 2>(CP, T, M, y, topk_weights, slot_local_ids, norm_w, eps, rsf, top_k, H, spec, out, stream);
+      else if (top_k <= 4) launch_combine1<false, 4>(CP, T, M, y, topk_weights, slot_local_ids, norm_w, eps, rsf, top_k, H, spec, out, stream);
+      else launch_combine1<false, 8>(CP, T, M, y, topk_weights, slot_local_ids, norm_w, eps, rsf, top_k, H, spec, out, stream);
     }
     return check_launch("moe_combine");
   }
   if (norm_w)
     hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)M), dim3(kCombineThreads), 0, stream, y,
-                       topk_weights, slot_local_ids, norm_w, eps, top_k, H, out);
+                       topk_weights, slot_local_ids, norm_w, eps, rsf, top_k, H, out);
   else
     hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)M), dim3(kCombineThreads), 0, stream, y,
-                       topk_weights, slot_local_ids, norm_w, eps, top_k, H, out);
+                       topk_weights, slot_local_ids, norm_w, eps, rsf, top_k, H, out);
   return check_launch("moe_combine");
 }
 

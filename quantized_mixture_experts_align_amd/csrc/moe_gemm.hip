@@ -36,10 +36,14 @@ static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64
   MOE_REQUIRE(W->codes && W->scales, MOE_EINVAL, "moe_w4a16_gemm: weights without codes/scales");
   MOE_REQUIRE(W->qtype != MOE_Q_NVFP4_G16 || W->global_scale, MOE_EINVAL,
               "moe_w4a16_gemm: NVFP4 weights without global scales");
-  const int ncols = act == kActNone ? W->N : W->N / 2;  // output columns
-  if (act != kActNone)
+  const bool paired = act_paired(act);
+  const int ncols = paired ? W->N / 2 : W->N;  // output columns
+  if (paired)
     MOE_REQUIRE((W->flags & MOE_PREP_GATE_UP) && W->N % (2 * kTileN) == 0, MOE_EINVAL,
-                "moe_w4a16_gemm_act: weights must be a gate/up pair (prepared with MOE_PREP_GATE_UP)");
+                "moe_w4a16_gemm_act: a gated activation needs a gate/up pair (prepared with MOE_PREP_GATE_UP)");
+  if (act == kActRelu2)
+    MOE_REQUIRE(!(W->flags & MOE_PREP_GATE_UP), MOE_EINVAL,
+                "moe_w4a16_gemm_act: relu2 is non-gated: weights must not be a gate/up pair");
   MOE_REQUIRE(numel >= 0 && numel < (1 << 30), MOE_EUNSUPPORTED, "moe_w4a16_gemm: numel=%lld", (long long)numel);
   MOE_REQUIRE(top_k >= 1 && block_m >= 1, MOE_EINVAL, "moe_w4a16_gemm: top_k=%d block_m=%d", top_k, block_m);
   MOE_REQUIRE(a_rows >= (numel + top_k - 1) / top_k, MOE_EINVAL,
@@ -60,7 +64,7 @@ static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64
   } else {
     int rc = moe_gemm_choose(W, numel, block_m, cus, &c);
     if (rc) return rc;
-    if (act != kActNone && c.ng < 2) c.ng = 2;  // the fused epilogue needs gate/up tile pairs
+    if (paired && c.ng < 2) c.ng = 2;  // the fused gated epilogue needs gate/up tile pairs
   }
   int64_t cap = 0, cap_blocks = 0;
   int rc = moe_align_capacity(numel, 1, W->n_experts, block_m, &cap, &cap_blocks);
@@ -122,9 +126,9 @@ extern "C" int moe_w4a16_gemm_act(moe_act_kind kind, float alpha, float limit, c
                                   const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
                                   int64_t numel, int32_t top_k, int32_t block_m,
                                   const moe_gemm_config* cfg, hipStream_t stream) {
-  MOE_REQUIRE(kind == MOE_ACT_SILU_MUL || kind == MOE_ACT_SWIGLU_ALPHA, MOE_EINVAL,
+  MOE_REQUIRE(kind == MOE_ACT_SILU_MUL || kind == MOE_ACT_SWIGLU_ALPHA || kind == MOE_ACT_RELU2, MOE_EINVAL,
               "moe_w4a16_gemm_act: unknown activation %d", (int)kind);
-  return gemm_impl(kind == MOE_ACT_SILU_MUL ? kActSilu : kActSwiglu, alpha, limit, A, a_rows, lda, out,
-                   ldo, W13, sorted_token_ids, expert_ids, num_tokens_post_padded, numel, top_k, block_m,
-                   cfg, stream);
+  const int act = kind == MOE_ACT_SILU_MUL ? kActSilu : (kind == MOE_ACT_SWIGLU_ALPHA ? kActSwiglu : kActRelu2);
+  return gemm_impl(act, alpha, limit, A, a_rows, lda, out, ldo, W13, sorted_token_ids, expert_ids,
+                   num_tokens_post_padded, numel, top_k, block_m, cfg, stream);
 }

@@ -38,7 +38,13 @@ struct GemmArgs {
 // Fused gate/up epilogue: the GEMM's output tiles come in (gate, up) pairs held by the same lane;
 // both are rounded to bf16 as the stored GEMM output would be, then the activation is applied
 // exactly as moe_act does, so the fused result equals GEMM + moe_act bit for bit.
-enum { kActNone = 0, kActSilu = 1, kActSwiglu = 2 };
+enum { kActNone = 0, kActSilu = 1, kActSwiglu = 2, kActRelu2 = 3 };
+// gated activations pair each gate tile with the up tile I/16 tiles further on
+template <int ACT>
+constexpr bool act_paired() { return ACT == kActSilu || ACT == kActSwiglu; }
+inline bool act_paired(int act) { return act == kActSilu || act == kActSwiglu; }
+// the non-gated relu2 epilogue: h rounded to bf16 as the stored GEMM output would be
+__device__ __forceinline__ float fused_relu2(float h) { return Relu2{0.f, 0.f}(bf16_to_f32(f32_to_bf16(h))); }
 template <int ACT>
 __device__ __forceinline__ float fused_act(float gate, float up, const GemmArgs& a) {
   const float g = bf16_to_f32(f32_to_bf16(gate)), u = bf16_to_f32(f32_to_bf16(up));

@@ -23,8 +23,8 @@ constexpr int kP = 2;  // K steps per prefetch batch
 
 template <int QT, bool BIAS, int NG, int KS, int ACT>
 __global__ __launch_bounds__(64 * KS) void gemm_decode_kernel(GemmArgs a, int gemv_rows) {
-  static_assert(ACT == kActNone || NG % 2 == 0, "the fused epilogue pairs gate and up tiles");
-  constexpr int NGA = ACT == kActNone ? NG : NG / 2;
+  static_assert(!act_paired<ACT>() || NG % 2 == 0, "the fused gated epilogue pairs gate and up tiles");
+  constexpr int NGA = act_paired<ACT>() ? NG / 2 : NG;
   extern __shared__ u32x4_t x_lds[];  // [gemv_rows][K / 8] activations of the dot-product path
   __shared__ int s_rows[16];
   __shared__ int s_cnt, s_e;
@@ -33,7 +33,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode_kernel(GemmArgs a, int ge
   // the wave index is uniform: keep it (and every LDS address derived from it) in scalar registers
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int NT = a.N / kTileN, KT = a.K / kTileK, kc = a.K / 8;
-  const int NTA = ACT == kActNone ? NT : NT / 2;  // tiles to assign (gate tiles if fused)
+  const int NTA = act_paired<ACT>() ? NT / 2 : NT;  // tiles to assign (gate tiles if fused)
   const int NS = (NTA + NGA - 1) / NGA;
   const int B = a.block_m;
   const int items = (*a.ntpp / B) * NS;
@@ -189,8 +189,10 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode_kernel(GemmArgs a, int ge
           for (int r = 0; r < kGemvMax; ++r) {
             if (r >= cnt) break;
             float v = epilogue<QT, BIAS>(dacc[g][r], a, e, n);
-            if constexpr (ACT != kActNone)
+            if constexpr (act_paired<ACT>())
               v = fused_act<ACT>(v, epilogue<QT, BIAS>(dacc[g + NGA][r], a, e, tile[g + NGA] * kTileN + lane), a);
+            else if constexpr (ACT == kActRelu2)
+              v = fused_relu2(v);
             a.C[(int64_t)s_rows[r] * a.ldc + n] = f32_to_bf16(v);
           }
         }
@@ -216,8 +218,10 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode_kernel(GemmArgs a, int ge
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) {
             v[qq] = epilogue<QT, BIAS>(macc[g][qq], a, e, n0 + qq);
-            if constexpr (ACT != kActNone)
+            if constexpr (act_paired<ACT>())
               v[qq] = fused_act<ACT>(v[qq], epilogue<QT, BIAS>(macc[g + NGA][qq], a, e, tile[g + NGA] * kTileN + 4 * (lane >> 4) + qq), a);
+            else if constexpr (ACT == kActRelu2)
+              v[qq] = fused_relu2(v[qq]);
           }
           *reinterpret_cast<u32x2_t*>(a.C + (int64_t)s_rows[m] * a.ldc + n0) =
               u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
@@ -242,13 +246,13 @@ static int launch_ng(const GemmArgs& a, const moe_gemm_config& c, int grid, hipS
 
 template <int QT, bool BIAS, int ACT>
 static int launch_decode_b(const GemmArgs& a, const moe_gemm_config& c, int grid, hipStream_t st) {
-  if constexpr (ACT == kActNone) {
+  if constexpr (!act_paired<ACT>()) {
     if (c.ng == 1) return launch_ng<QT, BIAS, 1, ACT>(a, c, grid, st);
   }
   switch (c.ng) {
     case 2: return launch_ng<QT, BIAS, 2, ACT>(a, c, grid, st);
     case 4: return launch_ng<QT, BIAS, 4, ACT>(a, c, grid, st);
-    default: return fail(MOE_EINVAL, "moe_w4a16_gemm: decode ng=%d (1, 2 or 4; 2 or 4 with a fused activation)", c.ng);
+    default: return fail(MOE_EINVAL, "moe_w4a16_gemm: decode ng=%d (1, 2 or 4; 2 or 4 with a fused gated activation)", c.ng);
   }
 }
 
@@ -256,7 +260,7 @@ template <int QT>
 int launch_gemm_decode(bool bias, int act, const GemmArgs& a, const moe_gemm_config& c, int cap_blocks,
                        int num_cus, hipStream_t st) {
   const int NT = a.N / kTileN;
-  const int nta = act == kActNone ? NT : NT / 2, nga = act == kActNone ? c.ng : c.ng / 2;
+  const int nta = act_paired(act) ? NT / 2 : NT, nga = act_paired(act) ? c.ng / 2 : c.ng;
   const int ns = (nta + nga - 1) / std::max(nga, 1);
   // persistent grid: enough workgroups to keep every CU streaming, never more than the items
   const int64_t max_items = (int64_t)cap_blocks * ns;
@@ -266,6 +270,8 @@ int launch_gemm_decode(bool bias, int act, const GemmArgs& a, const moe_gemm_con
       return bias ? launch_decode_b<QT, true, kActNone>(a, c, grid, st) : launch_decode_b<QT, false, kActNone>(a, c, grid, st);
     case kActSilu:
       return bias ? launch_decode_b<QT, true, kActSilu>(a, c, grid, st) : launch_decode_b<QT, false, kActSilu>(a, c, grid, st);
+    case kActRelu2:
+      return bias ? launch_decode_b<QT, true, kActRelu2>(a, c, grid, st) : launch_decode_b<QT, false, kActRelu2>(a, c, grid, st);
     default:
       return bias ? launch_decode_b<QT, true, kActSwiglu>(a, c, grid, st) : launch_decode_b<QT, false, kActSwiglu>(a, c, grid, st);
   }

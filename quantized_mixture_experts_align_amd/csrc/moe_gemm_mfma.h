@@ -89,8 +89,8 @@ __device__ __forceinline__ void grouped_block(int nblk, int gm_max, int& mb, int
 
 template <int QT, bool BIAS, int MG, int NG, int ACT>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
-  static_assert(ACT == kActNone || NG % 2 == 0, "the fused epilogue pairs gate and up tiles");
-  constexpr int NGA = ACT == kActNone ? NG : NG / 2;     // tiles per wave in the assigned range
+  static_assert(!act_paired<ACT>() || NG % 2 == 0, "the fused gated epilogue pairs gate and up tiles");
+  constexpr int NGA = act_paired<ACT>() ? NG / 2 : NG;     // tiles per wave in the assigned range
   constexpr int BM = 16 * MG;
   constexpr int FRAGS = 2 * MG * 64;                      // 16-B activation fragments per step
   constexpr int XL = FRAGS >= 256 ? FRAGS / 256 : 1;      // fragment loads per thread and step
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
   auto stage_ptr = [&](int stage) -> uint8_t* { return smem + stage * STAGE; };
 
   const int NT = a.N / kTileN, KT = a.K / kTileK;
-  const int NTA = ACT == kActNone ? NT : NT / 2;          // tiles to assign (gate tiles if fused)
+  const int NTA = act_paired<ACT>() ? NT / 2 : NT;          // tiles to assign (gate tiles if fused)
   const int nblk = (NTA + 4 * NGA - 1) / (4 * NGA);
   int mb, nb;
   grouped_block(nblk, a.group_m, mb, nb);
@@ -244,7 +244,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         o[q] = acc[g][h][q] * gsv + bv[g][q];
-        if constexpr (ACT != kActNone) o[q] = fused_act<ACT>(o[q], acc[g + NGA][h][q] * gsv + bv[g + NGA][q], a);
+        if constexpr (act_paired<ACT>()) o[q] = fused_act<ACT>(o[q], acc[g + NGA][h][q] * gsv + bv[g + NGA][q], a);
+        else if constexpr (ACT == kActRelu2) o[q] = fused_relu2(o[q]);
       }
       *reinterpret_cast<u32x2_t*>(a.C + (int64_t)row * a.ldc + n0) =
           u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
@@ -255,10 +256,10 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
 template <int QT, bool BIAS, int MG, int ACT>
 static int launch_mg(const GemmArgs& a, int ng, int blocks, hipStream_t st) {
   const int NT = a.N / kTileN;
-  const int nta = ACT == kActNone ? NT : NT / 2, nga = ACT == kActNone ? ng : ng / 2;
+  const int nta = act_paired<ACT>() ? NT / 2 : NT, nga = act_paired<ACT>() ? ng / 2 : ng;
   const int nblk = (nta + 4 * nga - 1) / (4 * nga);
   const dim3 grid((unsigned)((int64_t)nblk * blocks));
-  if constexpr (ACT == kActNone) {
+  if constexpr (!act_paired<ACT>()) {
     if (ng == 1) {
       hipLaunchKernelGGL((gemm_mfma_kernel<QT, BIAS, MG, 1, ACT>), grid, dim3(256), 0, st, a);
       return check_launch("moe_w4a16_gemm (mfma)");
@@ -268,7 +269,7 @@ static int launch_mg(const GemmArgs& a, int ng, int blocks, hipStream_t st) {
     case 2: hipLaunchKernelGGL((gemm_mfma_kernel<QT, BIAS, MG, 2, ACT>), grid, dim3(256), 0, st, a); break;
     case 4: hipLaunchKernelGGL((gemm_mfma_kernel<QT, BIAS, MG, 4, ACT>), grid, dim3(256), 0, st, a); break;
     default:
-      return fail(MOE_EINVAL, "moe_w4a16_gemm: ng=%d (1, 2 or 4; 2 or 4 with a fused activation)", ng);
+      return fail(MOE_EINVAL, "moe_w4a16_gemm: ng=%d (1, 2 or 4; 2 or 4 with a fused gated activation)", ng);
   }
   return check_launch("moe_w4a16_gemm (mfma)");
 }
@@ -296,6 +297,9 @@ int launch_gemm_mfma(bool bias, int act, const GemmArgs& a, const moe_gemm_confi
     case kActSilu:
       return bias ? launch_mfma_b<QT, true, kActSilu>(a, c.ng, cap_blocks, st)
                   : launch_mfma_b<QT, false, kActSilu>(a, c.ng, cap_blocks, st);
+    case kActRelu2:
+      return bias ? launch_mfma_b<QT, true, kActRelu2>(a, c.ng, cap_blocks, st)
+                  : launch_mfma_b<QT, false, kActRelu2>(a, c.ng, cap_blocks, st);
     default:
       return bias ? launch_mfma_b<QT, true, kActSwiglu>(a, c.ng, cap_blocks, st)
                   : launch_mfma_b<QT, false, kActSwiglu>(a, c.ng, cap_blocks, st);

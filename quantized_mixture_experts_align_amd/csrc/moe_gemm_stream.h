@@ -34,8 +34,8 @@ __device__ __forceinline__ void lds_barrier() {
 
 template <int QT, bool BIAS, int NG, int KS, int ACT>
 __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
-  static_assert(ACT == kActNone || NG % 2 == 0, "the fused epilogue pairs gate and up tiles");
-  constexpr int NGA = ACT == kActNone ? NG : NG / 2;
+  static_assert(!act_paired<ACT>() || NG % 2 == 0, "the fused gated epilogue pairs gate and up tiles");
+  constexpr int NGA = act_paired<ACT>() ? NG / 2 : NG;
   constexpr int D = NG >= 4 ? 4 : 8;  // ring depth (k-steps): about 9 KB of weights per wave
   __shared__ int t_e[kWin];
   __shared__ float t_gs[kWin];
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   // the wave index is uniform: keep it (and everything derived from it) in scalar registers
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int NT = a.N / kTileN, KT = a.K / kTileK;
-  const int NTA = ACT == kActNone ? NT : NT / 2;  // tiles to assign (gate tiles if fused)
+  const int NTA = act_paired<ACT>() ? NT / 2 : NT;  // tiles to assign (gate tiles if fused)
   const int NS = (NTA + NGA - 1) / NGA;           // strips per block
   const int B = a.block_m;
   const int items = (*a.ntpp / B) * NS;
@@ -163,7 +163,8 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) {
             v[qq] = fin(acc[g][qq], g, r0 + qq);
-            if constexpr (ACT != kActNone) v[qq] = fused_act<ACT>(v[qq], fin(acc[g + NGA][qq], g + NGA, r0 + qq), a);
+            if constexpr (act_paired<ACT>()) v[qq] = fused_act<ACT>(v[qq], fin(acc[g + NGA][qq], g + NGA, r0 + qq), a);
+            else if constexpr (ACT == kActRelu2) v[qq] = fused_relu2(v[qq]);
           }
           *reinterpret_cast<u32x2_t*>(a.C + (int64_t)s * a.ldc + tile_of(strip, g) * kTileN + r0) =
               u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
@@ -215,13 +216,13 @@ static int launch_stream_ng(const GemmArgs& a, int ks, int grid, hipStream_t st)
 
 template <int QT, bool BIAS, int ACT>
 static int launch_stream_b(const GemmArgs& a, const moe_gemm_config& c, int grid, hipStream_t st) {
-  if constexpr (ACT == kActNone) {
+  if constexpr (!act_paired<ACT>()) {
     if (c.ng == 1) return launch_stream_ng<QT, BIAS, 1, ACT>(a, c.ksplit, grid, st);
   }
   switch (c.ng) {
     case 2: return launch_stream_ng<QT, BIAS, 2, ACT>(a, c.ksplit, grid, st);
     case 4: return launch_stream_ng<QT, BIAS, 4, ACT>(a, c.ksplit, grid, st);
-    default: return fail(MOE_EINVAL, "moe_w4a16_gemm: decode ng=%d (1, 2 or 4; 2 or 4 with a fused activation)", c.ng);
+    default: return fail(MOE_EINVAL, "moe_w4a16_gemm: decode ng=%d (1, 2 or 4; 2 or 4 with a fused gated activation)", c.ng);
   }
 }
 
@@ -233,7 +234,7 @@ int launch_gemm_stream(bool bias, int act, const GemmArgs& a, const moe_gemm_con
   const int NT = a.N / kTileN, KT = a.K / kTileK;
   moe_gemm_config cc = c;  // every wave needs at least one k-tile: ksplit is capped at K/64
   while (cc.ksplit > 1 && cc.ksplit > KT) cc.ksplit /= 2;
-  const int nta = act == kActNone ? NT : NT / 2, nga = act == kActNone ? c.ng : c.ng / 2;
+  const int nta = act_paired(act) ? NT / 2 : NT, nga = act_paired(act) ? c.ng / 2 : c.ng;
   const int ns = (nta + nga - 1) / std::max(nga, 1);
   const int64_t max_items = (int64_t)cap_blocks * ns;
   const int64_t want = (int64_t)num_cus * std::max(1, 8 / std::max(cc.ksplit, 1));
@@ -245,6 +246,8 @@ int launch_gemm_stream(bool bias, int act, const GemmArgs& a, const moe_gemm_con
       return bias ? launch_stream_b<QT, true, kActNone>(a, cc, grid, st) : launch_stream_b<QT, false, kActNone>(a, cc, grid, st);
     case kActSilu:
       return bias ? launch_stream_b<QT, true, kActSilu>(a, cc, grid, st) : launch_stream_b<QT, false, kActSilu>(a, cc, grid, st);
+    case kActRelu2:
+      return bias ? launch_stream_b<QT, true, kActRelu2>(a, cc, grid, st) : launch_stream_b<QT, false, kActRelu2>(a, cc, grid, st);
     default:
       return bias ? launch_stream_b<QT, true, kActSwiglu>(a, cc, grid, st) : launch_stream_b<QT, false, kActSwiglu>(a, cc, grid, st);
   }

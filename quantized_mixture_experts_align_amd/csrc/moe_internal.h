@@ -76,6 +76,14 @@ struct SiluMul {
   float alpha, limit;
   __device__ __forceinline__ float operator()(float g, float u) const { return g * sigmoid_f(g) * u; }
 };
+// Non-gated relu(h)^2 (the relu2 activation of the sglang PR 31552 test, is_gated=False).
+struct Relu2 {
+  float alpha, limit;
+  __device__ __forceinline__ float operator()(float h) const {
+    const float r = fmaxf(h, 0.0f);
+    return r * r;
+  }
+};
 // GPT-OSS: gate clamped from above, up clamped to [-limit, limit], then
 // gate * sigmoid(alpha * gate) * (up + 1)  (swiglu_gpt_oss_sigmoid_alpha_contiguous, sglang PR 28231).
 struct SwigluAlpha {

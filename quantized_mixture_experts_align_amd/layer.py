@@ -36,27 +36,38 @@ class MoELayer:
 
     ``w13`` / ``w2``: dicts of device tensors in the canonical layouts: ``codes`` uint8
     [E, N, K/2], ``scales`` [E, N, K/g], optional ``gs`` fp32 [E] (NVFP4) and ``bias`` bf16 [E, N].
+    ``w13`` has 2I rows (gate, up) for the gated activations and I rows for ``relu2``.
+    ``routed_scaling_factor`` multiplies the combined output.
     """
 
     def __init__(self, qtype: str, w13: dict, w2: dict, *, expert_start: int, n_local: int,
                  top_k: int, act: str = "silu_mul", alpha: float = 1.702,
                  limit: float = float("inf"), post_norm_w: Optional[torch.Tensor] = None,
                  eps: float = 1e-8, interleaved_w13: bool = False, pad: bool = False,
-                 n_global: Optional[int] = None):
+                 n_global: Optional[int] = None, routed_scaling_factor: float = 1.0):
+        if act not in L.ACT:
+            raise ValueError(f"unknown activation {act!r}")
         self.qtype, self.expert_start, self.n_local, self.top_k = qtype, expert_start, n_local, top_k
         self.n_global = n_global
         self.act, self.alpha, self.limit, self.eps = act, alpha, limit, eps
-        f13 = L.PREP_GATE_UP | (L.PREP_INTERLEAVED if interleaved_w13 else 0) | (L.PREP_PAD if pad else 0)
+        self.gated = L.GATED[act]
+        self.routed_scaling_factor = routed_scaling_factor
+        if self.gated:
+            f13 = L.PREP_GATE_UP | (L.PREP_INTERLEAVED if interleaved_w13 else 0) | (L.PREP_PAD if pad else 0)
+        else:
+            if interleaved_w13:
+                raise ValueError("interleaved gate/up rows need a gated activation")
+            f13 = L.PREP_PAD if pad else 0
         f2 = L.PREP_PAD if pad else 0
         self.W13 = ops.moe_w4a16_prepare(qtype, w13["codes"], w13["scales"], w13.get("gs"),
                                          w13.get("bias"), f13)
         self.W2 = ops.moe_w4a16_prepare(qtype, w2["codes"], w2["scales"], w2.get("gs"),
                                         w2.get("bias"), f2)
-        if self.W2.K != self.W13.N // 2:
-            raise ValueError(f"down projection K={self.W2.K} != intermediate {self.W13.N // 2}")
+        self.I = self.W13.N // 2 if self.gated else self.W13.N
+        if self.W2.K != self.I:
+            raise ValueError(f"down projection K={self.W2.K} != intermediate {self.I}")
         if self.W2.n_experts != n_local or self.W13.n_experts != n_local:
             raise ValueError("weights must hold exactly the n_local local experts")
-        self.I = self.W13.N // 2
         self.H = self.W2.N
         self.norm_w = None if post_norm_w is None else ops.moe_norm_weight(post_norm_w)
 
@@ -85,7 +96,7 @@ class MoELayer:
         bf = dict(dtype=torch.bfloat16, device=device)
         return Workspace(M, B, torch.empty(s_len, **i32), torch.empty(b_len, **i32),
                          torch.empty(1, **i32), torch.empty((M, self.top_k), **i32),
-                         torch.empty(numel * max(2 * self.I, self.H), **bf),
+                         torch.empty(numel * max(self.W13.N, self.H), **bf),
                          torch.empty((numel, self.I), **bf), torch.empty((M, self.H), **bf),
                          self.configs(M, B))
 
@@ -93,8 +104,8 @@ class MoELayer:
                 ws: Optional[Workspace] = None, cfg13=None, cfg2=None,
                 fused_act: bool = True) -> torch.Tensor:
         """align -> gate/up GEMM -> activation -> down GEMM -> combine.  With fused_act the
-        activation runs in the gate/up GEMM's epilogue (bitwise the same result, one launch
-        and one [numel, 2I] round trip less); cfg13 must then have ng 2 or 4."""
+        activation runs in the GEMM1 epilogue (bitwise the same result, one launch and one
+        [numel, N13] round trip less); for a gated activation cfg13 then needs ng 2 or 4."""
         M = x.shape[0]
         if ws is None:
             ws = self.workspace(M, device=x.device)
@@ -110,16 +121,17 @@ class MoELayer:
             topk_ids, self.expert_start, self.n_local, B,
             out=(ws.sorted_ids, ws.expert_ids, ws.ntpp, ws.slot_local))
         if fused_act:
-            if cfg13.ng < 2:
+            if self.gated and cfg13.ng < 2:
                 cfg13 = ops.gemm_config(cfg13.kernel, 2, cfg13.ksplit, cfg13.gemv_rows, cfg13.group_m)
             ops.moe_w4a16_gemm_act(self.act, x, self.W13, sorted_ids, eids, ntpp, numel, self.top_k, B,
                                    self.alpha, self.limit, out=ws.a, cfg=cfg13)
         else:
-            h = ws.buf13[: numel * 2 * self.I].view(numel, 2 * self.I)
+            h = ws.buf13[: numel * self.W13.N].view(numel, self.W13.N)
             ops.moe_w4a16_gemm(x, self.W13, sorted_ids, eids, ntpp, numel, self.top_k, B, out=h, cfg=cfg13)
             ops.moe_act(self.act, h, self.I, loc.view(-1), self.alpha, self.limit, out=ws.a)
         y = ws.buf13[: numel * self.H].view(numel, self.H)
         ops.moe_w4a16_gemm(ws.a, self.W2, sorted_ids, eids, ntpp, numel, 1, B, out=y, cfg=cfg2)
-        return ops.moe_combine(y, topk_weights, loc, self.norm_w, self.eps, out=ws.out)
+        return ops.moe_combine(y, topk_weights, loc, self.norm_w, self.eps, out=ws.out,
+                               routed_scaling_factor=self.routed_scaling_factor)
 
     __call__ = forward

@@ -160,10 +160,12 @@ def moe_w4a16_gemm_act(kind: str, A: torch.Tensor, W13: PreparedWeights, sorted_
                        top_k: int, block_m: int, alpha: float = 1.702, limit: float = float("inf"),
                        out: Optional[torch.Tensor] = None,
                        cfg: Optional[L.MoeGemmConfig] = None) -> torch.Tensor:
-    """out[slot] = act(gate, up) of the gate/up GEMM, fused into one launch; out is [numel, I]."""
+    """out[slot] = act(gate, up) of the gate/up GEMM (or relu(h)^2 of the non-gated GEMM1),
+    fused into one launch; out is [numel, I]."""
     _need(A, torch.bfloat16, "A")
     if out is None:
-        out = torch.empty((numel, W13.N // 2), dtype=torch.bfloat16, device=A.device)
+        I = W13.N if kind == "relu2" else W13.N // 2
+        out = torch.empty((numel, I), dtype=torch.bfloat16, device=A.device)
     _need(out, torch.bfloat16, "out")
     L.check(L.lib().moe_w4a16_gemm_act(L.ACT[kind], alpha, limit, _ptr(A), A.shape[0], A.stride(0),
                                        _ptr(out), out.stride(0), C.byref(W13.desc),
@@ -188,7 +190,7 @@ def moe_act(kind: str, h: torch.Tensor, I: int, slot_local_ids: Optional[torch.T
 
 def moe_combine(y: torch.Tensor, topk_weights: torch.Tensor, slot_local_ids: torch.Tensor,
                 norm_w: Optional[torch.Tensor] = None, eps: float = 1e-8,
-                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                out: Optional[torch.Tensor] = None, routed_scaling_factor: float = 1.0) -> torch.Tensor:
     _need(y, torch.bfloat16, "y")
     _need(topk_weights, torch.float32, "topk_weights")
     _need(slot_local_ids, torch.int32, "slot_local_ids")
@@ -197,5 +199,5 @@ def moe_combine(y: torch.Tensor, topk_weights: torch.Tensor, slot_local_ids: tor
     if out is None:
         out = torch.empty((M, H), dtype=torch.bfloat16, device=y.device)
     L.check(L.lib().moe_combine(_ptr(y), _ptr(topk_weights), _ptr(slot_local_ids), _ptr(norm_w), eps,
-                                M, k, H, _ptr(out), _stream()), "moe_combine")
+                                routed_scaling_factor, M, k, H, _ptr(out), _stream()), "moe_combine")
     return out

@@ -28,7 +28,8 @@ def oracle_layer(wl: W.Workload, lw, inp, tokens=None):
     return O.moe_layer(wl.qtype, inp.x, inp.topk_ids, inp.topk_weights, lw.w13, lw.w2,
                        expert_start=wl.expert_start, n_local=wl.n_local, act=wl.act, alpha=wl.alpha,
                        limit=wl.limit, norm_w_bits=lw.norm_w, eps=wl.eps,
-                       interleaved_w13=wl.interleaved_w13, tokens=tokens)
+                       interleaved_w13=wl.interleaved_w13, routed_scaling_factor=wl.routed_scaling_factor,
+                       tokens=tokens)
 
 
 def make_layer(wl: W.Workload, lw, pad: bool = False):
@@ -37,7 +38,7 @@ def make_layer(wl: W.Workload, lw, pad: bool = False):
     return MoELayer(wl.qtype, w13, w2, expert_start=wl.expert_start, n_local=wl.n_local,
                     top_k=wl.top_k, act=wl.act, alpha=wl.alpha, limit=wl.limit, post_norm_w=nw,
                     eps=wl.eps, interleaved_w13=wl.interleaved_w13, pad=pad,
-                    n_global=wl.n_global)
+                    n_global=wl.n_global, routed_scaling_factor=wl.routed_scaling_factor)
 
 
 def announce(msg: str) -> None:

@@ -68,8 +68,11 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.moe_align(None, 4, 8, 0, 32, 16, None, e, n, None, None) == L.MOE_EINVAL
     assert lib.moe_act(7, s, 16, s, 8, 4, 8, None, 1.0, 1.0, None) == L.MOE_EINVAL
     assert lib.moe_act(0, s, 16, s, 8, 4, 12, None, 1.0, 1.0, None) == L.MOE_EUNSUPPORTED
-    assert lib.moe_combine(s, s, s, None, 1e-8, 4, 17, 64, s, None) == L.MOE_EUNSUPPORTED
-    assert lib.moe_combine(s, s, s, None, 1e-8, 4, 8, 60, s, None) == L.MOE_EUNSUPPORTED
+    assert lib.moe_combine(s, s, s, None, 1e-8, 1.0, 4, 17, 64, s, None) == L.MOE_EUNSUPPORTED
+    assert lib.moe_combine(s, s, s, None, 1e-8, 1.0, 4, 8, 60, s, None) == L.MOE_EUNSUPPORTED
+    # a gated activation's input needs 2I columns (relu2, non-gated, I: checked on the GPU)
+    assert lib.moe_act(L.ACT["silu_mul"], s, 16, s, 16, 4, 16, None, 1.0, 1.0, None) == L.MOE_EINVAL
+    assert lib.moe_act(L.ACT["relu2"], s, 8, s, 16, 4, 16, None, 1.0, 1.0, None) == L.MOE_EINVAL
     W = L.MoeWeights(1, 32, 8192, 4096, 8192, 4096, 1, 0, 256, 256, None, None)  # NVFP4 without gs
     assert lib.moe_w4a16_gemm(s, 8, 4096, s, 8192, C.byref(W), s, s, s, 8, 8, 16, None, None) == L.MOE_EINVAL
     W.global_scale = 256
@@ -82,6 +85,13 @@ def test_entry_points_reject_bad_arguments_before_launch():
     cfg = L.MoeGemmConfig(L.GEMM_DECODE, 0, 3, 4)
     assert lib.moe_w4a16_gemm(s, 8, 4096, s, 8192, C.byref(W), s, s, s, 8, 8, 16, C.byref(cfg), None) \
         != L.MOE_OK
+    # relu2 takes a plain projection, the gated kinds a gate/up pair
+    assert lib.moe_w4a16_gemm_act(L.ACT["relu2"], 1.0, 1.0, s, 8, 4096, s, 8192, C.byref(W), s, s, s, 8, 8, 16,
+                                  None, None) == L.MOE_EINVAL and b"non-gated" in lib.moe_last_error()
+    W.flags = 0
+    assert lib.moe_w4a16_gemm_act(L.ACT["silu_mul"], 1.0, 1.0, s, 8, 4096, s, 8192, C.byref(W), s, s, s, 8, 8,
+                                  16, None, None) == L.MOE_EINVAL and b"gate/up pair" in lib.moe_last_error()
+    W.flags = 1
     # numel == 0 is a no-op that needs no device
     assert lib.moe_w4a16_gemm(None, 0, 4096, None, 8192, C.byref(W), None, None, None, 0, 8, 16, None, None) \
         == L.MOE_OK

@@ -121,11 +121,13 @@ def test_gemm_pad_intermediate():
     assert W13.N == 640
 
 
-@pytest.mark.parametrize("kind,limit", [("silu_mul", math.inf), ("swiglu_alpha", math.inf), ("swiglu_alpha", 7.0)])
+@pytest.mark.parametrize("kind,limit", [("silu_mul", math.inf), ("swiglu_alpha", math.inf), ("swiglu_alpha", 7.0),
+                                        ("relu2", math.inf)])
 def test_act_matches_oracle(kind, limit):
     rng = np.random.default_rng(3)
     R, I = 77, 320
-    h_bits = W._to_bf16_bits((rng.standard_normal((R, 2 * I)) * 3).astype(np.float32))
+    cols = I if kind == "relu2" else 2 * I
+    h_bits = W._to_bf16_bits((rng.standard_normal((R, cols)) * 3).astype(np.float32))
     loc = rng.integers(-1, 4, size=R).astype(np.int32)
     out = torch.full((R, I), float("nan"), dtype=torch.bfloat16, device="cuda")
     P.moe_act(kind, _bf16_dev(h_bits), I, torch.from_numpy(loc).cuda(), 1.702, limit, out=out)
@@ -133,7 +135,10 @@ def test_act_matches_oracle(kind, limit):
     got = W.bf16_to_float(out)
     h = F.decode_bf16(h_bits)
     g, u = h[:, :I], h[:, I:]
-    ref = O.act_silu_mul(g, u) if kind == "silu_mul" else O.act_swiglu_alpha(g, u, 1.702, limit)
+    if kind == "relu2":
+        ref = O.act_relu2(h)
+    else:
+        ref = O.act_silu_mul(g, u) if kind == "silu_mul" else O.act_swiglu_alpha(g, u, 1.702, limit)
     live = loc >= 0
     assert np.all(np.isnan(got[~live]))                 # dead rows untouched
     err = np.abs(got[live] - ref[live])
@@ -146,7 +151,8 @@ def test_act_matches_oracle(kind, limit):
                                         (2880, True, 45, 8), (64, True, 45, 8), (4096, True, 300, 8),
                                         (512, False, 300, 2), (2880, True, 45, 4), (8192, True, 20, 8),
                                         (512, True, 20, 16), (16384, True, 5, 8)])
-def test_combine_matches_oracle(H, norm, M, k):
+@pytest.mark.parametrize("rsf", [1.0, 2.5])
+def test_combine_matches_oracle(H, norm, M, k, rsf):
     rng = np.random.default_rng(H + M + k)
     y_bits = W._to_bf16_bits(rng.standard_normal((M * k, H)).astype(np.float32))
     g = rng.random((M, k)).astype(np.float32)
@@ -156,10 +162,11 @@ def test_combine_matches_oracle(H, norm, M, k):
     y_dev.view(M, k, H)[torch.from_numpy(loc < 0).cuda()] = float("nan")   # dead rows never read
     nw_bits = W._to_bf16_bits(rng.normal(0, 0.1, H).astype(np.float32)) if norm else None
     nw_dev = P.moe_norm_weight(_bf16_dev(nw_bits)) if norm else None
-    out = P.moe_combine(y_dev, torch.from_numpy(g).cuda(), torch.from_numpy(loc).cuda(), nw_dev, 1e-8)
+    out = P.moe_combine(y_dev, torch.from_numpy(g).cuda(), torch.from_numpy(loc).cuda(), nw_dev, 1e-8,
+                        routed_scaling_factor=rsf)
     torch.cuda.synchronize()
     got = W.bf16_to_float(out)
-    ref = O.combine(F.decode_bf16(y_bits), g, loc, O.norm_weight(nw_bits) if norm else None, 1e-8)
+    ref = O.combine(F.decode_bf16(y_bits), g, loc, O.norm_weight(nw_bits) if norm else None, 1e-8, rsf)
     assert np.all(got[0] == 0)
     err = np.abs(got - ref)
     assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-3 * np.sqrt(np.mean(ref ** 2))), err.max()
@@ -167,24 +174,31 @@ def test_combine_matches_oracle(H, norm, M, k):
         assert np.array_equal(W.bf16_to_float(nw_dev), O.norm_weight(nw_bits))
 
 
-@pytest.mark.parametrize("kind", ["decode", "mfma"])
+@pytest.mark.parametrize("act", ["own", "relu2"])
+@pytest.mark.parametrize("kind", ["decode", "decode_gemv", "mfma"])
 @pytest.mark.parametrize("qtype", W.QTYPES)
-def test_fused_activation_equals_gemm_then_act(qtype, kind):
-    """The gate/up GEMM with the activation in its epilogue gives the same bytes as
-    moe_w4a16_gemm followed by moe_act (both round gate/up to bf16 before the activation)."""
+def test_fused_activation_equals_gemm_then_act(qtype, kind, act):
+    """GEMM1 with the activation in its epilogue gives the same bytes as moe_w4a16_gemm
+    followed by moe_act (both round the GEMM values to bf16 before the activation); "own" is
+    the workload's gated activation, relu2 the non-gated one (a plain projection)."""
     wl = W.small_workload(qtype)
+    if act == "relu2":
+        wl = wl.replace(act="relu2", interleaved_w13=False)
     lw = W.make_weights(wl)
-    M, B, cfg = (5, 16, P.gemm_config(L.GEMM_DECODE, 2, 4, 0)) if kind == "decode" else \
-        (150, 64, P.gemm_config(L.GEMM_MFMA, 2, 0, 0))
+    ng = 1 if act == "relu2" else 2
+    M, B, cfg = {"decode": (5, 16, P.gemm_config(L.GEMM_DECODE, ng, 4, 0)),
+                 "decode_gemv": (5, 16, P.gemm_config(L.GEMM_DECODE, 2, 2, 2)),
+                 "mfma": (150, 64, P.gemm_config(L.GEMM_MFMA, ng, 0, 0))}[kind]
     inp = W.make_inputs(wl, M)
     w13, _, _ = W.device_weights(lw)
-    flags = L.PREP_GATE_UP | (L.PREP_INTERLEAVED if wl.interleaved_w13 else 0)
+    flags = 0 if act == "relu2" else L.PREP_GATE_UP | (L.PREP_INTERLEAVED if wl.interleaved_w13 else 0)
     W13 = P.moe_w4a16_prepare(qtype, w13["codes"], w13["scales"], w13.get("gs"), w13.get("bias"), flags)
     s, e, n, loc = P.moe_align(torch.from_numpy(inp.topk_ids).cuda(), wl.expert_start, wl.n_local, B)
     x = _bf16_dev(inp.x)
     numel = M * wl.top_k
     h = P.moe_w4a16_gemm(x, W13, s, e, n, numel, wl.top_k, B, cfg=cfg)
-    a_ref = P.moe_act(wl.act, h, W13.N // 2, loc.view(-1), wl.alpha, 7.0)
+    I = W13.N if act == "relu2" else W13.N // 2
+    a_ref = P.moe_act(wl.act, h, I, loc.view(-1), wl.alpha, 7.0)
     a = P.moe_w4a16_gemm_act(wl.act, x, W13, s, e, n, numel, wl.top_k, B, wl.alpha, 7.0, cfg=cfg)
     torch.cuda.synchronize()
     live = torch.from_numpy(np.nonzero(loc.cpu().numpy().reshape(-1) >= 0)[0]).cuda()

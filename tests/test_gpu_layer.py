@@ -49,6 +49,28 @@ def test_small_layer_every_gemm_kernel(qtype):
         assert layer_violations(got, ref) == 0
 
 
+@pytest.mark.parametrize("qtype", W.QTYPES)
+def test_small_layer_relu2_routed_scaling(qtype):
+    # the non-gated relu2 activation (GEMM1 has I rows) and a routed scaling factor, on the
+    # streaming, dot-product and MFMA kernels.  (relu^2 makes the int4 outputs large -- RMS
+    # about 2.6 at factor 1 -- and the bar's absolute term does not scale with them: at factor
+    # 1.75 about 3 in 77k int4 outputs sit 4 sigma out, from the bf16 rounding of int4 weights.)
+    wl = W.small_workload(qtype).replace(act="relu2", interleaved_w13=False, routed_scaling_factor=0.625)
+    lw = W.make_weights(wl)
+    layer = make_layer(wl, lw)
+    assert layer.I == wl.I
+    for M, B, cfg in [(6, 16, None), (6, 16, P.gemm_config(L.GEMM_DECODE, 2, 2, 4)), (150, 64, None),
+                      (150, 32, P.gemm_config(L.GEMM_MFMA, 1, 0, 0))]:
+        inp = W.make_inputs(wl, M)
+        announce(f"layer relu2 {qtype} M={M} B={B}")
+        got = _forward(layer, inp, ws=layer.workspace(M, B), cfg13=cfg, cfg2=cfg)
+        ref = oracle_layer(wl, lw, inp)
+        assert layer_violations(got, ref) == 0
+        assert rel_rms(got, ref) < 0.01
+        unf = _forward(layer, inp, ws=layer.workspace(M, B), cfg13=cfg, cfg2=cfg, fused_act=False)
+        assert np.array_equal(got, unf)
+
+
 def test_padded_intermediate_layer():
     # I = 288: zero-padded to 320 at prepare (GPT-OSS tile padding); same result as unpadded
     wl = W.small_workload("mxfp4_g32", I=288)

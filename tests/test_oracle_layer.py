@@ -126,6 +126,12 @@ def test_swiglu_alpha_hand_values():
         12.0 * _sig(a * 12.0) * 10.0, rel=1e-15)
 
 
+def test_relu2_hand_values():
+    h = np.array([-2.0, -0.5, 0.0, 0.5, 3.0, -0.0])
+    assert list(O.act_relu2(h)) == [0.0, 0.0, 0.0, 0.25, 9.0, 0.0]
+    assert not O.GATED["relu2"] and O.GATED["silu_mul"] and O.GATED["swiglu_alpha"]
+
+
 def test_split_gate_up_golden():
     g = json.load(open(os.path.join(GOLDEN, "deinterleave_small.json")))
     rows = np.array(g["rows_in"], dtype=object)
@@ -160,6 +166,18 @@ def test_combine_reduces_to_rmsnorm_and_weighted_sum():
     out = O.combine(Y, g, loc, None, 1e-8)
     assert np.allclose(out[0], g[0, 0] * Y[0] + g[0, 1] * Y[1], rtol=1e-14)
     assert np.allclose(out[1], g[1, 0] * Y[3] + g[1, 2] * Y[5], rtol=1e-14)
+
+
+def test_combine_routed_scaling_factor():
+    Y = np.array([[1.0, -2.0], [0.5, 4.0]])
+    g = np.array([[0.25, 0.75]])
+    loc = np.array([[0, 3]])
+    out = O.combine(Y, g, loc, None, 1e-8, routed_scaling_factor=2.5)
+    assert np.allclose(out[0], [2.5 * (0.25 * 1.0 + 0.75 * 0.5), 2.5 * (0.25 * -2.0 + 0.75 * 4.0)], rtol=1e-15)
+    nw = np.array([1.0, 1.0])
+    a = O.combine(Y, g, loc, nw, 1e-8, routed_scaling_factor=1.0)
+    b = O.combine(Y, g, loc, nw, 1e-8, routed_scaling_factor=-3.0)
+    assert np.allclose(b, -3.0 * a, rtol=1e-15)
 
 
 def test_norm_weight_rounds_one_plus_w_to_bf16():
@@ -217,6 +235,23 @@ def test_layer_mxfp4_swiglu_interleaved_bias_closed_form(limit):
     a = g * _sig(1.702 * g) * (u + 1)
     y = 0.25 * I * a + 0.5
     assert np.allclose(out, 0.875 * y, rtol=1e-14)
+
+
+def test_layer_int4_relu2_non_gated_bias_closed_form():
+    # non-gated GEMM1 (I rows), relu(h)^2 with a negative row that relu zeroes, routed scaling
+    H, I = 128, 128
+    x0 = 0.25
+    b13 = [_bf16(0.25)] * I
+    w13 = _const_proj([11] * (I // 2) + [6] * (I // 2), H, _bf16(2.0 ** -7), np.uint16, 128, bias=b13)  # 3, -2
+    w2 = _const_proj([9] * H, I, _bf16(2.0 ** -5), np.uint16, 128, bias=[_bf16(-0.25)] * H)            # 1
+    x = np.full((1, H), _bf16(x0), np.uint16)
+    out = O.moe_layer("int4_g128", x, np.array([[0]], np.int32), np.array([[0.625]], np.float32),
+                      w13, w2, expert_start=0, n_local=1, act="relu2", routed_scaling_factor=1.5,
+                      bf16_intermediates=False)
+    hp = 3 * 2.0 ** -7 * H * x0 + 0.25           # = 1.0, relu keeps it
+    hn = -2 * 2.0 ** -7 * H * x0 + 0.25          # = -0.25, relu zeroes it
+    y = 2.0 ** -5 * ((I // 2) * hp ** 2 + (I // 2) * max(hn, 0.0) ** 2) - 0.25
+    assert np.allclose(out, 1.5 * 0.625 * y, rtol=1e-14)
 
 
 def _small(qtype, M=None, **kw):

@@ -55,7 +55,8 @@ class Workload:
     I: int
     Ms: tuple
     bias: bool = False
-    act: str = "silu_mul"  # or "swiglu_alpha"
+    act: str = "silu_mul"  # or "swiglu_alpha", or "relu2" (non-gated: GEMM1 has I rows)
+    routed_scaling_factor: float = 1.0
     alpha: float = 1.702
     limit: float = float("inf")
     norm: bool = False
@@ -151,11 +152,12 @@ def make_weights(wl: Workload) -> LayerWeights:
     if H % wl.group or I % wl.group:
         raise ValueError("H and I must be multiples of the quantisation group")
     rng = _rng(wl.seed, 0, _S_WEIGHTS)
-    w13 = _projection(rng, wl, E, 2 * I, H)
+    n13 = I if wl.act == "relu2" else 2 * I   # gate/up rows, or the non-gated projection
+    w13 = _projection(rng, wl, E, n13, H)
     w2 = _projection(rng, wl, E, H, I)
     aux = _rng(wl.seed, 0, _S_AUX)
     if wl.bias:
-        w13.bias = _to_bf16_bits(aux.normal(0.0, 0.1, size=(E, 2 * I)).astype(np.float32))
+        w13.bias = _to_bf16_bits(aux.normal(0.0, 0.1, size=(E, n13)).astype(np.float32))
         w2.bias = _to_bf16_bits(aux.normal(0.0, 0.1, size=(E, H)).astype(np.float32))
     norm_w = None
     if wl.norm:
