@@ -1,6 +1,6 @@
 """Benchmark of the W4A16 MoE expert layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config C] [--M M] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--M M] [--no-cpu-baseline]
 
 A step is one pass of the whole layer (align -> gate/up GEMM -> activation -> down GEMM ->
 combine) over one batch of seeded synthetic inputs already resident in HBM.  The default
@@ -107,13 +107,13 @@ def cpu_baseline(wl, lw, inp, budget_s: float = 12.0) -> dict:
 _LAYERS: dict = {}   # prepared weights reused across cells of one weight set
 
 
-def run_cell(cfg: int, M: int, steps: int, warmup: int, want_cpu: bool, seed=None) -> dict:
+def run_cell(name: str, M: int, steps: int, warmup: int, want_cpu: bool, seed=None) -> dict:
     import torch
     import workloads as W
     from quantized_mixture_experts_align_amd import MoELayer
     import quantized_mixture_experts_align_amd as P
 
-    wl = W.CONFIGS[cfg]
+    wl = W.WORKLOADS[name]
     dev = torch.device("cuda", 0)
     if _LAYERS.get("seed") != wl.seed:
         _LAYERS.clear()
@@ -269,7 +269,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--workload", default=None, help="workload name (default: the int4 layer with "
+                    "biases, M=2304); one of the names in workloads.WORKLOADS")
     ap.add_argument("--M", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="one line per configuration cell")
@@ -296,13 +297,17 @@ def main() -> int:
         return 0
     import workloads as W
     if a.sweep:
-        for cfg, wl in W.CONFIGS.items():
+        for name, wl in W.WORKLOADS.items():
             for M in wl.Ms:
-                r = run_cell(cfg, M, a.steps, a.warmup, False)
+                r = run_cell(name, M, a.steps, a.warmup, False)
                 print(json.dumps(r), flush=True)
         return 0
-    M = a.M or W.CONFIGS[a.config].Ms[0]
-    r = run_cell(a.config, M, a.steps, a.warmup, not a.no_cpu_baseline)
+    name = a.workload or W.HEADLINE
+    if name not in W.WORKLOADS:
+        print(f"unknown workload {name!r}; one of {list(W.WORKLOADS)}", file=sys.stderr)
+        return 2
+    M = a.M or W.WORKLOADS[name].Ms[0]
+    r = run_cell(name, M, a.steps, a.warmup, not a.no_cpu_baseline)
     print(json.dumps(r), flush=True)
     return 0
 

@@ -28,11 +28,13 @@ def _check(ids, start, n_local, B):
     assert np.array_equal(gl, rl)
 
 
-@pytest.mark.parametrize("cfg,M,B", [(0, 123, 32), (1, 2304, 128), (2, 1, 16), (2, 4, 16), (2, 16, 16),
-                                     (2, 64, 16), (3, 256, 64), (3, 1024, 128), (3, 4096, 128),
-                                     (4, 1, 16), (4, 32, 16), (4, 2048, 64)])
-def test_align_config_routing(cfg, M, B):
-    wl = W.CONFIGS[cfg]
+@pytest.mark.parametrize("name,M,B", [(W.INT4_SMALL, 123, 32), (W.INT4_BIAS, 2304, 128),
+                                      (W.NVFP4_DECODE, 1, 16), (W.NVFP4_DECODE, 4, 16), (W.NVFP4_DECODE, 16, 16),
+                                      (W.NVFP4_DECODE, 64, 16), (W.NVFP4_ZIPF, 256, 64), (W.NVFP4_ZIPF, 1024, 128),
+                                      (W.NVFP4_ZIPF, 4096, 128), (W.MXFP4_SWIGLU, 1, 16), (W.MXFP4_SWIGLU, 32, 16),
+                                      (W.MXFP4_SWIGLU, 2048, 64)])
+def test_align_workload_routing(name, M, B):
+    wl = W.WORKLOADS[name]
     inp = W.make_inputs(wl, M)
     _check(inp.topk_ids, wl.expert_start, wl.n_local, B)
 
@@ -71,7 +73,7 @@ def test_align_edge_cases():
 
 
 def test_align_deterministic_and_optional_slot_ids():
-    inp = W.make_inputs(W.CONFIGS[3], 4096)
+    inp = W.make_inputs(W.WORKLOADS[W.NVFP4_ZIPF], 4096)
     a = _run(inp.topk_ids, 0, 32, 128)
     b = _run(inp.topk_ids, 0, 32, 128, slot_ids=False)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2] and b[3] is None

@@ -1,5 +1,5 @@
 """Whole-layer GPU parity against the oracle: small shapes (several tiles, ragged tails) in
-full, the five workload configurations at full size on sampled tokens, and edge cases."""
+full, the five workloads at full size on sampled tokens, and edge cases."""
 import numpy as np
 import pytest
 import torch
@@ -97,12 +97,12 @@ def test_off_slice_tokens_are_zero_and_runs_repeat_bitwise():
     assert layer_violations(a, oracle_layer(wl, lw, inp2)) == 0
 
 
-# ----------------------------------------------------------------------------- full-size configs
+# ----------------------------------------------------------------------------- full-size workloads
 _CACHE = {}
 
 
-def _cfg_layer(cfg):
-    wl = W.CONFIGS[cfg]
+def _workload_layer(name):
+    wl = W.WORKLOADS[name]
     key = wl.seed
     if key not in _CACHE:
         _CACHE.clear()                   # keep one weight set resident at a time
@@ -118,13 +118,16 @@ def _sample(M, n, seed=0):
     return np.sort(rng.choice(M, size=n, replace=False))
 
 
-@pytest.mark.parametrize("cfg,M,n_sample", [(0, 123, 123), (1, 2304, 2304), (2, 1, 1), (2, 4, 4), (2, 16, 5),
-                                            (2, 64, 5), (3, 256, 4), (3, 1024, 3), (3, 4096, 3),
-                                            (4, 1, 1), (4, 32, 4), (4, 2048, 4)])
-def test_config_layer_matches_oracle(cfg, M, n_sample):
-    wl, lw, layer = _cfg_layer(cfg)
+@pytest.mark.parametrize("name,M,n_sample", [(W.INT4_SMALL, 123, 123), (W.INT4_BIAS, 2304, 2304),
+                                             (W.NVFP4_DECODE, 1, 1), (W.NVFP4_DECODE, 4, 4),
+                                             (W.NVFP4_DECODE, 16, 5), (W.NVFP4_DECODE, 64, 5),
+                                             (W.NVFP4_ZIPF, 256, 4), (W.NVFP4_ZIPF, 1024, 3), (W.NVFP4_ZIPF, 4096, 3),
+                                             (W.MXFP4_SWIGLU, 1, 1), (W.MXFP4_SWIGLU, 32, 4),
+                                             (W.MXFP4_SWIGLU, 2048, 4)])
+def test_workload_layer_matches_oracle(name, M, n_sample):
+    wl, lw, layer = _workload_layer(name)
     inp = W.make_inputs(wl, M)
-    announce(f"layer config {cfg} M={M} ({wl.name}) sampled tokens={n_sample}")
+    announce(f"layer {name} M={M} sampled tokens={n_sample}")
     got = _forward(layer, inp)
     toks = _sample(M, n_sample, seed=M)
     ref = oracle_layer(wl, lw, inp, tokens=toks)

@@ -84,9 +84,9 @@ def _check_invariants(ids, start, n_local, B):
         assert int(np.sum(be == x)) * B == -(-cnt // B) * B
 
 
-@pytest.mark.parametrize("cfg", [0, 2, 3, 4])
-def test_invariants_on_config_routing(cfg):
-    wl = W.CONFIGS[cfg]
+@pytest.mark.parametrize("name", [W.INT4_SMALL, W.NVFP4_DECODE, W.NVFP4_ZIPF, W.MXFP4_SWIGLU])
+def test_invariants_on_workload_routing(name):
+    wl = W.WORKLOADS[name]
     M = min(wl.Ms[-1], 512)
     inp = W.make_inputs(wl, M)
     B = 16

@@ -74,18 +74,23 @@ class Workload:
         return GROUP[self.qtype]
 
 
-CONFIGS = {
-    0: Workload("int4_m123_e8_top2_h512_i1024", "int4_g128", 8, 0, 8, 2, 512, 1024,
-                (123,), seed=0),
-    1: Workload("int4_bias_m2304_e8_top2_h512_i1024", "int4_g128", 8, 0, 8, 2, 512, 1024,
-                (2304,), bias=True, seed=1),
-    2: Workload("nvfp4_ep8_slice_decode_h4096_i4096", "nvfp4_g16", 256, 0, 32, 8, 4096, 4096,
-                (1, 4, 16, 64), norm=True, seed=2),
-    3: Workload("nvfp4_ep8_slice_zipf_prefill_h4096_i4096", "nvfp4_g16", 256, 0, 32, 8, 4096, 4096,
-                (256, 1024, 4096), norm=True, routing="zipf", seed=2),
-    4: Workload("mxfp4_swiglu_e128_top4_h2880_i2880", "mxfp4_g32", 128, 0, 128, 4, 2880, 2880,
-                (1, 32, 2048), bias=True, act="swiglu_alpha", interleaved_w13=True, seed=4),
-}
+# The five workloads, by name: int4 layers of 8 experts (123 tokens; 2304 tokens with biases),
+# one GPU's NVFP4 slice of 32 of 256 experts (uniform decode batches; Zipf-routed prefill
+# batches, same weights) and a 128-expert MXFP4 GPT-OSS-style layer.
+WORKLOADS = {w.name: w for w in [
+    Workload("int4_m123_e8_top2_h512_i1024", "int4_g128", 8, 0, 8, 2, 512, 1024,
+             (123,), seed=0),
+    Workload("int4_bias_m2304_e8_top2_h512_i1024", "int4_g128", 8, 0, 8, 2, 512, 1024,
+             (2304,), bias=True, seed=1),
+    Workload("nvfp4_ep8_slice_decode_h4096_i4096", "nvfp4_g16", 256, 0, 32, 8, 4096, 4096,
+             (1, 4, 16, 64), norm=True, seed=2),
+    Workload("nvfp4_ep8_slice_zipf_prefill_h4096_i4096", "nvfp4_g16", 256, 0, 32, 8, 4096, 4096,
+             (256, 1024, 4096), norm=True, routing="zipf", seed=2),
+    Workload("mxfp4_swiglu_e128_top4_h2880_i2880", "mxfp4_g32", 128, 0, 128, 4, 2880, 2880,
+             (1, 32, 2048), bias=True, act="swiglu_alpha", interleaved_w13=True, seed=4),
+]}
+INT4_SMALL, INT4_BIAS, NVFP4_DECODE, NVFP4_ZIPF, MXFP4_SWIGLU = WORKLOADS
+HEADLINE = INT4_BIAS   # the layer bench.py measures by default
 
 
 def _rng(a: int, b: int, stream: int) -> np.random.Generator:
