@@ -184,40 +184,46 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
   for (int s = 0; s < kStages - 1; ++s)
     if (s < KT) issue(s, s);
 
-  for (int kt0 = 0; kt0 < KT; kt0 += kStages) {
+  // one K step: wait for its operands, prefetch a later step, dequantise and multiply
+  auto step = [&](int kt, int u) {
+    // this wave's loads of step kt have landed once only later steps' loads are pending
+    const int later = min(kStages - 2, KT - 1 - kt);
+    if (xwave) wait_step<XL + LW, kStages>(later); else wait_step<LW, kStages>(later);
+    block_barrier();  // everyone's step kt is in LDS, and everyone is done with step kt-1
+    if (kt + kStages - 1 < KT) issue(kt + kStages - 1, (u + kStages - 1) % kStages);
+    const uint8_t* st = stage_ptr(u);
+    const u32x4_t* xs = reinterpret_cast<const u32x4_t*>(st);
+    u32x2_t wq[NG];
+    TileScale<QT> sc[NG];
 #pragma unroll
-    for (int u = 0; u < kStages; ++u) {
-      const int kt = kt0 + u;
-      if (kt >= KT) break;
-      // this wave's loads of step kt have landed once only later steps' loads are pending
-      const int later = min(kStages - 2, KT - 1 - kt);
-      if (xwave) wait_step<XL + LW, kStages>(later); else wait_step<LW, kStages>(later);
-      block_barrier();  // everyone's step kt is in LDS, and everyone is done with step kt-1
-      if (kt + kStages - 1 < KT) issue(kt + kStages - 1, (u + kStages - 1) % kStages);
-      const uint8_t* st = stage_ptr(u);
-      const u32x4_t* xs = reinterpret_cast<const u32x4_t*>(st);
-      u32x2_t wq[NG];
-      TileScale<QT> sc[NG];
+    for (int g = 0; g < NG; ++g) {
+      wq[g] = reinterpret_cast<const u32x2_t*>(st + XB + (w * NG + g) * kTileBytes)[lane];
+      const uint8_t* sb = st + XB + WB + (w * NG + g) * 64 + (lane & 15) * SROW;
+      sc[g].raw = SROW == 4 ? *reinterpret_cast<const uint32_t*>(sb) : *reinterpret_cast<const uint16_t*>(sb);
+    }
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        wq[g] = reinterpret_cast<const u32x2_t*>(st + XB + (w * NG + g) * kTileBytes)[lane];
-        const uint8_t* sb = st + XB + WB + (w * NG + g) * 64 + (lane & 15) * SROW;
-        sc[g].raw = SROW == 4 ? *reinterpret_cast<const uint32_t*>(sb) : *reinterpret_cast<const uint16_t*>(sb);
-      }
+    for (int i = 0; i < 2; ++i) {
+      u32x4_t af[NG];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        u32x4_t af[NG];
+      for (int g = 0; g < NG; ++g) af[g] = dequant8<QT>(wq[g][i], sc[g].s(i, lane));
 #pragma unroll
-        for (int g = 0; g < NG; ++g) af[g] = dequant8<QT>(wq[g][i], sc[g].s(i, lane));
+      for (int h = 0; h < MG; ++h) {
+        const u32x4_t bf = xs[(i * MG + h) * 64 + lane];
 #pragma unroll
-        for (int h = 0; h < MG; ++h) {
-          const u32x4_t bf = xs[(i * MG + h) * 64 + lane];
-#pragma unroll
-          for (int g = 0; g < NG; ++g) acc[g][h] = mfma(af[g], bf, acc[g][h]);
-        }
+        for (int g = 0; g < NG; ++g) acc[g][h] = mfma(af[g], bf, acc[g][h]);
       }
     }
+  };
+  // whole rounds of kStages steps (stage index = compile-time constant), then the remaining steps;
+  // no early exit inside the unrolled round, which would make the accumulators change registers
+  int kt0 = 0;
+  for (; kt0 + kStages <= KT; kt0 += kStages) {
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) step(kt0 + u, u);
   }
+#pragma unroll
+  for (int u = 0; u < kStages - 1; ++u)
+    if (kt0 + u < KT) step(kt0 + u, u);
 
   // epilogue: lane holds D[n = 4 (lane/16) + q][m = lane % 16] of each (n-tile, m-group)
   float gsv = 1.f;
