@@ -136,7 +136,7 @@ extern "C" int moe_gemm_choose(const moe_weights* W, int64_t numel, int32_t bloc
     c.ng = 2;
     if (block_m >= 128 && ((int64_t)(nt + 15) / 16) * mblocks >= 2 * num_cus) c.ng = 4;
     if (((int64_t)(nt + 7) / 8) * mblocks < 2 * num_cus) c.ng = 1;
-    c.group_m = default_group_m(numel, block_m);
+    c.group_m = default_group_m(W->K);
   }
   *cfg = c;
   return ok();

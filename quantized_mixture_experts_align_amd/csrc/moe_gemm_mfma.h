@@ -88,7 +88,9 @@ __device__ __forceinline__ void grouped_block(int nblk, int gm_max, int& mb, int
 }
 
 template <int QT, bool BIAS, int MG, int NG, int ACT>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
+// (at least two waves per SIMD: the 128-slot, 4-tile variants sit at the 256-register limit,
+// and one register more would halve their occupancy)
+__global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
   static_assert(!act_paired<ACT>() || NG % 2 == 0, "the fused gated epilogue pairs gate and up tiles");
   constexpr int NGA = act_paired<ACT>() ? NG / 2 : NG;     // tiles per wave in the assigned range
   constexpr int BM = 16 * MG;
