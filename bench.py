@@ -39,7 +39,9 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "quantized_mixture_experts_align_amd", "csrc")
 # every source the GEMM kernels are compiled from: a change to any of them voids old counters
 GEMM_SRCS = ["moe_gemm.hip", "moe_gemm_common.h", "moe_gemm_mfma.h", "moe_gemm_decode.h",
-             "moe_gemm_int4.hip", "moe_gemm_nvfp4.hip", "moe_gemm_mxfp4.hip", "moe_internal.h"]
+             "moe_gemm_stream.h", "moe_gemm_int4.hip", "moe_gemm_nvfp4.hip", "moe_gemm_mxfp4.hip",
+             "moe_gemm_stream_int4.hip", "moe_gemm_stream_nvfp4.hip", "moe_gemm_stream_mxfp4.hip",
+             "moe_internal.h"]
 FLUSH_BYTES = 1 << 30          # read between cold steps: more than L2 + MALL
 LAUNCHES = 20                  # back-to-back launches per graph when timing one GEMM
 
