@@ -94,6 +94,9 @@ static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64
     }
   }
   MOE_REQUIRE(c.kernel == MOE_GEMM_MFMA, MOE_EINVAL, "moe_w4a16_gemm: unknown kernel %d", c.kernel);
+  MOE_REQUIRE(a_rows * (int64_t)lda * 2 <= (int64_t)UINT32_MAX, MOE_EUNSUPPORTED,
+              "moe_w4a16_gemm: MFMA kernel addresses A with 32-bit byte offsets; A spans %lld bytes",
+              (long long)(a_rows * (int64_t)lda * 2));
   MOE_REQUIRE(c.ng == 1 || c.ng == 2 || c.ng == 4, MOE_EINVAL, "moe_w4a16_gemm: ng=%d (1, 2 or 4)", c.ng);
   MOE_REQUIRE(c.group_m >= 0 && c.group_m <= 64, MOE_EINVAL, "moe_w4a16_gemm: group_m=%d (0..64)", c.group_m);
   if (c.group_m == 0) c.group_m = moe::default_group_m(W->K);

@@ -51,18 +51,31 @@ __device__ __forceinline__ void wait_step(int later) {
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Direct global -> LDS load of BYTES (4 or 16) per lane: lane l's data lands at lds + l*BYTES.
+// The address is a wave-uniform 64-bit base in scalar registers + the lane's 32-bit byte offset,
+// so a step's address update is scalar work and the per-lane offsets never change.  (No
+// instruction offset: for these loads it would move the LDS destination too.)
 // Written as inline assembly so that the compiler's own wait insertion, which cannot tell which
 // LDS bytes such a load writes, does not add a full vmcnt(0) before every LDS read; the waits
 // for these loads are the explicit wait_vm<> calls.  (m0 holds the LDS address; one wait state
 // is required between writing m0 and the load.)
 template <int BYTES>
-__device__ __forceinline__ void dma_to_lds(const void* g, void* lds) {
+__device__ __forceinline__ void dma_to_lds(const uint8_t* sbase, uint32_t voff, void* lds) {
   const uint32_t off = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(off);
   if constexpr (BYTES == 16)
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(g) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 ::"s"(m0), "v"(voff), "s"(sbase) : "memory", "m0");
   else
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(g) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                 ::"s"(m0), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+
+// A pointer that is the same in every lane, held in scalar registers.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
 }
 
 // Workgroups go to the 8 XCDs round-robin by launch index, and each XCD has its own L2.  The
@@ -129,19 +142,20 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
   // activation fragment f = l*256 + tid -> k-step i, m-group g, MFMA lane fl: row g*16 + fl%16,
   // columns 32 i + 8 (fl/16) + 0..7 of the step; stage slot f (wave-contiguous for the DMA)
   const bool xwave = w < XWAVES;
-  const uint16_t* xsrc[XL];
+  const uint8_t* xbase = uniform_ptr(a.A);
+  uint32_t xoff[XL];  // byte offsets from A (the host checks that A spans less than 4 GiB)
 #pragma unroll
   for (int l = 0; l < XL; ++l) {
     const int f = l * 256 + tid;
     const int fl = f & 63, g = (f >> 6) % MG, i = (f >> 6) / MG;
     const int row = xwave ? s_crow[g * 16 + (fl & 15)] : -1;
-    xsrc[l] = a.A + (int64_t)(row >= 0 ? row / a.top_k : 0) * a.lda + 32 * i + 8 * (fl >> 4);
+    xoff[l] = (uint32_t)(((int64_t)(row >= 0 ? row / a.top_k : 0) * a.lda + 32 * i + 8 * (fl >> 4)) * 2);
   }
   // weights: NG consecutive 16-row tiles of this wave (clamped at the N edge, not stored)
   int ntile[NG];
   bool nok[NG];
-  const uint8_t* wsrc[NG];
-  const uint8_t* ssrc[NG];
+  const uint8_t* wbase[NG];
+  const uint8_t* sbase[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     if (g < NGA) {
@@ -153,26 +167,27 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
       ntile[g] = ntile[g - NGA] + NTA;
     }
     const int64_t tile0 = ((int64_t)e * NT + ntile[g]) * KT;
-    wsrc[g] = a.codes + tile0 * kTileBytes + lane * 4;
-    ssrc[g] = a.scales + (QT == MOE_Q_INT4_G128 ? ((int64_t)e * NT + ntile[g]) * (KT / 2) * 32
-                                                : tile0 * scale_bytes_per_tile(QT)) + lane * 4;
+    wbase[g] = uniform_ptr(a.codes + tile0 * kTileBytes);
+    sbase[g] = uniform_ptr(a.scales + (QT == MOE_Q_INT4_G128 ? ((int64_t)e * NT + ntile[g]) * (KT / 2) * 32
+                                                             : tile0 * scale_bytes_per_tile(QT)));
   }
+  const uint32_t loff = (uint32_t)lane * 4;  // a lane's dword of a 256-B weight or scale row
   auto issue = [&](int kt, int stage) {
     uint8_t* st = stage_ptr(stage);
     if (xwave) {
 #pragma unroll
       for (int l = 0; l < XL; ++l)
-        dma_to_lds<16>(xsrc[l] + kt * kTileK, st + (l * 256 + w * 64) * 16);
+        dma_to_lds<16>(xbase + kt * (kTileK * 2), xoff[l], st + (l * 256 + w * 64) * 16);
     }
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       uint8_t* wt = st + XB + (w * NG + g) * kTileBytes;
-      const uint8_t* src = wsrc[g] + (int64_t)kt * kTileBytes;
-      dma_to_lds<4>(src, wt);
-      dma_to_lds<4>(src + 256, wt + 256);
+      const uint8_t* src = wbase[g] + (int64_t)kt * kTileBytes;
+      dma_to_lds<4>(src, loff, wt);
+      dma_to_lds<4>(src + 256, loff, wt + 256);
       const int64_t soff = QT == MOE_Q_INT4_G128 ? (int64_t)(kt >> 1) * 32 : (int64_t)kt * scale_bytes_per_tile(QT);
       if (lane < SLANES)
-        dma_to_lds<4>(ssrc[g] + soff, st + XB + WB + (w * NG + g) * 64);
+        dma_to_lds<4>(sbase[g] + soff, loff, st + XB + WB + (w * NG + g) * 64);
     }
   };
 
