@@ -181,7 +181,7 @@ def run_cell(name: str, M: int, steps: int, warmup: int, want_cpu: bool, seed=No
     # (the average per launch is the kernel's duration plus the graph's small launch gap)
     import quantized_mixture_experts_align_amd.ops as ops
     calls = {}
-    orig, orig_act = ops.moe_w4a16_gemm, ops.moe_w4a16_gemm_act
+    orig, orig_act, orig_routed = ops.moe_w4a16_gemm, ops.moe_w4a16_gemm_act, ops.moe_w4a16_gemm_act_routed
 
     def record(fn, key):
         def wrapper(*a, **kw):
@@ -189,12 +189,14 @@ def run_cell(name: str, M: int, steps: int, warmup: int, want_cpu: bool, seed=No
             return fn(*a, **kw)
         return wrapper
     # gate/up GEMM (with the activation fused into it) and down GEMM
+    # (small batches: the gate/up GEMM with the align fused into it)
     ops.moe_w4a16_gemm_act = record(orig_act, "gemm13")
+    ops.moe_w4a16_gemm_act_routed = record(orig_routed, "gemm13")
     ops.moe_w4a16_gemm = record(orig, "gemm2")
     try:
         layer(x, ids, gw, ws=ws)
     finally:
-        ops.moe_w4a16_gemm, ops.moe_w4a16_gemm_act = orig, orig_act
+        ops.moe_w4a16_gemm, ops.moe_w4a16_gemm_act, ops.moe_w4a16_gemm_act_routed = orig, orig_act, orig_routed
     torch.cuda.synchronize()
     dur = {}
     for key, (fn, a, kw) in calls.items():
@@ -225,7 +227,7 @@ def run_cell(name: str, M: int, steps: int, warmup: int, want_cpu: bool, seed=No
         ach = bytes_13 / d13 / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4)}
-    roof["kernel"] = ("gemm_mfma_kernel" if layer_uses_mfma(layer, M, P) else "gemm_decode_kernel") + " (gate/up, activation fused)"
+    roof["kernel"] = gemm13_kernel_name(layer, M, calls["gemm13"][0] is orig_routed)
     roof["traffic"] = load_traffic("moe_gemm13", wl.name + f"_m{M}")
     roof["avg_launch_us"] = round(d13 * 1e6, 2)
 
@@ -262,8 +264,14 @@ def layer_fracs(nbytes: float, flops: float, t: float) -> dict:
             "roof_frac": round(max(t_hbm, t_mfma) / t, 4)}
 
 
-def layer_uses_mfma(layer, M, P) -> bool:
-    return layer.configs(M, layer.block_m(M))[0].kernel == 2
+def gemm13_kernel_name(layer, M, routed: bool) -> str:
+    from quantized_mixture_experts_align_amd import _lib as L
+    c = layer.configs(M, layer.block_m(M))[0]
+    if c.kernel == L.GEMM_MFMA:
+        name = "gemm_mfma_kernel"
+    else:
+        name = "gemm_stream_kernel" if c.gemv_rows == 0 else "gemm_decode_kernel"
+    return name + (" (gate/up, align and activation fused)" if routed else " (gate/up, activation fused)")
 
 
 def main() -> int:

@@ -6,14 +6,14 @@ library; the first call does, and fails loudly if it has not been built.
 """
 from . import _lib
 from .ops import (align_capacity, choose_block_m, gemm_choose, gemm_config, moe_act, moe_align,
-                  moe_combine, moe_norm_weight, moe_w4a16_gemm, moe_w4a16_gemm_act, moe_w4a16_prepare,
-                  prepared_size,
+                  moe_combine, moe_norm_weight, moe_w4a16_gemm, moe_w4a16_gemm_act,
+                  moe_w4a16_gemm_act_routed, moe_w4a16_prepare, prepared_size,
                   PreparedWeights)
 from .layer import MoELayer, Workspace
 
 __all__ = [
     "align_capacity", "choose_block_m", "gemm_choose", "gemm_config", "moe_act", "moe_align",
-    "moe_combine", "moe_norm_weight", "moe_w4a16_gemm", "moe_w4a16_gemm_act", "moe_w4a16_prepare",
-    "prepared_size",
+    "moe_combine", "moe_norm_weight", "moe_w4a16_gemm", "moe_w4a16_gemm_act",
+    "moe_w4a16_gemm_act_routed", "moe_w4a16_prepare", "prepared_size",
     "PreparedWeights", "MoELayer", "Workspace",
 ]

@@ -53,6 +53,9 @@ SIGNATURES = {
                                  _I64, _I32, _I32, C.POINTER(MoeGemmConfig), _P]),
     "moe_w4a16_gemm_act": (C.c_int, [C.c_int, _F, _F, _P, _I64, _I32, _P, _I32, C.POINTER(MoeWeights), _P,
                                      _P, _P, _I64, _I32, _I32, C.POINTER(MoeGemmConfig), _P]),
+    "moe_w4a16_gemm_act_routed": (C.c_int, [C.c_int, _F, _F, _P, _I64, _I32, _P, _I32, C.POINTER(MoeWeights),
+                                            _P, _I64, _I32, _I32, _I32, _P, _P, _P, _P,
+                                            C.POINTER(MoeGemmConfig), _P]),
     "moe_act": (C.c_int, [C.c_int, _P, _I32, _P, _I32, _I64, _I32, _P, _F, _F, _P]),
     "moe_combine": (C.c_int, [_P, _P, _P, _P, _F, _F, _I64, _I32, _I32, _P, _P]),
 }

@@ -23,10 +23,14 @@ int device_cu_count() {
 
 static bool al(const void* p, uintptr_t n) { return ((uintptr_t)p & (n - 1)) == 0; }
 
+// Routed mode (topk_ids set): the align of the numel <= kFusedAlignSlots slots is computed inside
+// the streaming kernel, and sorted_token_ids / expert_ids / num_tokens_post_padded / slot_local
+// are its outputs instead of inputs.
 static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64_t a_rows, int32_t lda,
                      uint16_t* C, int32_t ldc, const moe_weights* W, const int32_t* sorted_token_ids,
                      const int32_t* expert_ids, const int32_t* num_tokens_post_padded, int64_t numel,
-                     int32_t top_k, int32_t block_m, const moe_gemm_config* cfg, hipStream_t stream) {
+                     int32_t top_k, int32_t block_m, const moe_gemm_config* cfg, hipStream_t stream,
+                     const int32_t* topk_ids = nullptr, int32_t expert_start = 0, int32_t* slot_local = nullptr) {
   MOE_REQUIRE(W, MOE_EINVAL, "moe_w4a16_gemm: null weights");
   MOE_REQUIRE(W->qtype >= 0 && W->qtype <= 2, MOE_EINVAL, "moe_w4a16_gemm: bad qtype %d", W->qtype);
   MOE_REQUIRE(W->n_experts >= 1 && W->N >= kTileN && W->N % kTileN == 0 && W->K >= kTileK &&
@@ -66,13 +70,21 @@ static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64
     if (rc) return rc;
     if (paired && c.ng < 2) c.ng = 2;  // the fused gated epilogue needs gate/up tile pairs
   }
+  if (topk_ids) {
+    MOE_REQUIRE(c.kernel == MOE_GEMM_DECODE && c.gemv_rows == 0, MOE_EUNSUPPORTED,
+                "moe_w4a16_gemm_act_routed: the fused align runs in the streaming decode kernel "
+                "(kernel DECODE, gemv_rows 0)");
+    MOE_REQUIRE(slot_local, MOE_EINVAL, "moe_w4a16_gemm_act_routed: null slot_local_ids");
+  }
   int64_t cap = 0, cap_blocks = 0;
   int rc = moe_align_capacity(numel, 1, W->n_experts, block_m, &cap, &cap_blocks);
   if (rc) return rc;
   GemmArgs a{A, lda, C, ldc,
              static_cast<const uint8_t*>(W->codes), static_cast<const uint8_t*>(W->scales),
              W->global_scale, W->bias, sorted_token_ids, expert_ids, num_tokens_post_padded,
-             (int32_t)numel, top_k, block_m, W->N, W->K, W->n_experts, alpha, limit, c.group_m};
+             (int32_t)numel, top_k, block_m, W->N, W->K, W->n_experts, alpha, limit, c.group_m,
+             topk_ids, expert_start, (int32_t)cap, (int32_t)cap_blocks, const_cast<int32_t*>(sorted_token_ids),
+             const_cast<int32_t*>(expert_ids), const_cast<int32_t*>(num_tokens_post_padded), slot_local};
   const bool bias = W->bias != nullptr;
   if (c.kernel == MOE_GEMM_DECODE) {
     MOE_REQUIRE(block_m <= 16, MOE_EUNSUPPORTED, "moe_w4a16_gemm: decode kernel needs block_m <= 16");
@@ -121,6 +133,50 @@ extern "C" int moe_w4a16_gemm(const uint16_t* A, int64_t a_rows, int32_t lda, ui
                               const moe_gemm_config* cfg, hipStream_t stream) {
   return gemm_impl(kActNone, 0.f, 0.f, A, a_rows, lda, C, ldc, W, sorted_token_ids, expert_ids,
                    num_tokens_post_padded, numel, top_k, block_m, cfg, stream);
+}
+
+extern "C" int moe_w4a16_gemm_act_routed(moe_act_kind kind, float alpha, float limit, const uint16_t* A,
+                                         int64_t a_rows, int32_t lda, uint16_t* out, int32_t ldo,
+                                         const moe_weights* W13, const int32_t* topk_ids, int64_t M,
+                                         int32_t top_k, int32_t expert_start, int32_t block_m,
+                                         int32_t* sorted_token_ids, int32_t* expert_ids,
+                                         int32_t* num_tokens_post_padded, int32_t* slot_local_ids,
+                                         const moe_gemm_config* cfg, hipStream_t stream) {
+  MOE_REQUIRE(kind == MOE_ACT_SILU_MUL || kind == MOE_ACT_SWIGLU_ALPHA || kind == MOE_ACT_RELU2, MOE_EINVAL,
+              "moe_w4a16_gemm_act_routed: unknown activation %d", (int)kind);
+  MOE_REQUIRE(M >= 0 && top_k >= 1 && top_k <= 64, MOE_EINVAL, "moe_w4a16_gemm_act_routed: M=%lld top_k=%d",
+              (long long)M, top_k);
+  const int64_t numel = M * top_k;
+  MOE_REQUIRE(numel <= kFusedAlignSlots, MOE_EUNSUPPORTED,
+              "moe_w4a16_gemm_act_routed: %lld slots; the fused align takes at most %d (use moe_align)",
+              (long long)numel, kFusedAlignSlots);
+  MOE_REQUIRE(block_m >= 1 && block_m <= 16, MOE_EUNSUPPORTED,
+              "moe_w4a16_gemm_act_routed: block_m=%d outside 1..16", block_m);
+  MOE_REQUIRE(W13, MOE_EINVAL, "moe_w4a16_gemm_act_routed: null weights");
+  MOE_REQUIRE(W13->n_experts >= 1 && W13->n_experts <= 512, MOE_EUNSUPPORTED,
+              "moe_w4a16_gemm_act_routed: n_experts=%d outside 1..512", W13->n_experts);
+  MOE_REQUIRE(expert_start >= 0, MOE_EINVAL, "moe_w4a16_gemm_act_routed: expert_start=%d", expert_start);
+  MOE_REQUIRE(numel == 0 || topk_ids, MOE_EINVAL, "moe_w4a16_gemm_act_routed: null topk_ids");
+  MOE_REQUIRE(sorted_token_ids && expert_ids && num_tokens_post_padded && slot_local_ids, MOE_EINVAL,
+              "moe_w4a16_gemm_act_routed: null align output");
+  if (numel == 0) {  // nothing routed: the align outputs of an empty batch (moe_align writes the same)
+    return moe_align(topk_ids, 0, top_k, expert_start, W13->n_experts, block_m, sorted_token_ids, expert_ids,
+                     num_tokens_post_padded, slot_local_ids, stream);
+  }
+  const int act = kind == MOE_ACT_SILU_MUL ? kActSilu : (kind == MOE_ACT_SWIGLU_ALPHA ? kActSwiglu : kActRelu2);
+  moe_gemm_config c{};
+  if (cfg && cfg->kernel != MOE_GEMM_AUTO) {
+    c = *cfg;
+  } else {
+    int rc = moe_gemm_choose(W13, numel, block_m, device_cu_count(), &c);
+    if (rc) return rc;
+    if (act_paired(act) && c.ng < 2) c.ng = 2;
+    c.kernel = MOE_GEMM_DECODE;
+    c.gemv_rows = 0;
+  }
+  return gemm_impl(act, alpha, limit, A, a_rows, lda, out, ldo, W13, sorted_token_ids, expert_ids,
+                   num_tokens_post_padded, numel, top_k, block_m, &c, stream, topk_ids, expert_start,
+                   slot_local_ids);
 }
 
 extern "C" int moe_w4a16_gemm_act(moe_act_kind kind, float alpha, float limit, const uint16_t* A,

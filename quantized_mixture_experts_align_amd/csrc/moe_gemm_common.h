@@ -33,7 +33,17 @@ struct GemmArgs {
   int32_t numel, top_k, block_m, N, K, E;
   float alpha, limit;  // activation parameters of the fused gate/up epilogue
   int32_t group_m;     // MFMA: align blocks per XCD workgroup group
+  // Fused route-and-align (streaming kernel, at most kFusedAlignSlots slots): with topk_ids set,
+  // every workgroup computes the align itself instead of reading sorted/eids/ntpp, and
+  // workgroup 0 writes the align outputs for the kernels that follow.
+  const int32_t* topk_ids;
+  int32_t expert_start, cap, cap_blocks;
+  int32_t* sorted_out;
+  int32_t* eids_out;
+  int32_t* ntpp_out;
+  int32_t* slot_local_out;
 };
+constexpr int kFusedAlignSlots = 64;  // one slot per lane of one wave
 
 // Fused gate/up epilogue: the GEMM's output tiles come in (gate, up) pairs held by the same lane;
 // both are rounded to bf16 as the stored GEMM output would be, then the activation is applied

@@ -32,7 +32,60 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int QT, bool BIAS, int NG, int KS, int ACT>
+// Route-and-align of at most kFusedAlignSlots slots, computed by wave 0 with one slot per lane
+// (the same result as moe_align: local expert = id - start inside [start, start + E), else the
+// slot is dropped; slots grouped by ascending expert, ascending slot order inside an expert,
+// each expert's run padded to whole blocks of B rows with the sentinel numel).
+//   f_rows[b * 16 + r] = slot of row r of block b (numel for padding), f_be[b] = its expert,
+//   returns the block count.  Workgroup 0 also writes sorted_out[cap], eids_out[cap_blocks]
+//   (-1 past the last block), *ntpp_out and slot_local_out[numel].  Every thread calls it.
+__device__ int fused_align(const GemmArgs& a, int* f_rows, int* f_be, int* f_nblk) {
+  const int tid = (int)threadIdx.x, lane = tid & 63, B = a.block_m, numel = a.numel;
+  for (int p = tid; p < kFusedAlignSlots * 16; p += (int)blockDim.x) f_rows[p] = numel;
+  __syncthreads();
+  if (tid < 64) {
+    const int id = lane < numel ? a.topk_ids[lane] : -1;
+    const bool live = lane < numel && id >= a.expert_start && id - a.expert_start < a.E;
+    const int le = live ? id - a.expert_start : -1;
+    // lanes routed to the same expert: ballots over the bits of the expert id
+    uint64_t same = __ballot(live);
+    for (int b = 0; (1 << b) < a.E; ++b) {
+      const bool bit = live && ((le >> b) & 1);
+      const uint64_t m = __ballot(bit);
+      same &= bit ? m : ~m;
+    }
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const int r = __popcll(same & below);               // rank among the expert's slots
+    const int nbe = (__popcll(same) + B - 1) / B;       // blocks of the expert
+    const bool first = live && r == 0;
+    // blocks of the experts before this one: a walk over the first slot of every live expert
+    uint64_t fm = __ballot(first);
+    int bs = 0, tot = 0;
+    while (fm) {
+      const int j = __builtin_ctzll(fm);
+      fm &= fm - 1;
+      const int lej = __shfl(le, j), nj = __shfl(nbe, j);
+      if (lej < le) bs += nj;
+      tot += nj;
+    }
+    if (live) f_rows[(bs + r / B) * 16 + r % B] = lane;
+    if (first)
+      for (int t = 0; t < nbe; ++t) f_be[bs + t] = le;
+    if (lane == 0) *f_nblk = tot;
+    if (blockIdx.x == 0 && lane < numel) a.slot_local_out[lane] = le;
+  }
+  __syncthreads();
+  const int nb = *f_nblk;
+  if (blockIdx.x == 0) {
+    const int total = nb * B;
+    for (int p = tid; p < a.cap; p += (int)blockDim.x) a.sorted_out[p] = p < total ? f_rows[(p / B) * 16 + p % B] : numel;
+    for (int b = tid; b < a.cap_blocks; b += (int)blockDim.x) a.eids_out[b] = b < nb ? f_be[b] : -1;
+    if (tid == 0) *a.ntpp_out = total;
+  }
+  return nb;
+}
+
+template <int QT, bool BIAS, int NG, int KS, int ACT, bool FA>
 __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   static_assert(!act_paired<ACT>() || NG % 2 == 0, "the fused gated epilogue pairs gate and up tiles");
   constexpr int NGA = act_paired<ACT>() ? NG / 2 : NG;
@@ -49,7 +102,11 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   const int NTA = act_paired<ACT>() ? NT / 2 : NT;  // tiles to assign (gate tiles if fused)
   const int NS = (NTA + NGA - 1) / NGA;           // strips per block
   const int B = a.block_m;
-  const int items = (*a.ntpp / B) * NS;
+  __shared__ int f_rows[FA ? kFusedAlignSlots * 16 : 1];
+  __shared__ int f_be[FA ? kFusedAlignSlots : 1];
+  __shared__ int f_nblk;
+  const int nblocks = FA ? fused_align(a, f_rows, f_be, &f_nblk) : *a.ntpp / B;
+  const int items = nblocks * NS;
   const int per = (items + (int)gridDim.x - 1) / (int)gridDim.x;  // <= kWin by the launch
   const int i0 = (int)blockIdx.x * per, i1 = min(items, i0 + per);
   if (i0 >= i1) return;
@@ -68,12 +125,12 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
       const int q = t >> 4, mm = t & 15, b = (wb + q) / NS;
       int s = -1;
       if (mm < B) {
-        s = a.sorted[(int64_t)b * B + mm];
+        s = FA ? f_rows[b * 16 + mm] : a.sorted[(int64_t)b * B + mm];
         if (s < 0 || s >= a.numel) s = -1;
       }
       t_row[q][mm] = s;
       if (mm == 0) {
-        const int e = a.eids[b];
+        const int e = FA ? f_be[b] : a.eids[b];
         const bool ok = e >= 0 && e < a.E;
         t_e[q] = ok ? e : -1;
         t_gs[q] = (QT == MOE_Q_NVFP4_G16 && ok) ? a.gs[e] : 1.0f;
@@ -82,7 +139,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
     if constexpr (BIAS) {
       for (int t = tid; t < wn * NG * 16; t += 64 * KS) {
         const int q = t / (NG * 16), g = (t >> 4) % NG, r = t & 15;
-        const int it = wb + q, b = it / NS, e = a.eids[b];
+        const int it = wb + q, b = it / NS, e = FA ? f_be[b] : a.eids[b];
         t_bias[q][g][r] = (e >= 0 && e < a.E) ? a.bias[(int64_t)e * a.N + tile_of(it - b * NS, g) * kTileN + r] : 0;
       }
     }
@@ -202,27 +259,39 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   }
 }
 
-template <int QT, bool BIAS, int NG, int ACT>
+template <int QT, bool BIAS, int NG, int ACT, bool FA>
 static int launch_stream_ng(const GemmArgs& a, int ks, int grid, hipStream_t st) {
   switch (ks) {
-    case 1: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 1, ACT>), dim3(grid), dim3(64), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 2, ACT>), dim3(grid), dim3(128), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 4, ACT>), dim3(grid), dim3(256), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 8, ACT>), dim3(grid), dim3(512), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 1, ACT, FA>), dim3(grid), dim3(64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 2, ACT, FA>), dim3(grid), dim3(128), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 4, ACT, FA>), dim3(grid), dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 8, ACT, FA>), dim3(grid), dim3(512), 0, st, a); break;
     default: return fail(MOE_EINVAL, "moe_w4a16_gemm: ksplit=%d (1, 2, 4 or 8)", ks);
   }
   return check_launch("moe_w4a16_gemm (decode stream)");
 }
 
-template <int QT, bool BIAS, int ACT>
+template <int QT, bool BIAS, int ACT, bool FA>
 static int launch_stream_b(const GemmArgs& a, const moe_gemm_config& c, int grid, hipStream_t st) {
   if constexpr (!act_paired<ACT>()) {
-    if (c.ng == 1) return launch_stream_ng<QT, BIAS, 1, ACT>(a, c.ksplit, grid, st);
+    if (c.ng == 1) return launch_stream_ng<QT, BIAS, 1, ACT, FA>(a, c.ksplit, grid, st);
   }
   switch (c.ng) {
-    case 2: return launch_stream_ng<QT, BIAS, 2, ACT>(a, c.ksplit, grid, st);
-    case 4: return launch_stream_ng<QT, BIAS, 4, ACT>(a, c.ksplit, grid, st);
+    case 2: return launch_stream_ng<QT, BIAS, 2, ACT, FA>(a, c.ksplit, grid, st);
+    case 4: return launch_stream_ng<QT, BIAS, 4, ACT, FA>(a, c.ksplit, grid, st);
     default: return fail(MOE_EINVAL, "moe_w4a16_gemm: decode ng=%d (1, 2 or 4; 2 or 4 with a fused gated activation)", c.ng);
+  }
+}
+
+// the fused align exists for the gate/up GEMM with its activation (the first GEMM of the layer)
+template <int QT, bool BIAS, int ACT>
+static int launch_stream_fa(const GemmArgs& a, const moe_gemm_config& c, int grid, hipStream_t st) {
+  if constexpr (ACT == kActNone) {
+    return a.topk_ids ? fail(MOE_EUNSUPPORTED, "moe_w4a16_gemm: the fused align needs a fused activation")
+                      : launch_stream_b<QT, BIAS, ACT, false>(a, c, grid, st);
+  } else {
+    return a.topk_ids ? launch_stream_b<QT, BIAS, ACT, true>(a, c, grid, st)
+                      : launch_stream_b<QT, BIAS, ACT, false>(a, c, grid, st);
   }
 }
 
@@ -243,13 +312,13 @@ int launch_gemm_stream(bool bias, int act, const GemmArgs& a, const moe_gemm_con
   const int grid = (int)grid64;
   switch (act) {
     case kActNone:
-      return bias ? launch_stream_b<QT, true, kActNone>(a, cc, grid, st) : launch_stream_b<QT, false, kActNone>(a, cc, grid, st);
+      return bias ? launch_stream_fa<QT, true, kActNone>(a, cc, grid, st) : launch_stream_fa<QT, false, kActNone>(a, cc, grid, st);
     case kActSilu:
-      return bias ? launch_stream_b<QT, true, kActSilu>(a, cc, grid, st) : launch_stream_b<QT, false, kActSilu>(a, cc, grid, st);
+      return bias ? launch_stream_fa<QT, true, kActSilu>(a, cc, grid, st) : launch_stream_fa<QT, false, kActSilu>(a, cc, grid, st);
     case kActRelu2:
-      return bias ? launch_stream_b<QT, true, kActRelu2>(a, cc, grid, st) : launch_stream_b<QT, false, kActRelu2>(a, cc, grid, st);
+      return bias ? launch_stream_fa<QT, true, kActRelu2>(a, cc, grid, st) : launch_stream_fa<QT, false, kActRelu2>(a, cc, grid, st);
     default:
-      return bias ? launch_stream_b<QT, true, kActSwiglu>(a, cc, grid, st) : launch_stream_b<QT, false, kActSwiglu>(a, cc, grid, st);
+      return bias ? launch_stream_fa<QT, true, kActSwiglu>(a, cc, grid, st) : launch_stream_fa<QT, false, kActSwiglu>(a, cc, grid, st);
   }
 }
 

@@ -102,10 +102,12 @@ class MoELayer:
 
     def forward(self, x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
                 ws: Optional[Workspace] = None, cfg13=None, cfg2=None,
-                fused_act: bool = True) -> torch.Tensor:
+                fused_act: bool = True, fused_align: Optional[bool] = None) -> torch.Tensor:
         """align -> gate/up GEMM -> activation -> down GEMM -> combine.  With fused_act the
         activation runs in the GEMM1 epilogue (bitwise the same result, one launch and one
-        [numel, N13] round trip less); for a gated activation cfg13 then needs ng 2 or 4."""
+        [numel, N13] round trip less); for a gated activation cfg13 then needs ng 2 or 4.
+        With fused_align (default: whenever it applies -- at most 64 slots, the streaming decode
+        kernel, fused_act) the align runs inside that same launch as well (bitwise the same)."""
         M = x.shape[0]
         if ws is None:
             ws = self.workspace(M, device=x.device)
@@ -117,18 +119,31 @@ class MoELayer:
             c13, c2 = ws.cfgs if ws.cfgs is not None else self.configs(M, B)
             cfg13 = cfg13 or c13
             cfg2 = cfg2 or c2
-        sorted_ids, eids, ntpp, loc = ops.moe_align(
-            topk_ids, self.expert_start, self.n_local, B,
-            out=(ws.sorted_ids, ws.expert_ids, ws.ntpp, ws.slot_local))
-        if fused_act:
-            if self.gated and cfg13.ng < 2:
-                cfg13 = ops.gemm_config(cfg13.kernel, 2, cfg13.ksplit, cfg13.gemv_rows, cfg13.group_m)
-            ops.moe_w4a16_gemm_act(self.act, x, self.W13, sorted_ids, eids, ntpp, numel, self.top_k, B,
-                                   self.alpha, self.limit, out=ws.a, cfg=cfg13)
+        routable = (numel <= ops.FUSED_ALIGN_SLOTS and B <= 16 and cfg13.kernel == L.GEMM_DECODE
+                    and cfg13.gemv_rows == 0)
+        if fused_align is None:
+            fused_align = fused_act and routable
+        if fused_align and not (fused_act and routable):
+            raise ValueError("fused_align needs fused_act, at most 64 slots, block_m <= 16 and the "
+                             "streaming decode kernel")
+        align_out = (ws.sorted_ids, ws.expert_ids, ws.ntpp, ws.slot_local)
+        if fused_act and self.gated and cfg13.ng < 2:
+            cfg13 = ops.gemm_config(cfg13.kernel, 2, cfg13.ksplit, cfg13.gemv_rows, cfg13.group_m)
+        if fused_align:
+            _, (sorted_ids, eids, ntpp, loc) = ops.moe_w4a16_gemm_act_routed(
+                self.act, x, self.W13, topk_ids, self.expert_start, B, self.alpha, self.limit,
+                out=ws.a, align_out=align_out, cfg=cfg13)
         else:
-            h = ws.buf13[: numel * self.W13.N].view(numel, self.W13.N)
-            ops.moe_w4a16_gemm(x, self.W13, sorted_ids, eids, ntpp, numel, self.top_k, B, out=h, cfg=cfg13)
-            ops.moe_act(self.act, h, self.I, loc.view(-1), self.alpha, self.limit, out=ws.a)
+            sorted_ids, eids, ntpp, loc = ops.moe_align(topk_ids, self.expert_start, self.n_local, B,
+                                                        out=align_out)
+            if fused_act:
+                ops.moe_w4a16_gemm_act(self.act, x, self.W13, sorted_ids, eids, ntpp, numel, self.top_k,
+                                       B, self.alpha, self.limit, out=ws.a, cfg=cfg13)
+            else:
+                h = ws.buf13[: numel * self.W13.N].view(numel, self.W13.N)
+                ops.moe_w4a16_gemm(x, self.W13, sorted_ids, eids, ntpp, numel, self.top_k, B, out=h,
+                                   cfg=cfg13)
+                ops.moe_act(self.act, h, self.I, loc.view(-1), self.alpha, self.limit, out=ws.a)
         y = ws.buf13[: numel * self.H].view(numel, self.H)
         ops.moe_w4a16_gemm(ws.a, self.W2, sorted_ids, eids, ntpp, numel, 1, B, out=y, cfg=cfg2)
         return ops.moe_combine(y, topk_weights, loc, self.norm_w, self.eps, out=ws.out,

@@ -176,6 +176,40 @@ def moe_w4a16_gemm_act(kind: str, A: torch.Tensor, W13: PreparedWeights, sorted_
     return out
 
 
+FUSED_ALIGN_SLOTS = 64  # most slots (M * top_k) of moe_w4a16_gemm_act_routed
+
+
+def moe_w4a16_gemm_act_routed(kind: str, A: torch.Tensor, W13: PreparedWeights, topk_ids: torch.Tensor,
+                              expert_start: int, block_m: int, alpha: float = 1.702,
+                              limit: float = float("inf"), out: Optional[torch.Tensor] = None,
+                              align_out=None, cfg: Optional[L.MoeGemmConfig] = None):
+    """moe_align + moe_w4a16_gemm_act in one launch for at most 64 slots (block_m <= 16).
+    -> (out, (sorted_token_ids, expert_ids, num_tokens_post_padded, slot_local_ids))."""
+    _need(A, torch.bfloat16, "A")
+    _need(topk_ids, torch.int32, "topk_ids")
+    M, k = topk_ids.shape
+    n_local = W13.desc.n_experts
+    dev = topk_ids.device
+    if align_out is None:
+        s_len, b_len = align_capacity(M, k, n_local, block_m)
+        align_out = (torch.empty(s_len, dtype=torch.int32, device=dev),
+                     torch.empty(b_len, dtype=torch.int32, device=dev),
+                     torch.empty(1, dtype=torch.int32, device=dev),
+                     torch.empty((M, k), dtype=torch.int32, device=dev))
+    sorted_ids, eids, ntpp, loc = align_out
+    if out is None:
+        I = W13.N if kind == "relu2" else W13.N // 2
+        out = torch.empty((M * k, I), dtype=torch.bfloat16, device=A.device)
+    _need(out, torch.bfloat16, "out")
+    L.check(L.lib().moe_w4a16_gemm_act_routed(L.ACT[kind], alpha, limit, _ptr(A), A.shape[0], A.stride(0),
+                                              _ptr(out), out.stride(0), C.byref(W13.desc), _ptr(topk_ids),
+                                              M, k, expert_start, block_m, _ptr(sorted_ids), _ptr(eids),
+                                              _ptr(ntpp), _ptr(loc), None if cfg is None else C.byref(cfg),
+                                              _stream()),
+            "moe_w4a16_gemm_act_routed")
+    return out, align_out
+
+
 def moe_act(kind: str, h: torch.Tensor, I: int, slot_local_ids: Optional[torch.Tensor] = None,
             alpha: float = 1.702, limit: float = float("inf"),
             out: Optional[torch.Tensor] = None) -> torch.Tensor:
