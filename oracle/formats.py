@@ -32,6 +32,11 @@ def decode_uint4b8(nibbles: np.ndarray) -> np.ndarray:
     return np.asarray(nibbles, dtype=np.float64) - 8.0
 
 
+def decode_uint4(nibbles: np.ndarray) -> np.ndarray:
+    """Plain unsigned 4-bit value 0..15 (the asymmetric int4 format, whose zero point is separate)."""
+    return np.asarray(nibbles, dtype=np.float64)
+
+
 def decode_e4m3fn(codes: np.ndarray) -> np.ndarray:
     """float8 e4m3fn: bias 7, subnormals at exponent 0, S.1111.111 is NaN, no inf."""
     c = np.asarray(codes, dtype=np.int64)

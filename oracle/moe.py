@@ -23,7 +23,12 @@ design notes of the repository):
 * ``relu2`` is the non-gated activation of that loop: GEMM1 has I rows (no
   gate/up halves) and ``a = relu(h)^2``;
 * ``routed_scaling_factor`` (passed as 1.0 in that test, not defined on the
-  pages) multiplies the combined output of each token.
+  pages) multiplies the combined output of each token;
+* asymmetric int4 (the ``w1_zeros`` / ``w2_zeros`` and ``is_zp_float`` arguments of
+  the Marlin MoE call in sglang PR 31552, used with integer zero points): unsigned
+  codes, one integer zero point 0..15 and one bf16 scale per group of 128 along K,
+  stored one zero point per byte in ``[N, K/128]`` like the scales; the weight is
+  ``(u - z) * s``.
 """
 from __future__ import annotations
 
@@ -32,10 +37,10 @@ from typing import Optional
 
 import numpy as np
 
-from .formats import (decode_bf16, decode_e2m1, decode_e4m3fn, decode_e8m0, decode_uint4b8,
-                      round_to_bf16)
+from .formats import (decode_bf16, decode_e2m1, decode_e4m3fn, decode_e8m0, decode_uint4,
+                      decode_uint4b8, round_to_bf16)
 
-_GROUP = {"int4_g128": 128, "nvfp4_g16": 16, "mxfp4_g32": 32}
+_GROUP = {"int4_g128": 128, "nvfp4_g16": 16, "mxfp4_g32": 32, "int4zp_g128": 128}
 
 
 # ----------------------------------------------------------------------------- routing
@@ -101,10 +106,13 @@ def _nibbles(codes: np.ndarray) -> np.ndarray:
     return out
 
 
-def dequant(qtype: str, codes: np.ndarray, scales: np.ndarray, gs: Optional[float] = None) -> np.ndarray:
+def dequant(qtype: str, codes: np.ndarray, scales: np.ndarray, gs: Optional[float] = None,
+            zeros: Optional[np.ndarray] = None) -> np.ndarray:
     """Dense float64 [N, K] weight of one expert.
 
     * int4_g128: ``(u - 8) * s[n, k // 128]`` with bf16 ``s`` (uint4b8, group 128).
+    * int4zp_g128: ``(u - z[n, k // 128]) * s[n, k // 128]``, unsigned ``u``, integer
+      zero point ``z`` in 0..15, bf16 ``s`` (asymmetric int4, group 128).
     * nvfp4_g16: ``e2m1 * e4m3[n, k // 16] * gs`` (one fp32 global scale per
       expert and projection, as the experiment's ``_marlin_layer`` passes it).
     * mxfp4_g32: ``e2m1 * 2^(E[n, k // 32] - 127)``.
@@ -115,6 +123,11 @@ def dequant(qtype: str, codes: np.ndarray, scales: np.ndarray, gs: Optional[floa
     if qtype == "int4_g128":
         s = decode_bf16(scales)
         return decode_uint4b8(q) * np.repeat(s, g, axis=-1)
+    if qtype == "int4zp_g128":
+        if zeros is None:
+            raise ValueError("asymmetric int4 needs the zero points")
+        z = np.asarray(zeros, dtype=np.float64)
+        return (decode_uint4(q) - np.repeat(z, g, axis=-1)) * np.repeat(decode_bf16(scales), g, axis=-1)
     if qtype == "nvfp4_g16":
         if gs is None:
             raise ValueError("NVFP4 needs the per-expert global scale")
@@ -238,6 +251,11 @@ def combine(Y: np.ndarray, topk_weights: np.ndarray, slot_local: np.ndarray,
 
 
 # ----------------------------------------------------------------------------- layer
+def _zeros_of(w, e):
+    z = getattr(w, "zeros", None)
+    return None if z is None else z[e]
+
+
 def moe_layer(qtype: str, x_bits: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarray,
               w13, w2, *, expert_start: int, n_local: int, act: str = "silu_mul",
               alpha: float = 1.702, limit: float = math.inf, norm_w_bits=None,
@@ -245,8 +263,9 @@ def moe_layer(qtype: str, x_bits: np.ndarray, topk_ids: np.ndarray, topk_weights
               bf16_intermediates: bool = True, tokens=None, return_intermediates: bool = False):
     """The whole expert layer for one GPU's expert slice.
 
-    ``w13`` / ``w2`` carry ``codes``, ``scales``, ``gs`` (or None) and ``bias``
-    (or None) for the ``n_local`` local experts in the canonical layouts.
+    ``w13`` / ``w2`` carry ``codes``, ``scales``, ``gs`` (or None), ``bias``
+    (or None) and, for asymmetric int4, ``zeros`` for the ``n_local`` local experts in
+    the canonical layouts.
     ``tokens`` restricts the evaluation to a subset of tokens (each token's
     output depends only on its own slots), returning rows in that order.
     """
@@ -264,8 +283,9 @@ def moe_layer(qtype: str, x_bits: np.ndarray, topk_ids: np.ndarray, topk_weights
         rows = np.nonzero(flat == e)[0]             # ascending (token, slot) order
         if rows.size == 0:
             continue
-        W13 = dequant(qtype, w13.codes[e], w13.scales[e], None if w13.gs is None else w13.gs[e])
-        W2 = dequant(qtype, w2.codes[e], w2.scales[e], None if w2.gs is None else w2.gs[e])
+        W13 = dequant(qtype, w13.codes[e], w13.scales[e], None if w13.gs is None else w13.gs[e],
+                      _zeros_of(w13, e))
+        W2 = dequant(qtype, w2.codes[e], w2.scales[e], None if w2.gs is None else w2.gs[e], _zeros_of(w2, e))
         b13 = None if w13.bias is None else decode_bf16(w13.bias[e])
         b2 = None if w2.bias is None else decode_bf16(w2.bias[e])
         r = expert_forward(x[tok[rows // k]], W13, b13, W2, b2, act, alpha, limit,

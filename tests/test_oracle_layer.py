@@ -43,7 +43,7 @@ def _const_proj(n_rows_codes, K, scale_code, dtype_scale, group, gs=None, bias=N
 
 
 # ----------------------------------------------------------------------------- dequant
-def _brute_dequant_matvec(qtype, codes, scales, gs, x):
+def _brute_dequant_matvec(qtype, codes, scales, gs, x, zeros=None):
     """Per-element reading of the packed layout, independent of the oracle's
     vectorised unpack: byte k//2 of row n, low nibble for even k."""
     N, Kh = codes.shape
@@ -58,6 +58,9 @@ def _brute_dequant_matvec(qtype, codes, scales, gs, x):
             if qtype == "int4_g128":
                 s = struct.unpack("<f", struct.pack("<I", int(scales[n, k // 128]) << 16))[0]
                 w = (u - 8) * s
+            elif qtype == "int4zp_g128":
+                s = struct.unpack("<f", struct.pack("<I", int(scales[n, k // 128]) << 16))[0]
+                w = (u - int(zeros[n, k // 128])) * s
             else:
                 sign = -1.0 if u & 8 else 1.0
                 e, m = (u >> 1) & 3, u & 1
@@ -71,14 +74,18 @@ def _brute_dequant_matvec(qtype, codes, scales, gs, x):
     return np.array(out)
 
 
-@pytest.mark.parametrize("qtype,N,K", [("int4_g128", 3, 256), ("nvfp4_g16", 5, 48), ("mxfp4_g32", 4, 96)])
+@pytest.mark.parametrize("qtype,N,K", [("int4_g128", 3, 256), ("nvfp4_g16", 5, 48), ("mxfp4_g32", 4, 96),
+                                        ("int4zp_g128", 3, 384)])
 def test_dequant_matches_per_element_brute_force(qtype, N, K):
     rng = np.random.default_rng(7)
     codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
     g = W.GROUP[qtype]
-    if qtype == "int4_g128":
+    zeros = None
+    if qtype in ("int4_g128", "int4zp_g128"):
         scales = W._to_bf16_bits(rng.uniform(0.002, 0.02, (N, K // g)).astype(np.float32))
         gs = None
+        if qtype == "int4zp_g128":
+            zeros = rng.integers(0, 16, size=(N, K // g), dtype=np.uint8)
     elif qtype == "nvfp4_g16":
         scales = rng.integers(0x20, 0x70, size=(N, K // g), dtype=np.uint8)
         gs = np.float32(3.1e-3)
@@ -86,8 +93,8 @@ def test_dequant_matches_per_element_brute_force(qtype, N, K):
         scales = rng.integers(118, 130, size=(N, K // g), dtype=np.uint8)
         gs = None
     x = rng.standard_normal(K)
-    got = O.dequant(qtype, codes, scales, gs) @ x
-    ref = _brute_dequant_matvec(qtype, codes, scales, gs, x)
+    got = O.dequant(qtype, codes, scales, gs, zeros) @ x
+    ref = _brute_dequant_matvec(qtype, codes, scales, gs, x, zeros)
     assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
 
 
@@ -103,6 +110,28 @@ def test_dequant_constant_closed_forms():
     # nibble order: low nibble is the even K index
     d = O.dequant("mxfp4_g32", np.full((1, 16), 0x72, np.uint8), np.full((1, 1), 127, np.uint8))
     assert d[0, 0] == 1.0 and d[0, 1] == 6.0
+
+
+def test_dequant_asymmetric_int4_closed_forms():
+    # unsigned nibble 13 with zero point 5 -> 8; zero point 13 -> 0; the second group of a row
+    # takes its own zero point; nibble 2 (odd k of byte 0x2D) below zero point 5 -> -3
+    s = np.full((2, 2), _bf16(2.0 ** -7), np.uint16)
+    z = np.array([[5, 13], [13, 5]], np.uint8)
+    d = O.dequant("int4zp_g128", np.full((2, 128), 0xDD, np.uint8), s, None, z)
+    assert np.all(d[0, :128] == 8 * 2.0 ** -7) and np.all(d[0, 128:] == 0.0)
+    assert np.all(d[1, :128] == 0.0) and np.all(d[1, 128:] == 8 * 2.0 ** -7)
+    d = O.dequant("int4zp_g128", np.full((1, 64), 0x2D, np.uint8), s[:1, :1], None, np.full((1, 1), 5, np.uint8))
+    assert d[0, 0] == 8 * 2.0 ** -7 and d[0, 1] == -3 * 2.0 ** -7
+
+
+def test_dequant_asymmetric_int4_with_zero_point_8_is_uint4b8():
+    # uint4b8 is the asymmetric format with every zero point at 8
+    rng = np.random.default_rng(8)
+    codes = rng.integers(0, 256, size=(4, 128), dtype=np.uint8)
+    s = W._to_bf16_bits(rng.uniform(0.002, 0.02, (4, 2)).astype(np.float32))
+    a = O.dequant("int4zp_g128", codes, s, None, np.full((4, 2), 8, np.uint8))
+    b = O.dequant("int4_g128", codes, s)
+    assert np.array_equal(a, b)
 
 
 # ----------------------------------------------------------------------------- activations

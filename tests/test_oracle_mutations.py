@@ -69,7 +69,17 @@ MUTATIONS = {
     "square without the relu": ("act_relu2", lambda: (lambda h: np.square(h))),
     "segments reversed": ("moe_align", lambda: _align_reversed_segments),
     "off-slice kept": ("route_local", lambda: (lambda ids, start, n: (np.asarray(ids) % n).astype(np.int32))),
-    "global scale missing": ("dequant", lambda: (lambda q, c, s, gs=None: ORIG_DQ(q, c, s, None if gs is None else 1.0))),
+    "global scale missing": ("dequant", lambda: (lambda q, c, s, gs=None, zeros=None:
+                                                 ORIG_DQ(q, c, s, None if gs is None else 1.0, zeros))),
+    "zero point ignored": ("dequant", lambda: (lambda q, c, s, gs=None, zeros=None:
+                                               ORIG_DQ("int4_g128", c, s) if q == "int4zp_g128"
+                                               else ORIG_DQ(q, c, s, gs, zeros))),
+    "zero point sign flipped": ("dequant", lambda: (lambda q, c, s, gs=None, zeros=None:
+                                             ORIG_DQ(q, c, s, gs, None if zeros is None else (16 - zeros.astype(np.int64)) % 16)
+                                             if q == "int4zp_g128" else ORIG_DQ(q, c, s, gs, zeros))),
+    "zero point of the wrong group": ("dequant", lambda: (lambda q, c, s, gs=None, zeros=None:
+                                                          ORIG_DQ(q, c, s, gs, None if zeros is None else zeros[..., ::-1])
+                                                          if q == "int4zp_g128" else ORIG_DQ(q, c, s, gs, zeros))),
 }
 ORIG_EF, ORIG_COMBINE, ORIG_NIB, ORIG_SW, ORIG_DQ = (O.expert_forward, O.combine, O._nibbles,
                                                       O.act_swiglu_alpha, O.dequant)
@@ -77,6 +87,9 @@ ORIG_EF, ORIG_COMBINE, ORIG_NIB, ORIG_SW, ORIG_DQ = (O.expert_forward, O.combine
 PINS = [
     (TL.test_dequant_constant_closed_forms, {}),
     (TL.test_dequant_matches_per_element_brute_force, dict(qtype="nvfp4_g16", N=5, K=48)),
+    (TL.test_dequant_matches_per_element_brute_force, dict(qtype="int4zp_g128", N=3, K=384)),
+    (TL.test_dequant_asymmetric_int4_closed_forms, {}),
+    (TL.test_dequant_asymmetric_int4_with_zero_point_8_is_uint4b8, {}),
     (TL.test_silu_mul_hand_values, {}),
     (TL.test_swiglu_alpha_hand_values, {}),
     (TL.test_relu2_hand_values, {}),

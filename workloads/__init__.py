@@ -13,6 +13,8 @@ Canonical layouts (shared vocabulary of every caller):
   float8 e4m3fn codes (uint8) for NVFP4 (g = 16), E8M0 codes (uint8) for
   MXFP4 (g = 32).
 * ``gs``      float32 ``[E]``: NVFP4 per-expert global scale (else ``None``).
+* ``zeros``   uint8 ``[E, N, K/128]``: zero points 0..15 of the asymmetric int4
+  format (``int4zp_g128``: unsigned codes, bf16 scales like int4), else ``None``.
 * ``bias``    bf16 bits ``[E, N]`` or ``None``.
 * ``x``       bf16 bits ``[M, H]``; ``topk_ids`` int32 ``[M, k]`` global ids;
   ``topk_weights`` float32 ``[M, k]``; ``norm_w`` bf16 bits ``[H]``.
@@ -35,8 +37,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-QTYPES = ("int4_g128", "nvfp4_g16", "mxfp4_g32")
-GROUP = {"int4_g128": 128, "nvfp4_g16": 16, "mxfp4_g32": 32}
+QTYPES = ("int4_g128", "nvfp4_g16", "mxfp4_g32", "int4zp_g128")
+GROUP = {"int4_g128": 128, "nvfp4_g16": 16, "mxfp4_g32": 32, "int4zp_g128": 128}
 
 # stream ids of the seed sequence
 _S_WEIGHTS, _S_HIDDEN, _S_ROUTING, _S_AUX = 0, 1, 2, 3
@@ -74,9 +76,10 @@ class Workload:
         return GROUP[self.qtype]
 
 
-# The five workloads, by name: int4 layers of 8 experts (123 tokens; 2304 tokens with biases),
+# The workloads, by name: int4 layers of 8 experts (123 tokens; 2304 tokens with biases),
 # one GPU's NVFP4 slice of 32 of 256 experts (uniform decode batches; Zipf-routed prefill
-# batches, same weights) and a 128-expert MXFP4 GPT-OSS-style layer.
+# batches, same weights), a 128-expert MXFP4 GPT-OSS-style layer, and the int4 layer's shapes
+# with asymmetric int4 (zero points) weights.
 WORKLOADS = {w.name: w for w in [
     Workload("int4_m123_e8_top2_h512_i1024", "int4_g128", 8, 0, 8, 2, 512, 1024,
              (123,), seed=0),
@@ -88,8 +91,10 @@ WORKLOADS = {w.name: w for w in [
              (256, 1024, 4096), norm=True, routing="zipf", seed=2),
     Workload("mxfp4_swiglu_e128_top4_h2880_i2880", "mxfp4_g32", 128, 0, 128, 4, 2880, 2880,
              (1, 32, 2048), bias=True, act="swiglu_alpha", interleaved_w13=True, seed=4),
+    Workload("int4zp_e8_top2_h512_i1024", "int4zp_g128", 8, 0, 8, 2, 512, 1024,
+             (1, 2304), seed=5),
 ]}
-INT4_SMALL, INT4_BIAS, NVFP4_DECODE, NVFP4_ZIPF, MXFP4_SWIGLU = WORKLOADS
+INT4_SMALL, INT4_BIAS, NVFP4_DECODE, NVFP4_ZIPF, MXFP4_SWIGLU, INT4ZP = WORKLOADS
 HEADLINE = INT4_BIAS   # the layer bench.py measures by default
 
 
@@ -117,6 +122,7 @@ class ExpertWeights:
     bias: Optional[np.ndarray]
     N: int
     K: int
+    zeros: Optional[np.ndarray] = None
 
 
 @dataclass
@@ -137,8 +143,13 @@ class LayerInputs:
 def _projection(rng: np.random.Generator, wl: Workload, E: int, N: int, K: int) -> ExpertWeights:
     g = wl.group
     codes = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    zeros = None
     if wl.qtype == "int4_g128":
         scales = _to_bf16_bits(rng.uniform(0.002, 0.02, size=(E, N, K // g)).astype(np.float32))
+        gs = None
+    elif wl.qtype == "int4zp_g128":
+        scales = _to_bf16_bits(rng.uniform(0.002, 0.02, size=(E, N, K // g)).astype(np.float32))
+        zeros = rng.integers(0, 16, size=(E, N, K // g), dtype=np.uint8)
         gs = None
     elif wl.qtype == "nvfp4_g16":
         scales = _to_e4m3_codes(np.exp2(rng.uniform(4.0, 8.0, size=(E, N, K // g))).astype(np.float32))
@@ -148,7 +159,7 @@ def _projection(rng: np.random.Generator, wl: Workload, E: int, N: int, K: int) 
         gs = None
     else:
         raise ValueError(wl.qtype)
-    return ExpertWeights(codes, scales, gs, None, N, K)
+    return ExpertWeights(codes, scales, gs, None, N, K, zeros)
 
 
 def make_weights(wl: Workload) -> LayerWeights:
@@ -205,6 +216,8 @@ def small_workload(qtype: str, **kw) -> Workload:
                               norm=True, seed=101),
         "mxfp4_g32": Workload("mxfp4_small", "mxfp4_g32", 16, 0, 16, 4, 448, 320, (41,),
                               bias=True, act="swiglu_alpha", interleaved_w13=True, seed=102),
+        "int4zp_g128": Workload("int4zp_small", "int4zp_g128", 12, 2, 8, 2, 512, 384, (37,),
+                                bias=True, seed=103),
     }[qtype]
     return base.replace(**kw) if kw else base
 
@@ -220,6 +233,8 @@ def device_weights(lw: LayerWeights, device="cuda") -> tuple:
             d["gs"] = torch.from_numpy(p.gs).to(device)
         if p.bias is not None:
             d["bias"] = torch.from_numpy(p.bias.view(np.int16)).to(device).view(torch.bfloat16)
+        if p.zeros is not None:
+            d["zeros"] = torch.from_numpy(p.zeros).to(device)
         return d
     int4 = lw.w13.scales.dtype == np.uint16
     nw = None
