@@ -53,7 +53,9 @@ typedef enum {
 typedef enum {
   MOE_Q_INT4_G128 = 0,    /* uint4b8: nibble u means u - 8; bf16 scale per 128 along K       */
   MOE_Q_NVFP4_G16 = 1,    /* E2M1 codes; float8 e4m3fn scale per 16 along K; fp32 global/expert */
-  MOE_Q_MXFP4_G32 = 2     /* E2M1 codes; E8M0 scale per 32 along K                            */
+  MOE_Q_MXFP4_G32 = 2,    /* E2M1 codes; E8M0 scale per 32 along K                            */
+  MOE_Q_INT4ZP_G128 = 3   /* asymmetric int4: unsigned nibble u, integer zero point z (0..15)
+                             and bf16 scale s per 128 along K; the weight is (u - z) * s     */
 } moe_qtype;
 
 typedef enum {
@@ -124,7 +126,7 @@ typedef struct moe_weights {
   uint32_t flags;         /* the MOE_PREP_* flags used                                 */
   int32_t reserved;
   const void* codes;      /* tiled 4-bit codes                                         */
-  const void* scales;     /* tiled group scales                                        */
+  const void* scales;     /* tiled group scales (and zero points)                      */
   const float* global_scale; /* [E] NVFP4 per-expert scale, else NULL                  */
   const uint16_t* bias;   /* bf16 [E, N] or NULL                                       */
 } moe_weights;
@@ -139,18 +141,22 @@ int moe_w4a16_prepared_size(moe_qtype q, int32_t E, int32_t N, int32_t K, uint32
  * Load-time repack (the experiment's prepare / prepare_moe_nvfp4_layer_for_marlin step, and
  * for GPT-OSS the de-interleave and tile padding of sglang PR 28231).  Untimed.
  *   codes         device uint8 [E, N, K/2], two codes per byte, low nibble = even k
- *   scales        device [E, N, K/g]: bf16 bits (int4), e4m3fn codes (NVFP4), E8M0 codes (MXFP4)
+ *   scales        device [E, N, K/g]: bf16 bits (both int4 formats), e4m3fn codes (NVFP4), E8M0
+ *                 codes (MXFP4)
  *   global_scale  device fp32 [E] (NVFP4 only, else NULL)
  *   bias          device bf16 [E, N] or NULL (interleaved like the rows when INTERLEAVED)
+ *   zeros         device uint8 [E, N, K/128], zero points 0..15 (MOE_Q_INT4ZP_G128 only, else
+ *                 NULL; a value above 15 is an error of the caller and is used modulo 16)
  *   out           device buffer of at least `bytes` from moe_w4a16_prepared_size, 256-B aligned
  *   desc          host struct filled with the prepared dims and device pointers into `out`
- * Padded rows/columns get zero codes, unit scales and zero bias, which leaves the layer's
- * result unchanged (act(0, 0) = 0 for both activations).
+ * Padded rows/columns get zero weights (zero codes, and zero points equal to the code for the
+ * int4 formats), unit scales and zero bias, which leaves the layer's result unchanged
+ * (act(0, 0) = 0 for every activation).
  */
 int moe_w4a16_prepare(moe_qtype q, const uint8_t* codes, const void* scales,
-                      const float* global_scale, const uint16_t* bias, int32_t E, int32_t N,
-                      int32_t K, uint32_t flags, void* out, size_t out_bytes, moe_weights* desc,
-                      hipStream_t stream);
+                      const float* global_scale, const uint16_t* bias, const uint8_t* zeros,
+                      int32_t E, int32_t N, int32_t K, uint32_t flags, void* out, size_t out_bytes,
+                      moe_weights* desc, hipStream_t stream);
 
 /* The post-expert norm's effective weight: out[h] = bf16(1 + w[h]) (round to nearest even),
  * as the experiment's prepare binds it once.  w, out: device bf16 [H]. */

@@ -11,7 +11,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_w4a16.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ESIZE, MOE_EHIP = 0, -1, -2, -3, -4
-QTYPE = {"int4_g128": 0, "nvfp4_g16": 1, "mxfp4_g32": 2}
+QTYPE = {"int4_g128": 0, "nvfp4_g16": 1, "mxfp4_g32": 2, "int4zp_g128": 3}
 ACT = {"silu_mul": 0, "swiglu_alpha": 1, "relu2": 2}
 GATED = {"silu_mul": True, "swiglu_alpha": True, "relu2": False}
 PREP_GATE_UP, PREP_INTERLEAVED, PREP_PAD = 0x1, 0x2, 0x4
@@ -44,7 +44,7 @@ SIGNATURES = {
     "moe_align": (C.c_int, [_P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "moe_w4a16_prepared_size": (C.c_int, [C.c_int, _I32, _I32, _I32, C.c_uint32, _I32,
                                           C.POINTER(_I32), C.POINTER(_I32), C.POINTER(_SZ)]),
-    "moe_w4a16_prepare": (C.c_int, [C.c_int, _P, _P, _P, _P, _I32, _I32, _I32, C.c_uint32, _P,
+    "moe_w4a16_prepare": (C.c_int, [C.c_int, _P, _P, _P, _P, _P, _I32, _I32, _I32, C.c_uint32, _P,
                                     _SZ, C.POINTER(MoeWeights), _P]),
     "moe_norm_weight": (C.c_int, [_P, _I32, _P, _P]),
     "moe_choose_block_m": (C.c_int, [_I64, _I32, C.POINTER(_I32)]),

@@ -33,7 +33,7 @@ using namespace moe;
 
 extern "C" const char* moe_last_error(void) { return g_err; }
 
-extern "C" int32_t moe_abi_version(void) { return 1; }
+extern "C" int32_t moe_abi_version(void) { return 2; }
 
 extern "C" int moe_align_capacity(int64_t M, int32_t top_k, int32_t n_local, int32_t block_m,
                                   int64_t* sorted_len, int64_t* blocks_len) {
@@ -52,8 +52,8 @@ extern "C" int moe_align_capacity(int64_t M, int32_t top_k, int32_t n_local, int
 extern "C" int moe_w4a16_prepared_size(moe_qtype q, int32_t E, int32_t N, int32_t K, uint32_t flags,
                                        int32_t has_bias, int32_t* N_out, int32_t* K_out,
                                        size_t* bytes) {
-  MOE_REQUIRE(q == MOE_Q_INT4_G128 || q == MOE_Q_NVFP4_G16 || q == MOE_Q_MXFP4_G32, MOE_EINVAL,
-              "unknown qtype %d", (int)q);
+  MOE_REQUIRE(q == MOE_Q_INT4_G128 || q == MOE_Q_NVFP4_G16 || q == MOE_Q_MXFP4_G32 || q == MOE_Q_INT4ZP_G128,
+              MOE_EINVAL, "unknown qtype %d", (int)q);
   MOE_REQUIRE(E >= 1 && N >= 1 && K >= 1, MOE_EINVAL, "E=%d N=%d K=%d must be positive", E, N, K);
   MOE_REQUIRE((flags & ~(MOE_PREP_GATE_UP | MOE_PREP_INTERLEAVED | MOE_PREP_PAD)) == 0, MOE_EINVAL,
               "unknown prepare flags 0x%x", flags);
@@ -76,7 +76,7 @@ extern "C" int moe_w4a16_prepared_size(moe_qtype q, int32_t E, int32_t N, int32_
   if (pad) kout = (K + kTileK - 1) / kTileK * kTileK;
   MOE_REQUIRE(kout % kTileK == 0, MOE_EUNSUPPORTED,
               "K=%d is not a multiple of %d (use MOE_PREP_PAD)", K, kTileK);
-  if (q == MOE_Q_INT4_G128)
+  if (pair_grouped(q))
     MOE_REQUIRE(kout % 128 == 0, MOE_EUNSUPPORTED, "int4: K=%d must be a multiple of 128", kout);
   const size_t tiles = (size_t)E * (nout / kTileN) * (kout / kTileK);
   size_t total = align256(tiles * kTileBytes);

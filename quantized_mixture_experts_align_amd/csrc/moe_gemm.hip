@@ -32,7 +32,7 @@ static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64
                      int32_t top_k, int32_t block_m, const moe_gemm_config* cfg, hipStream_t stream,
                      const int32_t* topk_ids = nullptr, int32_t expert_start = 0, int32_t* slot_local = nullptr) {
   MOE_REQUIRE(W, MOE_EINVAL, "moe_w4a16_gemm: null weights");
-  MOE_REQUIRE(W->qtype >= 0 && W->qtype <= 2, MOE_EINVAL, "moe_w4a16_gemm: bad qtype %d", W->qtype);
+  MOE_REQUIRE(W->qtype >= 0 && W->qtype <= 3, MOE_EINVAL, "moe_w4a16_gemm: bad qtype %d", W->qtype);
   MOE_REQUIRE(W->n_experts >= 1 && W->N >= kTileN && W->N % kTileN == 0 && W->K >= kTileK &&
                   W->K % kTileK == 0,
               MOE_EINVAL, "moe_w4a16_gemm: weights E=%d N=%d K=%d not in the prepared layout",
@@ -96,12 +96,14 @@ static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64
       switch (W->qtype) {
         case MOE_Q_INT4_G128: return launch_gemm_stream<MOE_Q_INT4_G128>(bias, act, a, c, (int)cap_blocks, cus, stream);
         case MOE_Q_NVFP4_G16: return launch_gemm_stream<MOE_Q_NVFP4_G16>(bias, act, a, c, (int)cap_blocks, cus, stream);
+        case MOE_Q_INT4ZP_G128: return launch_gemm_stream<MOE_Q_INT4ZP_G128>(bias, act, a, c, (int)cap_blocks, cus, stream);
         default: return launch_gemm_stream<MOE_Q_MXFP4_G32>(bias, act, a, c, (int)cap_blocks, cus, stream);
       }
     }
     switch (W->qtype) {
       case MOE_Q_INT4_G128: return launch_gemm_decode<MOE_Q_INT4_G128>(bias, act, a, c, (int)cap_blocks, cus, stream);
       case MOE_Q_NVFP4_G16: return launch_gemm_decode<MOE_Q_NVFP4_G16>(bias, act, a, c, (int)cap_blocks, cus, stream);
+      case MOE_Q_INT4ZP_G128: return launch_gemm_decode<MOE_Q_INT4ZP_G128>(bias, act, a, c, (int)cap_blocks, cus, stream);
       default: return launch_gemm_decode<MOE_Q_MXFP4_G32>(bias, act, a, c, (int)cap_blocks, cus, stream);
     }
   }
@@ -118,6 +120,7 @@ static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64
   switch (W->qtype) {
     case MOE_Q_INT4_G128: return launch_gemm_mfma<MOE_Q_INT4_G128>(bias, act, a, c, (int)cap_blocks, stream);
     case MOE_Q_NVFP4_G16: return launch_gemm_mfma<MOE_Q_NVFP4_G16>(bias, act, a, c, (int)cap_blocks, stream);
+    case MOE_Q_INT4ZP_G128: return launch_gemm_mfma<MOE_Q_INT4ZP_G128>(bias, act, a, c, (int)cap_blocks, stream);
     default: return launch_gemm_mfma<MOE_Q_MXFP4_G32>(bias, act, a, c, (int)cap_blocks, stream);
   }
 }

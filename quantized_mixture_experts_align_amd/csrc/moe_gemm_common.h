@@ -65,7 +65,8 @@ __device__ __forceinline__ float fused_act(float gate, float up, const GemmArgs&
 // ---------------------------------------------------------------------------- dequant
 // Group scales of one 64-column tile for this lane, kept as raw bits (they sit in prefetch
 // rings) and converted to fp32 at use: s(i, lane) is the scale of k-step i (k = 32 i + 8 (lane/16)
-// + 0..7 of the tile).
+// + 0..7 of the tile); for the int4 formats m(i, lane) is the weight's additive term, -z * s
+// (z = 8 for uint4b8), so that a weight is u * s + m.
 template <int QT> struct TileScale;
 
 // NVFP4: the row's four e4m3 codes of the tile; k-step i of this lane is group 2 i + lane/32.
@@ -78,6 +79,7 @@ template <> struct TileScale<MOE_Q_NVFP4_G16> {
   __device__ __forceinline__ float s(int i, int lane) const {
     return __builtin_amdgcn_cvt_f32_fp8((int)(raw >> (8 * (lane >> 5) + 16 * i)), 0);
   }
+  __device__ __forceinline__ float m(int, int) const { return 0.f; }
 };
 // MXFP4: the row's two E8M0 codes (one per k-step) -> fp32 powers of two (exponent field = code).
 template <> struct TileScale<MOE_Q_MXFP4_G32> {
@@ -87,6 +89,7 @@ template <> struct TileScale<MOE_Q_MXFP4_G32> {
     raw = reinterpret_cast<const uint16_t*>(tile_scales)[(int64_t)kt * 16 + (lane & 15)];
   }
   __device__ __forceinline__ float s(int i, int) const { return __uint_as_float(((raw >> (8 * i)) & 0xFFu) << 23); }
+  __device__ __forceinline__ float m(int, int) const { return 0.f; }
 };
 // int4: one bf16 scale per group of 128 (a tile pair).
 template <> struct TileScale<MOE_Q_INT4_G128> {
@@ -96,6 +99,18 @@ template <> struct TileScale<MOE_Q_INT4_G128> {
     raw = reinterpret_cast<const uint16_t*>(tile_scales)[(int64_t)(kt >> 1) * 16 + (lane & 15)];
   }
   __device__ __forceinline__ float s(int, int) const { return __uint_as_float(raw << 16); }
+  __device__ __forceinline__ float m(int i, int lane) const { return -8.0f * s(i, lane); }
+};
+// asymmetric int4: per row and group of 128 one dword, bf16 scale | zero point << 16.
+template <> struct TileScale<MOE_Q_INT4ZP_G128> {
+  uint32_t raw;
+  static constexpr int kRowBytes = 4;  // per tile pair
+  __device__ __forceinline__ void load(const uint8_t* tile_scales, int kt, int lane) {
+    raw = reinterpret_cast<const uint32_t*>(tile_scales)[(int64_t)(kt >> 1) * 16 + (lane & 15)];
+  }
+  __device__ __forceinline__ float s(int, int) const { return __uint_as_float(raw << 16); }
+  // -z * s is exact in fp32 (4 x 8 significant bits)
+  __device__ __forceinline__ float m(int i, int lane) const { return -(float)((raw >> 16) & 0xFu) * s(i, lane); }
 };
 
 __device__ __forceinline__ uint32_t bits2(bf16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
@@ -113,8 +128,9 @@ __device__ __forceinline__ float ubyte_to_f32(uint32_t x) {
 }
 
 // Eight codes (one dword, k order) -> eight bf16 weights, scale folded in (the MFMA A operand).
+// m: the int4 formats' additive term (TileScale::m), unused by the fp4 formats.
 template <int QT>
-__device__ __forceinline__ u32x4_t dequant8(uint32_t w, float s) {
+__device__ __forceinline__ u32x4_t dequant8(uint32_t w, float s, float m) {
   u32x4_t o;
   if constexpr (QT == MOE_Q_MXFP4_G32) {
     // the hardware fp4 convert applies a power-of-two scale exactly (its exponent field)
@@ -133,10 +149,11 @@ __device__ __forceinline__ u32x4_t dequant8(uint32_t w, float s) {
     o[2] = pack_bf16x2(p2[0] * s, p2[1] * s);
     o[3] = pack_bf16x2(p3[0] * s, p3[1] * s);
   } else {
-    // uint4b8: (u - 8) * s, exact in fp32 (4 x 8 significant bits), rounded once to bf16;
-    // even-k nibbles are the low nibbles of the four bytes, odd-k the high ones
+    // int4 formats: u * s + m = (u - z) * s, exact in fp32 (4 x 8 significant bits), rounded once
+    // to bf16; even-k nibbles are the low nibbles of the four bytes, odd-k the high ones
+    static_assert(QT == MOE_Q_INT4_G128 || QT == MOE_Q_INT4ZP_G128, "unknown weight format");
     const uint32_t t0 = w & 0x0F0F0F0Fu, t1 = (w >> 4) & 0x0F0F0F0Fu;
-    const float m8s = -8.0f * s;
+    const float m8s = m;
     o[0] = pack_bf16x2(fmaf(ubyte_to_f32<0>(t0), s, m8s), fmaf(ubyte_to_f32<0>(t1), s, m8s));
     o[1] = pack_bf16x2(fmaf(ubyte_to_f32<1>(t0), s, m8s), fmaf(ubyte_to_f32<1>(t1), s, m8s));
     o[2] = pack_bf16x2(fmaf(ubyte_to_f32<2>(t0), s, m8s), fmaf(ubyte_to_f32<2>(t1), s, m8s));
@@ -148,7 +165,7 @@ __device__ __forceinline__ u32x4_t dequant8(uint32_t w, float s) {
 // Raw codes for the dot-product path: the group scale is applied to the partial sum instead
 // (NVFP4), or folded into the exact power-of-two convert (MXFP4), or into the weight (int4).
 template <int QT>
-__device__ __forceinline__ u32x4_t dequant8_raw(uint32_t w, float s) {
+__device__ __forceinline__ u32x4_t dequant8_raw(uint32_t w, float s, float m) {
   if constexpr (QT == MOE_Q_NVFP4_G16) {
     u32x4_t o;
     o[0] = bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0));
@@ -157,7 +174,7 @@ __device__ __forceinline__ u32x4_t dequant8_raw(uint32_t w, float s) {
     o[3] = bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3));
     return o;
   } else {
-    return dequant8<QT>(w, s);
+    return dequant8<QT>(w, s, m);
   }
 }
 

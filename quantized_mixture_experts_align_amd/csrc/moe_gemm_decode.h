@@ -79,8 +79,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode_kernel(GemmArgs a, int ge
       tile[g] = g < NGA ? min(strip * NGA + g, NTA - 1) : tile[g - NGA] + NTA;
       const int64_t tile0 = ((int64_t)e * NT + tile[g]) * KT;
       wp[g] = reinterpret_cast<const u32x2_t*>(a.codes + tile0 * kTileBytes) + lane;
-      sp[g] = a.scales + (QT == MOE_Q_INT4_G128 ? ((int64_t)e * NT + tile[g]) * (KT / 2) * 32
-                                                : tile0 * scale_bytes_per_tile(QT));
+      sp[g] = a.scales + ((int64_t)e * NT + tile[g]) * (pair_grouped(QT) ? KT / 2 : KT) * scale_step_bytes(QT);
     }
     const bool gemv = cnt <= gemv_rows;
     const int m = lane & 15;
@@ -129,7 +128,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode_kernel(GemmArgs a, int ge
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
               const float s = sc[slot][u][g].s(i, lane);
-              const u32x4_t wv = dequant8_raw<QT>(q[slot][u][g][i], s);
+              const u32x4_t wv = dequant8_raw<QT>(q[slot][u][g][i], s, sc[slot][u][g].m(i, lane));
 #pragma unroll
               for (int r = 0; r < kGemvMax; ++r) {
                 if (r >= cnt) break;
@@ -142,7 +141,8 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode_kernel(GemmArgs a, int ge
           } else {
 #pragma unroll
             for (int g = 0; g < NG; ++g)
-              macc[g] = mfma(dequant8<QT>(q[slot][u][g][i], sc[slot][u][g].s(i, lane)), xv[slot][u][i], macc[g]);
+              macc[g] = mfma(dequant8<QT>(q[slot][u][g][i], sc[slot][u][g].s(i, lane), sc[slot][u][g].m(i, lane)),
+                             xv[slot][u][i], macc[g]);
           }
         }
       }

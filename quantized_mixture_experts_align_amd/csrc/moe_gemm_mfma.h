@@ -168,8 +168,8 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
     }
     const int64_t tile0 = ((int64_t)e * NT + ntile[g]) * KT;
     wbase[g] = uniform_ptr(a.codes + tile0 * kTileBytes);
-    sbase[g] = uniform_ptr(a.scales + (QT == MOE_Q_INT4_G128 ? ((int64_t)e * NT + ntile[g]) * (KT / 2) * 32
-                                                             : tile0 * scale_bytes_per_tile(QT)));
+    sbase[g] = uniform_ptr(a.scales + ((int64_t)e * NT + ntile[g]) * (pair_grouped(QT) ? KT / 2 : KT) *
+                                          scale_step_bytes(QT));
   }
   const uint32_t loff = (uint32_t)lane * 4;  // a lane's dword of a 256-B weight or scale row
   auto issue = [&](int kt, int stage) {
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
       const uint8_t* src = wbase[g] + (int64_t)kt * kTileBytes;
       dma_to_lds<4>(src, loff, wt);
       dma_to_lds<4>(src + 256, loff, wt + 256);
-      const int64_t soff = QT == MOE_Q_INT4_G128 ? (int64_t)(kt >> 1) * 32 : (int64_t)kt * scale_bytes_per_tile(QT);
+      const int64_t soff = (int64_t)(pair_grouped(QT) ? kt >> 1 : kt) * scale_step_bytes(QT);
       if (lane < SLANES)
         dma_to_lds<4>(sbase[g] + soff, loff, st + XB + WB + (w * NG + g) * 64);
     }
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
     for (int i = 0; i < 2; ++i) {
       u32x4_t af[NG];
 #pragma unroll
-      for (int g = 0; g < NG; ++g) af[g] = dequant8<QT>(wq[g][i], sc[g].s(i, lane));
+      for (int g = 0; g < NG; ++g) af[g] = dequant8<QT>(wq[g][i], sc[g].s(i, lane), sc[g].m(i, lane));
 #pragma unroll
       for (int h = 0; h < MG; ++h) {
         const u32x4_t bf = xs[(i * MG + h) * 64 + lane];

@@ -157,7 +157,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
       for (int g = 0; g < NG; ++g) {
         const int64_t tile = (int64_t)e * NT + tile_of(strip, g);
         wp[g] = reinterpret_cast<const u32x2_t*>(a.codes + tile * KT * kTileBytes) + lane;
-        sp[g] = a.scales + (QT == MOE_Q_INT4_G128 ? tile * (KT / 2) * 32 : tile * KT * scale_bytes_per_tile(QT));
+        sp[g] = a.scales + tile * (pair_grouped(QT) ? KT / 2 : KT) * scale_step_bytes(QT);
       }
       const int s = t_row[q][m];
       xp = a.A + (int64_t)(s >= 0 ? s / a.top_k : 0) * a.lda + j8;
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int g = 0; g < NG; ++g)
-          acc[g] = mfma(dequant8<QT>(rq[u][g][i], rs[u][g].s(i, lane)), rx[u][i], acc[g]);
+          acc[g] = mfma(dequant8<QT>(rq[u][g][i], rs[u][g].s(i, lane), rs[u][g].m(i, lane)), rx[u][i], acc[g]);
       if (++cs == L) {
         finish(cq);
         cs = 0;

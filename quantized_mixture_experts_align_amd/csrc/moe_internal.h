@@ -32,12 +32,19 @@ constexpr int kTileN = 16;
 constexpr int kTileK = 64;
 constexpr int kTileBytes = kTileN * kTileK / 2;
 
-inline __host__ __device__ int group_of(int q) { return q == MOE_Q_INT4_G128 ? 128 : (q == MOE_Q_NVFP4_G16 ? 16 : 32); }
+// the int4 formats: a group of 128 along K spans two 64-column tiles
+inline __host__ __device__ bool pair_grouped(int q) { return q == MOE_Q_INT4_G128 || q == MOE_Q_INT4ZP_G128; }
+inline __host__ __device__ int group_of(int q) { return pair_grouped(q) ? 128 : (q == MOE_Q_NVFP4_G16 ? 16 : 32); }
 
 // Scale bytes per (16-row x 64-column) tile.  NVFP4: 16 rows x 4 e4m3 codes; MXFP4: 16 rows x
-// 2 E8M0 codes; int4: the group of 128 spans two tiles, stored per tile pair as 16 bf16.
+// 2 E8M0 codes; int4: the group of 128 spans two tiles, stored per tile pair as 16 bf16;
+// asymmetric int4: per tile pair 16 dwords, each bf16 scale | zero point << 16.
 inline __host__ __device__ int scale_bytes_per_tile(int q) {
-  return q == MOE_Q_NVFP4_G16 ? 64 : (q == MOE_Q_MXFP4_G32 ? 32 : 16);
+  return q == MOE_Q_NVFP4_G16 ? 64 : (q == MOE_Q_MXFP4_G32 ? 32 : (q == MOE_Q_INT4ZP_G128 ? 32 : 16));
+}
+// bytes of scales per scale step of a 16-row tile column: a tile pair (int4 formats) or a tile
+inline __host__ __device__ int scale_step_bytes(int q) {
+  return pair_grouped(q) ? 2 * scale_bytes_per_tile(q) : scale_bytes_per_tile(q);
 }
 
 inline __host__ __device__ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

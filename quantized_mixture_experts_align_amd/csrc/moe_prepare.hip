@@ -8,6 +8,7 @@
 //   scales  NVFP4: [E][N/16][K/64][16 rows][4 e4m3]   (the four groups of 16 of the tile)
 //           MXFP4: [E][N/16][K/64][16 rows][2 E8M0]   (the two groups of 32)
 //           int4:  [E][N/16][K/128][16 rows] bf16      (one group of 128 per tile pair)
+//           asymmetric int4: [E][N/16][K/128][16 rows] u32 = bf16 scale | zero point << 16
 //   gs      fp32 [E]                 (NVFP4)
 //   bias    bf16 [E][N]              (optional)
 // Output row n of a gate/up pair: gate j = n for n < I_pad, up j = n - I_pad otherwise; source
@@ -55,10 +56,32 @@ __global__ void prep_codes_kernel(const uint8_t* __restrict__ src, uint32_t* __r
 }
 
 // one thread per output scale element
-__global__ void prep_scales_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, PrepGeom g) {
+__global__ void prep_scales_kernel(const uint8_t* __restrict__ src, const uint8_t* __restrict__ zeros,
+                                   uint8_t* __restrict__ dst, PrepGeom g) {
   const int NT = g.Nout / kTileN, KT = g.Kout / kTileK;
   const int grp = group_of(g.q);
   const int ngroups = g.K / grp;  // groups per source row
+  if (g.q == MOE_Q_INT4ZP_G128) {  // padding: unit scale, zero point 0 (padding codes are 0)
+    const uint16_t* s16 = reinterpret_cast<const uint16_t*>(src);
+    uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
+    const int64_t total = (int64_t)g.E * NT * (KT / 2) * 16;
+    for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < total;
+         d += (int64_t)gridDim.x * blockDim.x) {
+      const int row = (int)(d & 15);
+      const int64_t t = d >> 4;
+      const int kp = (int)(t % (KT / 2));
+      const int64_t et = t / (KT / 2);
+      const int nt = (int)(et % NT), e = (int)(et / NT);
+      const int r = src_row(g, nt * kTileN + row);
+      uint32_t v = 0x3F80u;
+      if (r >= 0 && kp < ngroups) {
+        const int64_t i = ((int64_t)e * g.N + r) * ngroups + kp;
+        v = (uint32_t)s16[i] | ((uint32_t)(zeros[i] & 0xF) << 16);
+      }
+      d32[d] = v;
+    }
+    return;
+  }
   if (g.q == MOE_Q_INT4_G128) {
     const uint16_t* s16 = reinterpret_cast<const uint16_t*>(src);
     uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);
@@ -110,9 +133,9 @@ static int grid_for(int64_t n) { return (int)std::min<int64_t>((n + 255) / 256, 
 using namespace moe;
 
 extern "C" int moe_w4a16_prepare(moe_qtype q, const uint8_t* codes, const void* scales,
-                                 const float* global_scale, const uint16_t* bias, int32_t E,
-                                 int32_t N, int32_t K, uint32_t flags, void* out, size_t out_bytes,
-                                 moe_weights* desc, hipStream_t stream) {
+                                 const float* global_scale, const uint16_t* bias, const uint8_t* zeros,
+                                 int32_t E, int32_t N, int32_t K, uint32_t flags, void* out,
+                                 size_t out_bytes, moe_weights* desc, hipStream_t stream) {
   int32_t Nout = 0, Kout = 0;
   size_t need = 0;
   int rc = moe_w4a16_prepared_size(q, E, N, K, flags, bias != nullptr, &Nout, &Kout, &need);
@@ -120,6 +143,8 @@ extern "C" int moe_w4a16_prepare(moe_qtype q, const uint8_t* codes, const void* 
   MOE_REQUIRE(codes && scales && out && desc, MOE_EINVAL, "moe_w4a16_prepare: null pointer");
   MOE_REQUIRE((q == MOE_Q_NVFP4_G16) == (global_scale != nullptr), MOE_EINVAL,
               "moe_w4a16_prepare: a global scale is required for NVFP4 and only for NVFP4");
+  MOE_REQUIRE((q == MOE_Q_INT4ZP_G128) == (zeros != nullptr), MOE_EINVAL,
+              "moe_w4a16_prepare: zero points are required for asymmetric int4 and only for it");
   MOE_REQUIRE(out_bytes >= need, MOE_ESIZE, "moe_w4a16_prepare: out has %zu bytes, %zu needed",
               out_bytes, need);
   MOE_REQUIRE(((uintptr_t)out & 255) == 0, MOE_EINVAL, "moe_w4a16_prepare: out must be 256-byte aligned");
@@ -135,7 +160,7 @@ extern "C" int moe_w4a16_prepare(moe_qtype q, const uint8_t* codes, const void* 
   hipLaunchKernelGGL(prep_codes_kernel, dim3(grid_for((int64_t)tiles * 128)), dim3(256), 0, stream,
                      codes, reinterpret_cast<uint32_t*>(p_codes), g);
   hipLaunchKernelGGL(prep_scales_kernel, dim3(grid_for((int64_t)tiles * 64)), dim3(256), 0, stream,
-                     static_cast<const uint8_t*>(scales), p_scales, g);
+                     static_cast<const uint8_t*>(scales), zeros, p_scales, g);
   if (q == MOE_Q_NVFP4_G16) {
     hipError_t e = hipMemcpyAsync(p_gs, global_scale, (size_t)E * 4, hipMemcpyDeviceToDevice, stream);
     MOE_REQUIRE(e == hipSuccess, MOE_EHIP, "moe_w4a16_prepare: copy of the global scales: %s",

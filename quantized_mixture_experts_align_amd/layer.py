@@ -60,9 +60,9 @@ class MoELayer:
             f13 = L.PREP_PAD if pad else 0
         f2 = L.PREP_PAD if pad else 0
         self.W13 = ops.moe_w4a16_prepare(qtype, w13["codes"], w13["scales"], w13.get("gs"),
-                                         w13.get("bias"), f13)
+                                         w13.get("bias"), f13, w13.get("zeros"))
         self.W2 = ops.moe_w4a16_prepare(qtype, w2["codes"], w2["scales"], w2.get("gs"),
-                                        w2.get("bias"), f2)
+                                        w2.get("bias"), f2, w2.get("zeros"))
         self.I = self.W13.N // 2 if self.gated else self.W13.N
         if self.W2.K != self.I:
             raise ValueError(f"down projection K={self.W2.K} != intermediate {self.I}")

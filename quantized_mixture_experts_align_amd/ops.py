@@ -96,8 +96,9 @@ def prepared_size(qtype: str, E: int, N: int, K: int, flags: int, has_bias: bool
 
 def moe_w4a16_prepare(qtype: str, codes: torch.Tensor, scales: torch.Tensor,
                       global_scale: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
-                      flags: int = 0) -> PreparedWeights:
-    """Repack canonical [E, N, K/2] codes and [E, N, K/g] scales into the tiled layout."""
+                      flags: int = 0, zeros: Optional[torch.Tensor] = None) -> PreparedWeights:
+    """Repack canonical [E, N, K/2] codes and [E, N, K/g] scales (and, for int4zp_g128, the
+    uint8 [E, N, K/128] zero points) into the tiled layout."""
     _need(codes, torch.uint8, "codes")
     if not scales.is_cuda or not scales.is_contiguous():
         raise ValueError("scales must be a contiguous device tensor")
@@ -110,11 +111,13 @@ def moe_w4a16_prepare(qtype: str, codes: torch.Tensor, scales: torch.Tensor,
             raise ValueError("bias must hold bf16 values")
         if not bias.is_cuda or not bias.is_contiguous():
             raise ValueError("bias must be a contiguous device tensor")
+    if zeros is not None:
+        _need(zeros, torch.uint8, "zeros")
     _, _, nbytes = prepared_size(qtype, E, N, K, flags, bias is not None)
     buf = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
     desc = L.MoeWeights()
     L.check(L.lib().moe_w4a16_prepare(L.QTYPE[qtype], _ptr(codes), _ptr(scales), _ptr(global_scale),
-                                      _ptr(bias), E, N, K, flags, _ptr(buf), nbytes, C.byref(desc),
+                                      _ptr(bias), _ptr(zeros), E, N, K, flags, _ptr(buf), nbytes, C.byref(desc),
                                       _stream()), "moe_w4a16_prepare")
     return PreparedWeights(buf, desc)
 

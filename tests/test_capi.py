@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(lib, n), n
         assert n in L.SIGNATURES, f"{n} has no binding"
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 @pytest.mark.parametrize("M,k,E,B", [(0, 8, 32, 16), (1, 8, 32, 16), (123, 2, 8, 64), (4096, 8, 32, 128),
@@ -57,6 +57,12 @@ def test_prepared_size_validation():
         P.prepared_size("int4_g128", 4, 64, 256, L.PREP_INTERLEAVED, False)
     with pytest.raises(ValueError):
         P.prepared_size("nvfp4_g16", 4, 40, 256, 0, False)   # N not a multiple of 16
+    # asymmetric int4: 512-B code tiles, 64 B of (scale, zero point) dwords per tile pair
+    n, k, b = P.prepared_size("int4zp_g128", 4, 64, 256, 0, False)
+    tiles = 4 * (64 // 16) * (256 // 64)
+    assert (n, k, b) == (64, 256, tiles * 512 + tiles * 32)
+    with pytest.raises(ValueError):
+        P.prepared_size("int4zp_g128", 4, 64, 192, 0, False)  # K not a multiple of 128
 
 
 def test_entry_points_reject_bad_arguments_before_launch():
@@ -104,6 +110,13 @@ def test_entry_points_reject_bad_arguments_before_launch():
     cfg = L.MoeGemmConfig(L.GEMM_MFMA, 2, 0, 0)
     assert routed(L.ACT["silu_mul"], 1.0, 1.0, a16, 1, 4096, a16, 4096, C.byref(W), s, 1, 8, 0, 16,
                   s, s, s, s, C.byref(cfg), None) == L.MOE_EUNSUPPORTED and b"streaming" in lib.moe_last_error()
+    # zero points: required for asymmetric int4 and only for it (checked before any launch)
+    desc = L.MoeWeights()
+    out = C.c_void_p(1 << 20)
+    assert lib.moe_w4a16_prepare(L.QTYPE["int4zp_g128"], s, s, None, None, None, 4, 64, 256, 0, out, 1 << 20,
+                                 C.byref(desc), None) == L.MOE_EINVAL and b"zero points" in lib.moe_last_error()
+    assert lib.moe_w4a16_prepare(L.QTYPE["int4_g128"], s, s, None, None, s, 4, 64, 256, 0, out, 1 << 20,
+                                 C.byref(desc), None) == L.MOE_EINVAL and b"zero points" in lib.moe_last_error()
     # numel == 0 is a no-op that needs no device
     assert lib.moe_w4a16_gemm(None, 0, 4096, None, 8192, C.byref(W), None, None, None, 0, 8, 16, None, None) \
         == L.MOE_OK

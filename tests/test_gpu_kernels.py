@@ -30,11 +30,12 @@ def _gemm_case(qtype, which, M, B, cfg, wl_kw=None):
     w13, w2, _ = W.device_weights(lw)
     if which == 13:
         flags = L.PREP_GATE_UP | (L.PREP_INTERLEAVED if wl.interleaved_w13 else 0)
-        Wp = P.moe_w4a16_prepare(qtype, w13["codes"], w13["scales"], w13.get("gs"), w13.get("bias"), flags)
+        Wp = P.moe_w4a16_prepare(qtype, w13["codes"], w13["scales"], w13.get("gs"), w13.get("bias"), flags,
+                                 w13.get("zeros"))
         proj, top_k = lw.w13, wl.top_k
         A_bits = inp.x
     else:
-        Wp = P.moe_w4a16_prepare(qtype, w2["codes"], w2["scales"], w2.get("gs"), w2.get("bias"), 0)
+        Wp = P.moe_w4a16_prepare(qtype, w2["codes"], w2["scales"], w2.get("gs"), w2.get("bias"), 0, w2.get("zeros"))
         proj, top_k = lw.w2, 1
         rng = np.random.default_rng(M)
         A_bits = W._to_bf16_bits(rng.standard_normal((M * wl.top_k, wl.I)).astype(np.float32))
@@ -50,7 +51,8 @@ def _gemm_case(qtype, which, M, B, cfg, wl_kw=None):
     ref = np.zeros((rows.size, Wp.N))
     for j, slot in enumerate(rows):
         ex = local[slot]
-        Wd = O.dequant(qtype, proj.codes[ex], proj.scales[ex], None if proj.gs is None else proj.gs[ex])
+        Wd = O.dequant(qtype, proj.codes[ex], proj.scales[ex], None if proj.gs is None else proj.gs[ex],
+                       None if proj.zeros is None else proj.zeros[ex])
         h = Wd @ A[slot // top_k]
         if proj.bias is not None:
             h = h + F.decode_bf16(proj.bias[ex])
@@ -88,7 +90,7 @@ def test_gemm_matches_oracle(qtype, kind, which):
     got, ref, _ = _gemm_case(qtype, which, M, B, cfg)
     err = np.abs(got - ref)
     assert np.all(err <= gemm_tolerance(ref)), f"max err {err.max()} rel rms {rel_rms(got, ref)}"
-    assert rel_rms(got, ref) < (4e-3 if qtype == "int4_g128" else 2e-3)
+    assert rel_rms(got, ref) < (4e-3 if qtype in ("int4_g128", "int4zp_g128") else 2e-3)
 
 
 @pytest.mark.parametrize("qtype", W.QTYPES)
@@ -192,7 +194,8 @@ def test_fused_activation_equals_gemm_then_act(qtype, kind, act):
     inp = W.make_inputs(wl, M)
     w13, _, _ = W.device_weights(lw)
     flags = 0 if act == "relu2" else L.PREP_GATE_UP | (L.PREP_INTERLEAVED if wl.interleaved_w13 else 0)
-    W13 = P.moe_w4a16_prepare(qtype, w13["codes"], w13["scales"], w13.get("gs"), w13.get("bias"), flags)
+    W13 = P.moe_w4a16_prepare(qtype, w13["codes"], w13["scales"], w13.get("gs"), w13.get("bias"), flags,
+                              w13.get("zeros"))
     s, e, n, loc = P.moe_align(torch.from_numpy(inp.topk_ids).cuda(), wl.expert_start, wl.n_local, B)
     x = _bf16_dev(inp.x)
     numel = M * wl.top_k

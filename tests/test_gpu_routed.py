@@ -23,7 +23,7 @@ def _w13(qtype):
         w13, _, _ = W.device_weights(lw)
         flags = L.PREP_GATE_UP | (L.PREP_INTERLEAVED if wl.interleaved_w13 else 0)
         _W13[qtype] = (wl, P.moe_w4a16_prepare(qtype, w13["codes"], w13["scales"], w13.get("gs"),
-                                               w13.get("bias"), flags))
+                                               w13.get("bias"), flags, w13.get("zeros")))
     return _W13[qtype]
 
 

@@ -149,7 +149,9 @@ def _projection(rng: np.random.Generator, wl: Workload, E: int, N: int, K: int) 
         gs = None
     elif wl.qtype == "int4zp_g128":
         scales = _to_bf16_bits(rng.uniform(0.002, 0.02, size=(E, N, K // g)).astype(np.float32))
-        zeros = rng.integers(0, 16, size=(E, N, K // g), dtype=np.uint8)
+        # a min/max quantiser puts a roughly zero-centred group's zero point near the middle of
+        # 0..15; the tails still reach both ends
+        zeros = np.clip(np.rint(rng.normal(7.5, 2.5, size=(E, N, K // g))), 0, 15).astype(np.uint8)
         gs = None
     elif wl.qtype == "nvfp4_g16":
         scales = _to_e4m3_codes(np.exp2(rng.uniform(4.0, 8.0, size=(E, N, K // g))).astype(np.float32))
