@@ -149,7 +149,8 @@ def test_act_matches_oracle(kind, limit):
 
 # single-pass kernel (top_k <= 8, H <= 8192; M <= 256 also reads y of dead slots, unused) and
 # the two-pass kernel beyond that
-@pytest.mark.parametrize("H,norm,M,k", [(512, False, 45, 8), (4096, True, 45, 8), (2880, False, 45, 8),
+@pytest.mark.parametrize("H,norm,M,k", [(512, False, 45, 8), (512, False, 2305, 2), (256, False, 18, 3),
+                                        (4096, True, 45, 8), (2880, False, 45, 8),
                                         (2880, True, 45, 8), (64, True, 45, 8), (4096, True, 300, 8),
                                         (512, False, 300, 2), (2880, True, 45, 4), (8192, True, 20, 8),
                                         (512, True, 20, 16), (16384, True, 5, 8)])
