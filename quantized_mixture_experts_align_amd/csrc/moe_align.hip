@@ -41,8 +41,9 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   // every wave owns a chunk (the scatter is serial per 64-slot batch within a wave, so short
   // chunks are faster even when most waves are idle)
   const int nwv = kAlignWaves;
-  for (int i = tid; i < nwv * n_local; i += kAlignThreads) cnt[i] = 0;
-  __syncthreads();
+  // each wave zeroes and then counts into its own row only: a wave barrier suffices here
+  for (int i = lane; i < n_local; i += 64) cnt[w * n_local + i] = 0;
+  __builtin_amdgcn_wave_barrier();
 
   // chunk of wave w: [c0, c1), a multiple of 64 slots long (empty for waves >= nwv)
   const int per = ((numel + nwv - 1) / nwv + 63) & ~63;
