@@ -151,3 +151,17 @@ def test_gemm_choose_contract(N, K, E):
     # more work never selects a narrower tile
     ngs = [P.gemm_choose(W, n, 128, 256).ng for n in (256, 1024, 8192, 65536)]
     assert ngs == sorted(ngs)
+
+
+def test_gemm_choose_tiles_for_streamed_prefill_weights():
+    # 64-slot blocks: four tiles per wave when K is long and the dequantisation cheap (MXFP4) or the
+    # projection is not a gate/up pair; two for an NVFP4 gate/up pair and for short K (int4 shapes)
+    def ng(q, N, K, E, flags, numel=8192, B=64):
+        W = P.PreparedWeights(None, L.MoeWeights(L.QTYPE[q], E, N, K, N, K, flags, 0, 1, 1, None, None))
+        return P.gemm_choose(W, numel, B, 256).ng
+    assert ng("mxfp4_g32", 5760, 2880, 128, L.PREP_GATE_UP) == 4
+    assert ng("mxfp4_g32", 2880, 2880, 128, 0) == 4
+    assert ng("nvfp4_g16", 4096, 4096, 32, 0, numel=1479) == 4
+    assert ng("nvfp4_g16", 8192, 4096, 32, L.PREP_GATE_UP, numel=1479) == 2
+    assert ng("int4_g128", 2048, 512, 8, L.PREP_GATE_UP, numel=4608) == 2
+    assert ng("int4zp_g128", 2048, 512, 8, L.PREP_GATE_UP, numel=4608) == 2
