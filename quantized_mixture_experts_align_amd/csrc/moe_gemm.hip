@@ -160,8 +160,13 @@ extern "C" int moe_w4a16_gemm_act_routed(moe_act_kind kind, float alpha, float l
               "moe_w4a16_gemm_act_routed: n_experts=%d outside 1..512", W13->n_experts);
   MOE_REQUIRE(expert_start >= 0, MOE_EINVAL, "moe_w4a16_gemm_act_routed: expert_start=%d", expert_start);
   MOE_REQUIRE(numel == 0 || topk_ids, MOE_EINVAL, "moe_w4a16_gemm_act_routed: null topk_ids");
-  MOE_REQUIRE(sorted_token_ids && expert_ids && num_tokens_post_padded && slot_local_ids, MOE_EINVAL,
-              "moe_w4a16_gemm_act_routed: null align output");
+  int64_t cap = 0, cap_blocks = 0;
+  int rc = moe_align_capacity(M, top_k, W13->n_experts, block_m, &cap, &cap_blocks);
+  if (rc) return rc;
+  // (as moe_align: empty buffers may be NULL)
+  MOE_REQUIRE(num_tokens_post_padded && ((sorted_token_ids && expert_ids) || cap == 0) &&
+                  (slot_local_ids || numel == 0),
+              MOE_EINVAL, "moe_w4a16_gemm_act_routed: null align output");
   if (numel == 0) {  // nothing routed: the align outputs of an empty batch (moe_align writes the same)
     return moe_align(topk_ids, 0, top_k, expert_start, W13->n_experts, block_m, sorted_token_ids, expert_ids,
                      num_tokens_post_padded, slot_local_ids, stream);
@@ -171,7 +176,7 @@ extern "C" int moe_w4a16_gemm_act_routed(moe_act_kind kind, float alpha, float l
   if (cfg && cfg->kernel != MOE_GEMM_AUTO) {
     c = *cfg;
   } else {
-    int rc = moe_gemm_choose(W13, numel, block_m, device_cu_count(), &c);
+    rc = moe_gemm_choose(W13, numel, block_m, device_cu_count(), &c);
     if (rc) return rc;
     if (act_paired(act) && c.ng < 2) c.ng = 2;
     c.kernel = MOE_GEMM_DECODE;

@@ -97,6 +97,32 @@ def test_off_slice_tokens_are_zero_and_runs_repeat_bitwise():
     assert layer_violations(a, oracle_layer(wl, lw, inp2)) == 0
 
 
+@pytest.mark.parametrize("qtype", W.QTYPES)
+def test_degenerate_batches(qtype):
+    # an empty batch; batches with no slot on the local slice (fused align at 1 token, the align
+    # kernel at 100); a single token whose top-k all land on one local expert (repeated ids)
+    wl = W.small_workload(qtype)
+    lw = W.make_weights(wl)
+    layer = make_layer(wl, lw)
+    off = wl.expert_start + wl.n_local   # first global id outside the slice
+    announce(f"layer degenerate {qtype}")
+    x0 = torch.zeros((0, wl.H), dtype=torch.bfloat16, device="cuda")
+    out0 = layer(x0, torch.zeros((0, wl.top_k), dtype=torch.int32, device="cuda"),
+                 torch.zeros((0, wl.top_k), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    assert out0.shape == (0, wl.H)
+    for M in (1, 100):
+        inp = W.make_inputs(wl, M)
+        inp = W.LayerInputs(inp.x, np.full_like(inp.topk_ids, off), inp.topk_weights, M)
+        got = _forward(layer, inp)
+        assert np.all(got == 0.0)
+    inp = W.make_inputs(wl, 1)
+    inp = W.LayerInputs(inp.x, np.full_like(inp.topk_ids, wl.expert_start + 1), inp.topk_weights, 1)
+    got = _forward(layer, inp)
+    ref = oracle_layer(wl, lw, inp)
+    assert layer_violations(got, ref) == 0 and np.any(got != 0.0)
+
+
 # ----------------------------------------------------------------------------- full-size workloads
 _CACHE = {}
 
