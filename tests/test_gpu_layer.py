@@ -123,6 +123,24 @@ def test_degenerate_batches(qtype):
     assert layer_violations(got, ref) == 0 and np.any(got != 0.0)
 
 
+@pytest.mark.parametrize("qtype,kw,M", [
+    ("int4_g128", dict(top_k=1), 70),                                  # top-1: slot = token
+    ("nvfp4_g16", dict(n_global=16, expert_start=3, n_local=1), 40),    # one local expert
+    ("mxfp4_g32", dict(top_k=16, n_global=32, n_local=32), 9),          # top-16: two-pass combine
+    ("int4zp_g128", dict(top_k=8, n_global=16, expert_start=0, n_local=16), 8),   # 64 slots: fused align
+    ("int4zp_g128", dict(top_k=5, n_global=16, expert_start=0, n_local=16), 13),  # 65 slots: align kernel
+])
+def test_layer_edge_shapes(qtype, kw, M):
+    wl = W.small_workload(qtype).replace(**kw)
+    lw = W.make_weights(wl)
+    inp = W.make_inputs(wl, M)
+    announce(f"layer edge {qtype} {kw} M={M}")
+    got = _forward(make_layer(wl, lw), inp)
+    ref = oracle_layer(wl, lw, inp)
+    assert layer_violations(got, ref) == 0
+    assert rel_rms(got, ref) < 0.01
+
+
 # ----------------------------------------------------------------------------- full-size workloads
 _CACHE = {}
 
