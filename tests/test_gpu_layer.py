@@ -192,3 +192,30 @@ def test_small_layer_unfused_activation(qtype):
     got = _forward(layer, inp, fused_act=False)
     assert layer_violations(got, oracle_layer(wl, lw, inp)) == 0
     assert np.array_equal(got, _forward(layer, inp))      # fused and unfused give the same bytes
+
+
+@pytest.mark.parametrize("qtype,M", [("nvfp4_g16", 1), ("mxfp4_g32", 100), ("int4_g128", 300), ("int4zp_g128", 5)])
+def test_graph_replays_equal_eager_runs(qtype, M):
+    # the layer captured once in a HIP graph (as bench.py times it), then replayed on three different
+    # inputs copied into the captured tensors, eager work in between: every replay equals an eager run
+    wl = W.small_workload(qtype)
+    lw = W.make_weights(wl)
+    layer = make_layer(wl, lw)
+    announce(f"graph replay {qtype} M={M}")
+    x, ids, gw = W.device_inputs(W.make_inputs(wl, M, seed=500))
+    ws = layer.workspace(M, device=x.device)
+    layer(x, ids, gw, ws=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = layer(x, ids, gw, ws=ws)
+    torch.cuda.synchronize()
+    for seed in (501, 502, 503):
+        x2, ids2, gw2 = W.device_inputs(W.make_inputs(wl, M, seed=seed))
+        ref = layer(x2, ids2, gw2).clone()           # eager, its own workspace
+        x.copy_(x2)
+        ids.copy_(ids2)
+        gw.copy_(gw2)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
