@@ -11,7 +11,8 @@
 //   1. count:   LDS histogram cnt[w][e] (atomics only add; the totals do not depend on order)
 //   2. scan:    per expert, exclusive scan over the waves (a 16-lane segmented shuffle scan per
 //               expert) -> offset of wave w inside the expert's segment and the expert's total;
-//               padded totals scanned over experts -> segment starts
+//               padded totals scanned over experts -> segment starts (up to 64 experts: wave 0
+//               alone does both, one lane per expert, behind a single barrier)
 //   3. scatter: each wave walks its chunk in order, 64 slots at a time; the rank of a lane among
 //               the lanes of its batch with the same expert comes from ballots over the bits of
 //               the expert id (a wave multi-split), so the write position is
@@ -71,41 +72,67 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   }
   __syncthreads();
 
-  // per expert: exclusive scan of the waves' counts (wave order) and the total; lanes
-  // 16 j .. 16 j + 15 of a wave hold waves 0..15 of one expert
-  for (int base = 0; base < n_local * 16; base += kAlignThreads) {
-    const int i = base + tid, e = i >> 4, v = i & 15;
-    const int c = (e < n_local && v < nwv) ? cnt[v * n_local + e] : 0;
-    int x = c;
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) {
-      const int o = __shfl_up(x, d, 16);
-      if (v >= d) x += o;
+  if (n_local <= 64) {
+    // few experts: wave 0 alone, lane e = expert e -- its waves' counts in wave order (exclusive
+    // prefix) and total, then the padded totals scanned over the lanes; one barrier instead of three
+    if (w == 0) {
+      int t = 0;
+      if (lane < n_local)
+        for (int v = 0; v < nwv; ++v) {
+          const int c = cnt[v * n_local + lane];
+          cnt[v * n_local + lane] = t;
+          t += c;
+        }
+      const int p = lane < n_local ? (t + B - 1) / B * B : 0;
+      int incl = p;
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+      }
+      if (lane < n_local) {
+        tot[lane] = t;
+        seg[lane] = incl - p;
+      }
+      if (lane == n_local - 1) seg[n_local] = incl;
     }
-    if (e < n_local) {
-      if (v < nwv) cnt[v * n_local + e] = x - c;
-      if (v == 15) tot[e] = x;
-    }
-  }
-  __syncthreads();
-
-  // exclusive scan of the padded totals over experts (n_local <= 512 < threads)
-  {
-    const int p = tid < n_local ? (tot[tid] + B - 1) / B * B : 0;
-    int incl = p;
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
-    }
-    if (lane == 63) wave_sum[w] = incl;
     __syncthreads();
-    int before = 0;
-    for (int v = 0; v < w; ++v) before += wave_sum[v];
-    incl += before;
-    if (tid < n_local) seg[tid] = incl - p;
-    if (tid == n_local - 1) seg[n_local] = incl;
+  } else {
+    // per expert: exclusive scan of the waves' counts (wave order) and the total; lanes
+    // 16 j .. 16 j + 15 of a wave hold waves 0..15 of one expert
+    for (int base = 0; base < n_local * 16; base += kAlignThreads) {
+      const int i = base + tid, e = i >> 4, v = i & 15;
+      const int c = (e < n_local && v < nwv) ? cnt[v * n_local + e] : 0;
+      int x = c;
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) {
+        const int o = __shfl_up(x, d, 16);
+        if (v >= d) x += o;
+      }
+      if (e < n_local) {
+        if (v < nwv) cnt[v * n_local + e] = x - c;
+        if (v == 15) tot[e] = x;
+      }
+    }
+    __syncthreads();
+
+    // exclusive scan of the padded totals over experts (n_local <= 512 < threads)
+    {
+      const int p = tid < n_local ? (tot[tid] + B - 1) / B * B : 0;
+      int incl = p;
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+      }
+      if (lane == 63) wave_sum[w] = incl;
+      __syncthreads();
+      int before = 0;
+      for (int v = 0; v < w; ++v) before += wave_sum[v];
+      incl += before;
+      if (tid < n_local) seg[tid] = incl - p;
+      if (tid == n_local - 1) seg[n_local] = incl;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // scatter in slot order
   int nbits = 0;
