@@ -18,6 +18,8 @@ Sources (the four pages the method is described on):
   NVFP4 expert slice, ``expert_map`` routing, ``moe_align_block_size``, the
   two GEMMs, ``silu_and_mul`` and the post-expert-norm weighted sum
   (``_expert_norm_factors`` / ``_expert_norm_sum``).
+* "sglang PR 35760" summary on prhub.com.cn: the W4AFP8 per-token -> per-tensor
+  float8 requant of the dispatched activations (``oracle/requant.py``).
 
 Every function pinned by a test says what pins it; see ``tests/test_oracle*.py``.
 """

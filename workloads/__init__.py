@@ -254,3 +254,89 @@ def device_inputs(inp: LayerInputs, device="cuda") -> tuple:
 def bf16_to_float(t: torch.Tensor) -> np.ndarray:
     """A bf16 device tensor as float64 numpy (exact)."""
     return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+# ----------------------------------------------------------------------------- fp8 requant inputs
+# The W4AFP8 activation requant ("sglang PR 35760" summary): after the low-latency dispatch
+# expert e holds max_m row slots of K float8 e4m3fn values, the first masked_m[e] live, with
+# one float32 scale per row and 128-wide group.  Shapes follow the page: K = 7168 (56 groups of
+# 128, the DeepSeek-V3 hidden size its geometry tests use), 256 local experts with one row each
+# (the decode case it quotes), and a skew axis in which one hot expert takes `skew` times the
+# mean row count while the others share the rest, keeping the total fixed.
+REQUANT_GROUP = 128
+
+
+@dataclass(frozen=True)
+class RequantWorkload:
+    name: str
+    E: int              # local experts
+    K: int              # hidden size, a multiple of 128
+    rows: int           # mean live rows per expert
+    skew: int = 1       # the hot expert (index 0) takes skew * rows
+    max_m: int = 0      # row slots per expert (0: just enough for the hot expert)
+    seed: int = 0
+
+
+REQUANT_WORKLOADS = {w.name: w for w in [
+    RequantWorkload("requant_e256_k7168_rows1", 256, 7168, 1, max_m=8, seed=1),
+    RequantWorkload("requant_e32_k7168_rows32_skew16", 32, 7168, 32, skew=16, seed=2),
+    RequantWorkload("requant_e8_k7168_rows256", 8, 7168, 256, seed=3),
+]}
+REQUANT_HEADLINE = REQUANT_WORKLOADS["requant_e256_k7168_rows1"]
+
+
+def requant_counts(wl: RequantWorkload) -> np.ndarray:
+    """Live rows per expert (int32 [E]): uniform, or expert 0 hot with skew * rows and the
+    remainder shared as evenly as integers allow."""
+    total = wl.E * wl.rows
+    if wl.skew <= 1 or wl.E == 1:
+        return np.full(wl.E, wl.rows, dtype=np.int32)
+    hot = min(total, wl.skew * wl.rows)
+    rest = total - hot
+    c = np.full(wl.E - 1, rest // (wl.E - 1), dtype=np.int64)
+    c[: rest % (wl.E - 1)] += 1
+    return np.concatenate([[hot], c]).astype(np.int32)
+
+
+def requant_max_m(wl: RequantWorkload) -> int:
+    return wl.max_m or int(requant_counts(wl).max())
+
+
+@dataclass
+class RequantInputs:
+    x: np.ndarray            # uint8 [E, max_m, K] float8 e4m3fn codes (every slot filled)
+    scales: np.ndarray       # float32 [E, max_m, K/128] per row and group (logical order)
+    masked_m: np.ndarray     # int32 [E]
+    tensor_scale: np.float32
+
+
+def make_requant_inputs(E: int, max_m: int, K: int, masked_m, seed: int,
+                        tensor_scale_factor: float = 1.0) -> RequantInputs:
+    """Per-token-group quantised activations: values N(0, 1) times a log-normal row magnitude
+    with a few 20x outliers, each (row, group) scaled so that its largest magnitude maps to 448
+    and cast to float8 e4m3fn (torch's cast); the per-tensor scale is the largest group scale
+    times `tensor_scale_factor` (below 1 some values saturate)."""
+    assert K % REQUANT_GROUP == 0
+    G = K // REQUANT_GROUP
+    rng = _rng(seed, 0x5EC, _S_HIDDEN)
+    masked_m = np.asarray(masked_m, dtype=np.int32)
+    live = np.arange(max_m)[None, :] < np.clip(masked_m, 0, max_m)[:, None]
+    L = int(live.sum())
+    # rows that are not live hold arbitrary codes and scales (a kernel must neither use nor write them)
+    x = rng.integers(0, 256, size=(E, max_m, K), dtype=np.uint8)
+    scales = np.exp2(rng.uniform(-4, 4, size=(E, max_m, G))).astype(np.float32)
+    mag = np.exp(rng.normal(0.0, 0.5, size=(L, 1))).astype(np.float32)
+    a = rng.standard_normal((L, K), dtype=np.float32) * mag
+    a[rng.random((L, K), dtype=np.float32) < 1e-3] *= 20.0
+    g = a.reshape(L, G, REQUANT_GROUP)
+    amax = np.maximum(np.abs(g).max(axis=-1), np.float32(1e-6))
+    s_live = (amax / np.float32(448.0)).astype(np.float32)
+    x[live] = _to_e4m3_codes((g / s_live[..., None]).reshape(L, K))
+    scales[live] = s_live
+    ts = np.float32((s_live.max() if L else np.float32(1.0)) * np.float32(tensor_scale_factor))
+    return RequantInputs(x, scales, masked_m, ts)
+
+
+def requant_inputs_for(wl: RequantWorkload, tensor_scale_factor: float = 1.0) -> RequantInputs:
+    return make_requant_inputs(wl.E, requant_max_m(wl), wl.K, requant_counts(wl), wl.seed,
+                               tensor_scale_factor)
