@@ -1,6 +1,6 @@
 """Benchmark of the W4A16 MoE expert layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--M M] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--M M] [--no-cpu-baseline] [--sweep]
 
 A step is one pass of the whole layer (align -> gate/up GEMM -> activation -> down GEMM ->
 combine) over one batch of seeded synthetic inputs already resident in HBM.  The default
@@ -15,6 +15,11 @@ with HIP events on its launch stream around replays of a graph of back-to-back l
 arguments of a real step, and its algorithmic work per launch is the flops (prefill) or weight
 bytes (decode) it must process.  The CPU
 baseline is the float64 oracle on a bounded sample of the same workload on the host cores.
+
+The W4AFP8 activation requant (moe_fp8_requant) has workloads of its own (`--workload
+requant_...`, and in --sweep): its step is one launch over a masked [E, max_m, K] float8 batch,
+its roofline is HBM on the algorithmic bytes (live rows x (2K + 4K/128): codes read and written,
+group scales read), and its CPU baseline is the requant oracle.
 
 Prints one JSON line.  With --sweep, prints one JSON line per configuration cell instead.
 """
@@ -46,9 +51,12 @@ FLUSH_BYTES = 1 << 30          # read between cold steps: more than L2 + MALL
 LAUNCHES = 20                  # back-to-back launches per graph when timing one GEMM
 
 
-def gemm_source_hash() -> str:
+REQUANT_SRCS = ["moe_requant.hip", "moe_internal.h"]
+
+
+def gemm_source_hash(srcs=None) -> str:
     h = hashlib.sha256()
-    for f in GEMM_SRCS:
+    for f in srcs or GEMM_SRCS:
         h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -66,14 +74,14 @@ def weight_bytes_per_expert(wl, proj: str) -> int:
     return codes + scales + zeros + gs + bias
 
 
-def load_traffic(kernel: str, workload: str):
+def load_traffic(kernel: str, workload: str, srcs=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None if there
     is none for this kernel/workload or the kernel source changed since it was taken."""
     path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
-    if d.get("source_sha256_16") != gemm_source_hash():
+    if d.get("source_sha256_16") != gemm_source_hash(srcs):
         return None
     return d.get("bytes_per_launch")
 
@@ -256,6 +264,96 @@ def run_cell(name: str, M: int, steps: int, warmup: int, want_cpu: bool, seed=No
     return out
 
 
+def run_requant_cell(name: str, steps: int, warmup: int, want_cpu: bool) -> dict:
+    import torch
+    import workloads as W
+    from quantized_mixture_experts_align_amd import moe_fp8_requant, requant_choose
+
+    wl = W.REQUANT_WORKLOADS[name]
+    dev = torch.device("cuda", 0)
+    inp = W.requant_inputs_for(wl)
+    E, max_m, K = inp.x.shape
+    x = torch.from_numpy(inp.x).to(dev)
+    sc = torch.from_numpy(inp.scales).to(dev)
+    mm = torch.from_numpy(inp.masked_m).to(dev)
+    ts = torch.tensor([inp.tensor_scale], dtype=torch.float32, device=dev)
+    out = torch.empty_like(x)
+    rows = int(np.clip(inp.masked_m, 0, max_m).sum())
+    nbytes = rows * (2 * K + 4 * (K // W.REQUANT_GROUP))
+    # the launch hint from the rows the dispatch reports per expert, (rows + E) // E as in the page
+    cfg = requant_choose(E, max_m, K, expected_rows=(rows + E) // E)
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        moe_fp8_requant(x, sc, mm, ts, W.REQUANT_GROUP, out=out, cfg=cfg)
+    for _ in range(3):
+        launch()
+    torch.cuda.synchronize()
+    # value: a graph of LAUNCHES back-to-back launches, HIP events on the launch stream
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(LAUNCHES):
+            launch()
+    for _ in range(max(1, warmup // LAUNCHES)):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(5, steps // LAUNCHES)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / (reps * LAUNCHES)
+    # cold: one launch after reading 1 GiB through the caches, median over launches
+    flush = torch.ones(FLUSH_BYTES // 8, dtype=torch.int64, device=dev)
+    cold = []
+    for _ in range(max(50, min(steps, 200))):
+        flush.sum()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        launch()
+        s1.record(stream)
+        cold.append((s0, s1))
+    torch.cuda.synchronize()
+    cold_s = float(np.median([a.elapsed_time(b) for a, b in cold])) * 1e-3
+    del flush
+    ach = nbytes / t / 1e9
+    r = {
+        "metric": "fp8 requant GB/s (algorithmic bytes) vs HBM roofline", "value": round(ach, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": reps * LAUNCHES, "warmup": warmup,
+        "ms_per_step": round(t * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3fn/f32", "data": "synthetic",
+        "config": {"workload": wl.name, "E": E, "max_m": max_m, "K": K, "live_rows": rows,
+                   "group": W.REQUANT_GROUP, "expected_rows": (rows + E) // E,
+                   "workgroups": cfg.workgroups, "unroll": cfg.unroll},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(ach / PEAK_HBM_GBS, 4), "kernel": "requant_kernel",
+                     "traffic": load_traffic("requant_kernel", wl.name, REQUANT_SRCS), "avg_launch_us": round(t * 1e6, 3),
+                     "bytes_per_launch": nbytes},
+        "cold": {"us_per_launch": round(cold_s * 1e6, 3), "GBps": round(nbytes / cold_s / 1e9, 1),
+                 "frac": round(nbytes / cold_s / 1e9 / PEAK_HBM_GBS, 4), "launches": len(cold),
+                 "note": "median single launch after reading 1 GiB"},
+    }
+    if want_cpu:
+        r["cpu_baseline"] = requant_cpu_baseline(inp, nbytes)
+    return r
+
+
+def requant_cpu_baseline(inp, nbytes: int, budget_s: float = 10.0) -> dict:
+    from oracle import requant as R
+    t0 = time.perf_counter()
+    R.requant(inp.x, inp.scales, inp.masked_m, inp.tensor_scale)
+    one = time.perf_counter() - t0
+    reps = max(1, int(budget_s / max(one, 1e-3)))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        R.requant(inp.x, inp.scales, inp.masked_m, inp.tensor_scale)
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes * reps / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"numpy requant oracle (single-threaded), the whole batch, {reps} runs, {dt:.1f} s wall"}
+
+
 def layer_fracs(nbytes: float, flops: float, t: float) -> dict:
     """Fractions of the MI355X roofline reached by a whole step: of HBM peak on the touched
     weight bytes, of dense bf16 MFMA peak on the live-slot flops, and of the binding bound
@@ -313,8 +411,13 @@ def main() -> int:
             for M in wl.Ms:
                 r = run_cell(name, M, a.steps, a.warmup, False)
                 print(json.dumps(r), flush=True)
+        for name in W.REQUANT_WORKLOADS:
+            print(json.dumps(run_requant_cell(name, a.steps, a.warmup, False)), flush=True)
         return 0
     name = a.workload or W.HEADLINE
+    if name in W.REQUANT_WORKLOADS:
+        print(json.dumps(run_requant_cell(name, a.steps, a.warmup, not a.no_cpu_baseline)), flush=True)
+        return 0
     if name not in W.WORKLOADS:
         print(f"unknown workload {name!r}; one of {list(W.WORKLOADS)}", file=sys.stderr)
         return 2

@@ -11,6 +11,9 @@
  *   moe_combine      out[t] = sum over live slots of g * y, optionally after the
  *                    weight-first post-expert RMSNorm with weight bf16(1 + w)
  *
+ * and, for the W4AFP8 variant of the expert path, moe_fp8_requant: float8 activations
+ * quantised per token and group re-expressed against one per-tensor scale.
+ *
  * Sources.  The steps and their arguments follow the pages the method is described on:
  * the Muse Spark NVFP4 experiment "013-moe-middle-tiles.py" (bishal.us open-kernel-challenge):
  * Inputs / Weights / Config, prepare and kernel_fn (expert_map, moe_align_block_size, two
@@ -291,6 +294,62 @@ int moe_act(moe_act_kind kind, const uint16_t* in, int32_t ld_in, uint16_t* out,
 int moe_combine(const uint16_t* y, const float* topk_weights, const int32_t* slot_local_ids,
                 const uint16_t* norm_w, float eps, float routed_scaling_factor, int64_t M,
                 int32_t top_k, int32_t H, uint16_t* out, hipStream_t stream);
+
+/* ----------------------------------------------------------------------------- fp8 requant */
+
+/*
+ * Launch hint of moe_fp8_requant (results never depend on it).
+ *   workgroups  >= 1 workgroups of four waves; each wave takes every (workgroups*4)-th item
+ *   unroll      work items in flight per wave: 1, 2 or 4
+ */
+typedef struct {
+  int32_t workgroups;
+  int32_t unroll;
+} moe_requant_config;
+
+/*
+ * A launch hint for moe_fp8_requant on E experts of max_m row slots of K codes, a device with
+ * num_cus compute units, and expected_rows live rows per expert (the dispatch's expected_m of
+ * the "sglang PR 35760" summary, item 4; <= 0 = unknown: every row slot is assumed live, which
+ * is what moe_fp8_requant uses when cfg is NULL).  About two 1024-byte items per wave as two,
+ * four or eight workgroups per CU, never more waves than the batch can have items; a wave takes
+ * two or four items at a time beyond that.  Any value is correct: only speed depends on it.  A pure host
+ * function.  Errors: MOE_EINVAL for a null cfg or E, max_m < 0, K < 16, num_cus < 1.
+ */
+int moe_fp8_requant_choose(int32_t E, int32_t max_m, int32_t K, int32_t expected_rows,
+                           int32_t num_cus, moe_requant_config* cfg);
+
+/*
+ * W4AFP8 activation requant ("sglang PR 35760" summary: "Feature and motivation",
+ * "Implementation breakdown" items 1-3): float8 e4m3fn activations quantised per token and
+ * group are re-expressed against one per-tensor scale.  For every live element
+ *     out = e4m3fn_sat( float32( float32(x * s) * r ) ),   r = float32(1 / *tensor_scale)
+ * with x the decoded code, s its (row, group) scale, and e4m3fn_sat rounding to nearest (ties
+ * to the even code) after clamping the magnitude to 448, keeping the sign (-0 -> 0x80) and
+ * sending NaN to 0x7F.
+ *   x             device uint8 [E, max_m, K]: e4m3fn codes, row m of expert e live iff
+ *                 m < clamp(masked_m[e], 0, max_m)
+ *   scales        device fp32; the scale of (e, m, group g = k / group_size) is
+ *                 scales[e*scale_stride_e + m*scale_stride_m + g*scale_stride_g] (elements):
+ *                 row-major [E, max_m, K/group_size] is (max_m*G, G, 1); the column-major
+ *                 per-expert layout [E, K/group_size, max_m] of a DeepEP dispatch is (G*max_m, 1, max_m)
+ *   masked_m      device int32 [E]: live rows per expert (values outside [0, max_m] are clamped)
+ *   tensor_scale  device fp32 [1]: the per-tensor scale
+ *   group_size    a multiple of 16 dividing K (128 on the page)
+ *   out           device uint8 [E, max_m, K]: live rows written; every other row slot is left
+ *                 untouched.  out == x (in place) is allowed; any other overlap is rejected.
+ *   cfg           launch hint or NULL (moe_fp8_requant_choose)
+ * Nothing is read or written for row slots that are not live, so their contents are free.
+ * E = 0 or max_m = 0 launches nothing.  Errors: MOE_EINVAL for null pointers, x/out not 16-byte
+ * aligned, K not a positive multiple of group_size, negative strides, a bad cfg, or a partial
+ * overlap; MOE_EUNSUPPORTED for group_size not a multiple of 16, more than 1024 experts or
+ * E*max_m*ceil(K/1024) >= 2^31.
+ */
+int moe_fp8_requant(const uint8_t* x, const float* scales, int64_t scale_stride_e,
+                    int64_t scale_stride_m, int64_t scale_stride_g, const int32_t* masked_m,
+                    const float* tensor_scale, int32_t E, int32_t max_m, int32_t K,
+                    int32_t group_size, uint8_t* out, const moe_requant_config* cfg,
+                    hipStream_t stream);
 
 #ifdef __cplusplus
 }

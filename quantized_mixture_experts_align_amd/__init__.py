@@ -8,12 +8,13 @@ from . import _lib
 from .ops import (align_capacity, choose_block_m, gemm_choose, gemm_config, moe_act, moe_align,
                   moe_combine, moe_norm_weight, moe_w4a16_gemm, moe_w4a16_gemm_act,
                   moe_w4a16_gemm_act_routed, moe_w4a16_prepare, prepared_size,
-                  PreparedWeights)
+                  PreparedWeights, moe_fp8_requant, requant_choose, requant_config)
 from .layer import MoELayer, Workspace
 
 __all__ = [
     "align_capacity", "choose_block_m", "gemm_choose", "gemm_config", "moe_act", "moe_align",
     "moe_combine", "moe_norm_weight", "moe_w4a16_gemm", "moe_w4a16_gemm_act",
     "moe_w4a16_gemm_act_routed", "moe_w4a16_prepare", "prepared_size",
-    "PreparedWeights", "MoELayer", "Workspace",
+    "PreparedWeights", "MoELayer", "Workspace", "moe_fp8_requant", "requant_choose",
+    "requant_config",
 ]

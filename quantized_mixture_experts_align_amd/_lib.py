@@ -32,6 +32,10 @@ class MoeGemmConfig(C.Structure):
                 ("gemv_rows", C.c_int32), ("group_m", C.c_int32)]
 
 
+class MoeRequantConfig(C.Structure):
+    _fields_ = [("workgroups", C.c_int32), ("unroll", C.c_int32)]
+
+
 class MoeError(RuntimeError):
     pass
 
@@ -58,6 +62,9 @@ SIGNATURES = {
                                             C.POINTER(MoeGemmConfig), _P]),
     "moe_act": (C.c_int, [C.c_int, _P, _I32, _P, _I32, _I64, _I32, _P, _F, _F, _P]),
     "moe_combine": (C.c_int, [_P, _P, _P, _P, _F, _F, _I64, _I32, _I32, _P, _P]),
+    "moe_fp8_requant_choose": (C.c_int, [_I32, _I32, _I32, _I32, _I32, C.POINTER(MoeRequantConfig)]),
+    "moe_fp8_requant": (C.c_int, [_P, _P, _I64, _I64, _I64, _P, _P, _I32, _I32, _I32, _I32, _P,
+                                  C.POINTER(MoeRequantConfig), _P]),
 }
 
 _lib = None

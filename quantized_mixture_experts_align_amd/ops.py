@@ -238,3 +238,51 @@ def moe_combine(y: torch.Tensor, topk_weights: torch.Tensor, slot_local_ids: tor
     L.check(L.lib().moe_combine(_ptr(y), _ptr(topk_weights), _ptr(slot_local_ids), _ptr(norm_w), eps,
                                 routed_scaling_factor, M, k, H, _ptr(out), _stream()), "moe_combine")
     return out
+
+
+def requant_choose(E: int, max_m: int, K: int, expected_rows: int = 0, num_cus: int = 0) -> L.MoeRequantConfig:
+    """Launch hint for moe_fp8_requant; expected_rows = live rows per expert if known (0 = not)."""
+    c = L.MoeRequantConfig()
+    if num_cus <= 0:
+        num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    L.check(L.lib().moe_fp8_requant_choose(E, max_m, K, expected_rows, num_cus, C.byref(c)),
+            "moe_fp8_requant_choose")
+    return c
+
+
+def requant_config(workgroups: int, unroll: int) -> L.MoeRequantConfig:
+    return L.MoeRequantConfig(workgroups, unroll)
+
+
+def moe_fp8_requant(x: torch.Tensor, scales: torch.Tensor, masked_m: torch.Tensor,
+                    tensor_scale: torch.Tensor, group_size: int = 128,
+                    out: Optional[torch.Tensor] = None,
+                    cfg: Optional[L.MoeRequantConfig] = None) -> torch.Tensor:
+    """x uint8 [E, max_m, K] (float8 e4m3fn codes; a float8_e4m3fn tensor is viewed as bytes);
+    scales float32 [E, max_m, K/group_size], any strides (a transposed view of a column-major
+    [E, K/group_size, max_m] array is passed as is); masked_m int32 [E]; tensor_scale float32 [1].
+    Returns out (uint8, same shape as x): live rows requantised, other rows untouched."""
+    if x.dtype == torch.float8_e4m3fn:
+        x = x.view(torch.uint8)
+    _need(x, torch.uint8, "x")
+    _need(masked_m, torch.int32, "masked_m")
+    _need(tensor_scale, torch.float32, "tensor_scale")
+    if not scales.is_cuda or scales.dtype != torch.float32 or scales.dim() != 3:
+        raise ValueError("scales must be a float32 device tensor [E, max_m, K/group_size]")
+    E, max_m, K = x.shape
+    if tuple(scales.shape) != (E, max_m, K // group_size) or tuple(masked_m.shape) != (E,):
+        raise ValueError(f"shapes: x {tuple(x.shape)}, scales {tuple(scales.shape)}, "
+                         f"masked_m {tuple(masked_m.shape)} do not match group_size {group_size}")
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.dtype == torch.float8_e4m3fn:
+        out = out.view(torch.uint8)
+    _need(out, torch.uint8, "out")
+    if tuple(out.shape) != tuple(x.shape):
+        raise ValueError(f"out {tuple(out.shape)} must have the shape of x {tuple(x.shape)}")
+    se, sm, sg = scales.stride()
+    L.check(L.lib().moe_fp8_requant(_ptr(x), _ptr(scales), se, sm, sg, _ptr(masked_m), _ptr(tensor_scale),
+                                    E, max_m, K, group_size, _ptr(out),
+                                    None if cfg is None else C.byref(cfg), _stream()),
+            "moe_fp8_requant")
+    return out

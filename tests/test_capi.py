@@ -165,3 +165,61 @@ def test_gemm_choose_tiles_for_streamed_prefill_weights():
     assert ng("nvfp4_g16", 8192, 4096, 32, L.PREP_GATE_UP, numel=1479) == 2
     assert ng("int4_g128", 2048, 512, 8, L.PREP_GATE_UP, numel=4608) == 2
     assert ng("int4zp_g128", 2048, 512, 8, L.PREP_GATE_UP, numel=4608) == 2
+
+
+def test_requant_choose_contract():
+    lib = L.lib()
+
+    def choose(E, max_m, K, expected=0, cus=256):
+        c = L.MoeRequantConfig()
+        assert lib.moe_fp8_requant_choose(E, max_m, K, expected, cus, C.byref(c)) == 0
+        return c.workgroups, c.unroll
+
+    for E, max_m, K in [(256, 8, 7168), (32, 512, 7168), (8, 256, 7168), (1, 1, 128), (1024, 3, 256),
+                        (256, 4096, 7168)]:
+        chunks = -(-K // 1024)
+        prev = 0
+        for expected in (0, 1, 2, 8, 33, 257, 10 ** 6):
+            wg, u = choose(E, max_m, K, expected)
+            rows = max_m if expected <= 0 else min(expected, max_m)
+            items = max(1, E * rows * chunks)
+            assert 1 <= wg <= 8 * 256 and u in (1, 2, 4)
+            assert (wg - 1) * 4 < max(1, E * max_m * chunks)    # no workgroup without a possible item
+            assert wg * 4 * u * 2 >= items or wg == 8 * 256     # about two items per wave
+            assert wg in (512, 1024, 2048) or (wg - 1) * 4 < E * max_m * chunks <= wg * 4   # 2, 4, 8 per CU
+            if expected > 0:
+                assert wg >= prev                                # more rows, never a smaller grid
+                prev = wg
+        assert choose(E, max_m, K, 0) == choose(E, max_m, K, max_m)   # unknown = every slot live
+        assert choose(E, max_m, K, 10 ** 6) == choose(E, max_m, K, max_m)
+    assert choose(256, 8, 7168, 2) == (512, 1)                   # sparse decode rows: 2 per CU
+    assert choose(256, 4096, 7168, 0)[1] == 4
+    c = L.MoeRequantConfig()
+    assert lib.moe_fp8_requant_choose(-1, 8, 7168, 0, 256, C.byref(c)) == L.MOE_EINVAL
+    assert lib.moe_fp8_requant_choose(8, 8, 7168, 0, 256, None) == L.MOE_EINVAL
+
+
+def test_requant_rejects_bad_arguments_before_launch():
+    lib = L.lib()
+    fake = 1 << 20   # never dereferenced: every call below fails on the host
+    cfg = L.MoeRequantConfig(4, 2)
+    args = dict(x=fake, s=fake, se=16, sm=2, sg=1, m=fake, t=fake, E=8, max_m=8, K=256, g=128, out=fake * 4)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.moe_fp8_requant(a["x"], a["s"], a["se"], a["sm"], a["sg"], a["m"], a["t"], a["E"],
+                                   a["max_m"], a["K"], a["g"], a["out"], C.byref(a.get("cfg", cfg)), None)
+
+    assert call(E=-1) == L.MOE_EINVAL
+    assert call(E=1025) == L.MOE_EUNSUPPORTED
+    assert call(g=8, K=256) == L.MOE_EUNSUPPORTED
+    assert call(K=200) == L.MOE_EINVAL                 # not a multiple of the group
+    assert call(x=0) == L.MOE_EINVAL                   # null pointer
+    assert call(x=fake + 8) == L.MOE_EINVAL            # not 16-byte aligned
+    assert call(sg=-1) == L.MOE_EINVAL
+    assert call(out=fake + 1024) == L.MOE_EINVAL       # partial overlap with x
+    assert call(cfg=L.MoeRequantConfig(0, 1)) == L.MOE_EINVAL
+    assert call(cfg=L.MoeRequantConfig(1, 3)) == L.MOE_EINVAL
+    assert call(E=1 << 12, max_m=1 << 20) == L.MOE_EUNSUPPORTED
+    assert "moe_fp8_requant" in lib.moe_last_error().decode()
+    assert call(E=0) == L.MOE_OK and call(max_m=0) == L.MOE_OK   # nothing to launch
