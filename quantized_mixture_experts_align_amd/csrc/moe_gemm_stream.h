@@ -107,8 +107,10 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   __shared__ int f_nblk;
   const int nblocks = FA ? fused_align(a, f_rows, f_be, &f_nblk) : *a.ntpp / B;
   const int items = nblocks * NS;
-  const int per = (items + (int)gridDim.x - 1) / (int)gridDim.x;  // <= kWin by the launch
-  const int i0 = (int)blockIdx.x * per, i1 = min(items, i0 + per);
+  // items split evenly over the whole grid (every workgroup gets floor or ceil of the mean, at
+  // most kWin by the launch), so that no workgroup idles while others take an extra item
+  const int i0 = (int)((int64_t)blockIdx.x * items / (int)gridDim.x);
+  const int i1 = (int)((int64_t)(blockIdx.x + 1) * items / (int)gridDim.x);
   if (i0 >= i1) return;
   const int kt0 = KT * w / KS, kt1 = KT * (w + 1) / KS, L = kt1 - kt0;  // L >= 1: KT >= KS
   const int m = lane & 15, j8 = 8 * (lane >> 4);
