@@ -131,18 +131,17 @@ extern "C" int moe_gemm_choose(const moe_weights* W, int64_t numel, int32_t bloc
     // prefill: with 128-row blocks four 16-row tiles per wave (the dequantised weights then
     // feed 32 MFMAs per k-step), else two; one when the grid would not cover the CUs twice.
     // With 64-row blocks and a long K (the weights stream from HBM through long K loops) four
-    // tiles as well, except for a gate/up pair whose dequantisation is not cheap (VALU-bound
-    // with four).  Measured on the int4, NVFP4 and MXFP4 prefill shapes: MXFP4 M=2048 gate/up
-    // 565 -> 428 us and down 291 -> 242 us, NVFP4 M=256 down 163 -> 141 us; NVFP4 gate/up and
-    // the int4 GEMMs (K <= 1024) are faster with two.
+    // tiles as well.  Measured on the int4, NVFP4 and MXFP4 prefill shapes: MXFP4 M=2048 gate/up
+    // 565 -> 428 us and down 291 -> 242 us, NVFP4 M=256 down 163 -> 141 us and gate/up
+    // 271 -> 232 us, NVFP4 M=1024 (64-row blocks) gate/up 583 -> 507 us; the int4 GEMMs
+    // (K <= 1024) are faster with two.
     c.kernel = MOE_GEMM_MFMA;
     const int64_t mblocks = numel / block_m + std::min<int64_t>(numel, W->n_experts);
-    const bool streamed = block_m >= 64 && W->K >= 2048 &&
-                          (W->qtype == MOE_Q_MXFP4_G32 || !(W->flags & MOE_PREP_GATE_UP));
+    const bool streamed = block_m >= 64 && W->K >= 2048;
     c.ng = 2;
     if ((block_m >= 128 || streamed) && ((int64_t)(nt + 15) / 16) * mblocks >= 2 * num_cus) c.ng = 4;
     if (((int64_t)(nt + 7) / 8) * mblocks < 2 * num_cus) c.ng = 1;
-    c.group_m = default_group_m(W->K);
+    c.group_m = default_group_m(W->K, block_m);
   }
   *cfg = c;
   return ok();

@@ -51,10 +51,11 @@ inline __host__ __device__ size_t align256(size_t x) { return (x + 255) & ~(size
 
 // MFMA GEMM: align blocks per XCD workgroup group (launch order only, never results).  With a
 // short K (<= 1024) a workgroup is brief and an expert's whole weight set fits an XCD's L2, so
-// eight consecutive blocks -- mostly one expert's -- share one XCD; with a long K the weights
-// stream anyway and one block per group spreads the work evenly (measured: int4 layers 5-10%
-// faster with 8, NVFP4/MXFP4 prefill within noise or slower).
-inline int default_group_m(int K) { return K <= 1024 ? 8 : 1; }
+// eight consecutive blocks -- mostly one expert's -- share one XCD (measured: int4 layers 5-10%
+// faster than with 1).  With a long K the weights stream from HBM: two consecutive 64-slot blocks
+// per XCD let a pair share each weight fetch through one L2 (measured: NVFP4 and MXFP4 prefill
+// GEMMs 0.5-6% faster than 1, 4 and 8 are slower); 128-slot blocks keep 1.
+inline int default_group_m(int K, int block_m) { return K <= 1024 ? 8 : (block_m == 64 ? 2 : 1); }
 
 // ---------------------------------------------------------------------------- device math
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

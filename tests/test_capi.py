@@ -154,17 +154,19 @@ def test_gemm_choose_contract(N, K, E):
 
 
 def test_gemm_choose_tiles_for_streamed_prefill_weights():
-    # 64-slot blocks: four tiles per wave when K is long and the dequantisation cheap (MXFP4) or the
-    # projection is not a gate/up pair; two for an NVFP4 gate/up pair and for short K (int4 shapes)
-    def ng(q, N, K, E, flags, numel=8192, B=64):
+    # 64-slot blocks: four tiles per wave when K is long (the weights stream from HBM), two for
+    # short K (int4 shapes); XCD groups of 8 blocks for short K, 2 for long K at 64 slots, else 1
+    def cfg(q, N, K, E, flags, numel=8192, B=64):
         W = P.PreparedWeights(None, L.MoeWeights(L.QTYPE[q], E, N, K, N, K, flags, 0, 1, 1, None, None))
-        return P.gemm_choose(W, numel, B, 256).ng
-    assert ng("mxfp4_g32", 5760, 2880, 128, L.PREP_GATE_UP) == 4
-    assert ng("mxfp4_g32", 2880, 2880, 128, 0) == 4
-    assert ng("nvfp4_g16", 4096, 4096, 32, 0, numel=1479) == 4
-    assert ng("nvfp4_g16", 8192, 4096, 32, L.PREP_GATE_UP, numel=1479) == 2
-    assert ng("int4_g128", 2048, 512, 8, L.PREP_GATE_UP, numel=4608) == 2
-    assert ng("int4zp_g128", 2048, 512, 8, L.PREP_GATE_UP, numel=4608) == 2
+        c = P.gemm_choose(W, numel, B, 256)
+        return c.ng, c.group_m
+    assert cfg("mxfp4_g32", 5760, 2880, 128, L.PREP_GATE_UP) == (4, 2)
+    assert cfg("mxfp4_g32", 2880, 2880, 128, 0) == (4, 2)
+    assert cfg("nvfp4_g16", 4096, 4096, 32, 0, numel=1479) == (4, 2)
+    assert cfg("nvfp4_g16", 8192, 4096, 32, L.PREP_GATE_UP, numel=1479) == (4, 2)
+    assert cfg("nvfp4_g16", 8192, 4096, 32, L.PREP_GATE_UP, numel=23283, B=128) == (4, 1)
+    assert cfg("int4_g128", 2048, 512, 8, L.PREP_GATE_UP, numel=4608) == (2, 8)
+    assert cfg("int4zp_g128", 2048, 512, 8, L.PREP_GATE_UP, numel=4608) == (2, 8)
 
 
 def test_requant_choose_contract():
