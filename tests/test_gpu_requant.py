@@ -170,6 +170,42 @@ def test_results_do_not_depend_on_the_launch_geometry():
         assert np.array_equal(got, ref), (wg, u)
 
 
+def test_graph_replays_on_new_inputs():
+    # one launch captured in a HIP graph, replayed on three different batches copied into the same
+    # buffers, with eager work between the replays: every replay equals the oracle
+    from quantized_mixture_experts_align_amd import moe_fp8_requant
+    E, max_m, K = 24, 6, 2048
+    x = torch.empty((E, max_m, K), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((E, max_m, K // 128), dtype=torch.float32, device="cuda")
+    mm = torch.empty(E, dtype=torch.int32, device="cuda")
+    ts = torch.empty(1, dtype=torch.float32, device="cuda")
+    out = torch.full_like(x, SENTINEL)
+    batches = []
+    for seed in range(4):
+        rng = np.random.default_rng(100 + seed)
+        inp = W.make_requant_inputs(E, max_m, K, rng.integers(0, max_m + 1, size=E), seed=100 + seed)
+        batches.append(inp)
+    def load(inp):
+        x.copy_(torch.from_numpy(inp.x)); sc.copy_(torch.from_numpy(inp.scales))
+        mm.copy_(torch.from_numpy(inp.masked_m)); ts.fill_(float(inp.tensor_scale))
+        out.fill_(SENTINEL)
+    load(batches[0])
+    moe_fp8_requant(x, sc, mm, ts, out=out)          # eager warm-up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe_fp8_requant(x, sc, mm, ts, out=out)
+    for inp in batches[1:]:
+        load(inp)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        want, live = R.requant(inp.x, inp.scales, inp.masked_m, inp.tensor_scale)
+        assert np.array_equal(got[live], want[live])
+        assert (got[~live] == SENTINEL).all()
+
+
 def test_rejects_bad_arguments():
     from quantized_mixture_experts_align_amd import moe_fp8_requant, requant_config
     x = torch.zeros((2, 3, 256), dtype=torch.uint8, device="cuda")
