@@ -28,7 +28,11 @@ design notes of the repository):
   the Marlin MoE call in sglang PR 31552, used with integer zero points): unsigned
   codes, one integer zero point 0..15 and one bf16 scale per group of 128 along K,
   stored one zero point per byte in ``[N, K/128]`` like the scales; the weight is
-  ``(u - z) * s``.
+  ``(u - z) * s``;
+* act-order int4 (the ``g_idx1`` / ``g_idx2`` arguments of that call; the pages pass the
+  setup's result through without defining it): ``g_idx[k]`` names the group of 128 whose
+  scale (and zero point) input column ``k`` uses; every group holds 128 columns, in any
+  order (the GPTQ ``desc_act`` grouping).
 """
 from __future__ import annotations
 
@@ -107,27 +111,35 @@ def _nibbles(codes: np.ndarray) -> np.ndarray:
 
 
 def dequant(qtype: str, codes: np.ndarray, scales: np.ndarray, gs: Optional[float] = None,
-            zeros: Optional[np.ndarray] = None) -> np.ndarray:
+            zeros: Optional[np.ndarray] = None, g_idx: Optional[np.ndarray] = None) -> np.ndarray:
     """Dense float64 [N, K] weight of one expert.
 
-    * int4_g128: ``(u - 8) * s[n, k // 128]`` with bf16 ``s`` (uint4b8, group 128).
-    * int4zp_g128: ``(u - z[n, k // 128]) * s[n, k // 128]``, unsigned ``u``, integer
+    * int4_g128: ``(u - 8) * s[n, G(k)]`` with bf16 ``s`` (uint4b8, group 128).
+    * int4zp_g128: ``(u - z[n, G(k)]) * s[n, G(k)]``, unsigned ``u``, integer
       zero point ``z`` in 0..15, bf16 ``s`` (asymmetric int4, group 128).
     * nvfp4_g16: ``e2m1 * e4m3[n, k // 16] * gs`` (one fp32 global scale per
       expert and projection, as the experiment's ``_marlin_layer`` passes it).
     * mxfp4_g32: ``e2m1 * 2^(E[n, k // 32] - 127)``.
-    Pinned by constant-code closed forms and a tiny brute-force matmul.
+    ``G(k) = k // 128``, or with act-order ``G(k) = g_idx[k]`` (the ``g_idx`` of the Marlin MoE
+    call in sglang PR 31552: the quantisation group of input column ``k``, each group holding
+    128 columns in any order; int4 formats only).
+    Pinned by constant-code closed forms, a tiny brute-force matmul and, for act-order, the
+    plain path on the column-sorted weights.
     """
     q = _nibbles(codes)
     g = _GROUP[qtype]
+    if g_idx is not None and qtype not in ("int4_g128", "int4zp_g128"):
+        raise ValueError("act-order (g_idx) is defined for the int4 formats only")
+    K = q.shape[-1]
+    grp = (np.arange(K) // g) if g_idx is None else np.asarray(g_idx, dtype=np.int64)
     if qtype == "int4_g128":
         s = decode_bf16(scales)
-        return decode_uint4b8(q) * np.repeat(s, g, axis=-1)
+        return decode_uint4b8(q) * s[..., grp]
     if qtype == "int4zp_g128":
         if zeros is None:
             raise ValueError("asymmetric int4 needs the zero points")
         z = np.asarray(zeros, dtype=np.float64)
-        return (decode_uint4(q) - np.repeat(z, g, axis=-1)) * np.repeat(decode_bf16(scales), g, axis=-1)
+        return (decode_uint4(q) - z[..., grp]) * decode_bf16(scales)[..., grp]
     if qtype == "nvfp4_g16":
         if gs is None:
             raise ValueError("NVFP4 needs the per-expert global scale")
@@ -251,6 +263,11 @@ def combine(Y: np.ndarray, topk_weights: np.ndarray, slot_local: np.ndarray,
 
 
 # ----------------------------------------------------------------------------- layer
+def _gidx_of(w, e):
+    g = getattr(w, "g_idx", None)
+    return None if g is None else g[e]
+
+
 def _zeros_of(w, e):
     z = getattr(w, "zeros", None)
     return None if z is None else z[e]
@@ -264,8 +281,8 @@ def moe_layer(qtype: str, x_bits: np.ndarray, topk_ids: np.ndarray, topk_weights
     """The whole expert layer for one GPU's expert slice.
 
     ``w13`` / ``w2`` carry ``codes``, ``scales``, ``gs`` (or None), ``bias``
-    (or None) and, for asymmetric int4, ``zeros`` for the ``n_local`` local experts in
-    the canonical layouts.
+    (or None), for asymmetric int4 ``zeros`` and, for act-order int4, ``g_idx`` (int
+    ``[E, K]``) for the ``n_local`` local experts in the canonical layouts.
     ``tokens`` restricts the evaluation to a subset of tokens (each token's
     output depends only on its own slots), returning rows in that order.
     """
@@ -284,8 +301,9 @@ def moe_layer(qtype: str, x_bits: np.ndarray, topk_ids: np.ndarray, topk_weights
         if rows.size == 0:
             continue
         W13 = dequant(qtype, w13.codes[e], w13.scales[e], None if w13.gs is None else w13.gs[e],
-                      _zeros_of(w13, e))
-        W2 = dequant(qtype, w2.codes[e], w2.scales[e], None if w2.gs is None else w2.gs[e], _zeros_of(w2, e))
+                      _zeros_of(w13, e), _gidx_of(w13, e))
+        W2 = dequant(qtype, w2.codes[e], w2.scales[e], None if w2.gs is None else w2.gs[e], _zeros_of(w2, e),
+                     _gidx_of(w2, e))
         b13 = None if w13.bias is None else decode_bf16(w13.bias[e])
         b2 = None if w2.bias is None else decode_bf16(w2.bias[e])
         r = expert_forward(x[tok[rows // k]], W13, b13, W2, b2, act, alpha, limit,

@@ -43,11 +43,13 @@ def _const_proj(n_rows_codes, K, scale_code, dtype_scale, group, gs=None, bias=N
 
 
 # ----------------------------------------------------------------------------- dequant
-def _brute_dequant_matvec(qtype, codes, scales, gs, x, zeros=None):
+def _brute_dequant_matvec(qtype, codes, scales, gs, x, zeros=None, g_idx=None):
     """Per-element reading of the packed layout, independent of the oracle's
-    vectorised unpack: byte k//2 of row n, low nibble for even k."""
+    vectorised unpack: byte k//2 of row n, low nibble for even k; with act-order the group of
+    column k is g_idx[k] instead of k // 128."""
     N, Kh = codes.shape
     K = Kh * 2
+    grp = [k // 128 for k in range(K)] if g_idx is None else [int(v) for v in g_idx]
     e4m3 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().tolist()
     out = []
     for n in range(N):
@@ -56,11 +58,11 @@ def _brute_dequant_matvec(qtype, codes, scales, gs, x, zeros=None):
             byte = int(codes[n, k // 2])
             u = (byte >> 4) if (k & 1) else (byte & 0xF)
             if qtype == "int4_g128":
-                s = struct.unpack("<f", struct.pack("<I", int(scales[n, k // 128]) << 16))[0]
+                s = struct.unpack("<f", struct.pack("<I", int(scales[n, grp[k]]) << 16))[0]
                 w = (u - 8) * s
             elif qtype == "int4zp_g128":
-                s = struct.unpack("<f", struct.pack("<I", int(scales[n, k // 128]) << 16))[0]
-                w = (u - int(zeros[n, k // 128])) * s
+                s = struct.unpack("<f", struct.pack("<I", int(scales[n, grp[k]]) << 16))[0]
+                w = (u - int(zeros[n, grp[k]])) * s
             else:
                 sign = -1.0 if u & 8 else 1.0
                 e, m = (u >> 1) & 3, u & 1
@@ -96,6 +98,75 @@ def test_dequant_matches_per_element_brute_force(qtype, N, K):
     got = O.dequant(qtype, codes, scales, gs, zeros) @ x
     ref = _brute_dequant_matvec(qtype, codes, scales, gs, x, zeros)
     assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def _pack_nibbles(q):
+    """[..., K] nibbles -> [..., K/2] bytes, low nibble = even k."""
+    q = np.asarray(q, dtype=np.uint8)
+    return (q[..., 0::2] | (q[..., 1::2] << 4)).astype(np.uint8)
+
+
+def _act_order_case(qtype, N, K, seed):
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = W._to_bf16_bits(rng.uniform(0.002, 0.02, (N, K // 128)).astype(np.float32))
+    zeros = rng.integers(0, 16, size=(N, K // 128), dtype=np.uint8) if qtype == "int4zp_g128" else None
+    g_idx = W.make_g_idx(rng, 1, K)[0]
+    return codes, scales, zeros, g_idx
+
+
+@pytest.mark.parametrize("qtype", ["int4_g128", "int4zp_g128"])
+def test_dequant_act_order_brute_force_and_identity_grouping(qtype):
+    codes, scales, zeros, g_idx = _act_order_case(qtype, 3, 384, 5)
+    assert np.array_equal(np.bincount(g_idx), [128, 128, 128])       # 128 columns per group
+    x = np.random.default_rng(6).standard_normal(384)
+    got = O.dequant(qtype, codes, scales, None, zeros, g_idx) @ x
+    assert np.allclose(got, _brute_dequant_matvec(qtype, codes, scales, None, x, zeros, g_idx),
+                       rtol=1e-12, atol=1e-12)
+    # the grouping of the plain format, written out, is the plain format
+    plain = np.arange(384) // 128
+    assert np.array_equal(O.dequant(qtype, codes, scales, None, zeros, plain),
+                          O.dequant(qtype, codes, scales, None, zeros))
+
+
+@pytest.mark.parametrize("qtype", ["int4_g128", "int4zp_g128"])
+def test_dequant_act_order_is_the_plain_format_on_sorted_columns(qtype):
+    # sorting the columns by group turns an act-order weight into a plain one with the same
+    # scales (GPTQ desc_act): dequant(codes, g_idx)[:, perm] == dequant(codes[:, perm])
+    codes, scales, zeros, g_idx = _act_order_case(qtype, 5, 512, 9)
+    perm = np.argsort(g_idx, kind="stable")
+    q = np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(5, 512)
+    sorted_codes = _pack_nibbles(q[:, perm])
+    act = O.dequant(qtype, codes, scales, None, zeros, g_idx)
+    assert np.array_equal(act[:, perm], O.dequant(qtype, sorted_codes, scales, None, zeros))
+    assert not np.array_equal(act, O.dequant(qtype, codes, scales, None, zeros))
+
+
+def test_layer_act_order_equals_plain_layer_on_permuted_columns():
+    # the layer with act-order weights equals the plain layer whose GEMM1 columns (with x) and
+    # GEMM2 columns (with GEMM1's intermediate features: gate and up rows, biases) are
+    # permuted into group order (float64 throughout)
+    wl = W.small_workload("int4_g128").replace(bias=True, act_order=True, n_global=8, n_local=8)
+    lw = W.make_weights(wl)
+    inp = W.make_inputs(wl, 9)
+    kw = dict(expert_start=0, n_local=8, act="silu_mul", bf16_intermediates=False)
+    ref = O.moe_layer("int4_g128", inp.x, inp.topk_ids, inp.topk_weights, lw.w13, lw.w2, **kw)
+    E, I, H = 8, wl.I, wl.H
+    out = np.zeros_like(ref)
+    for e in range(E):   # one expert at a time: each has its own column orders
+        p1 = np.argsort(lw.w13.g_idx[e], kind="stable")
+        p2 = np.argsort(lw.w2.g_idx[e], kind="stable")
+        q13 = np.stack([lw.w13.codes[e] & 0xF, lw.w13.codes[e] >> 4], axis=-1).reshape(2 * I, H)[:, p1]
+        rows = np.concatenate([p2, I + p2])                      # gate and up rows in p2 order
+        c13 = _pack_nibbles(q13[rows])[None]
+        q2 = np.stack([lw.w2.codes[e] & 0xF, lw.w2.codes[e] >> 4], axis=-1).reshape(H, I)[:, p2]
+        w13 = NS(codes=c13, scales=lw.w13.scales[e][rows][None], gs=None, bias=lw.w13.bias[e][rows][None])
+        w2 = NS(codes=_pack_nibbles(q2)[None], scales=lw.w2.scales[e][None], gs=None, bias=lw.w2.bias[e][None])
+        ids = np.where(inp.topk_ids == e, 0, -1).astype(np.int32)
+        xb = np.ascontiguousarray(inp.x[:, p1])
+        out += O.moe_layer("int4_g128", xb, ids, inp.topk_weights, w13, w2,
+                           **dict(kw, expert_start=0, n_local=1))
+    assert np.allclose(out, ref, rtol=1e-9, atol=1e-9)
 
 
 def test_dequant_constant_closed_forms():

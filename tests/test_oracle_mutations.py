@@ -69,17 +69,22 @@ MUTATIONS = {
     "square without the relu": ("act_relu2", lambda: (lambda h: np.square(h))),
     "segments reversed": ("moe_align", lambda: _align_reversed_segments),
     "off-slice kept": ("route_local", lambda: (lambda ids, start, n: (np.asarray(ids) % n).astype(np.int32))),
-    "global scale missing": ("dequant", lambda: (lambda q, c, s, gs=None, zeros=None:
-                                                 ORIG_DQ(q, c, s, None if gs is None else 1.0, zeros))),
-    "zero point ignored": ("dequant", lambda: (lambda q, c, s, gs=None, zeros=None:
-                                               ORIG_DQ("int4_g128", c, s) if q == "int4zp_g128"
-                                               else ORIG_DQ(q, c, s, gs, zeros))),
-    "zero point sign flipped": ("dequant", lambda: (lambda q, c, s, gs=None, zeros=None:
-                                             ORIG_DQ(q, c, s, gs, None if zeros is None else (16 - zeros.astype(np.int64)) % 16)
-                                             if q == "int4zp_g128" else ORIG_DQ(q, c, s, gs, zeros))),
-    "zero point of the wrong group": ("dequant", lambda: (lambda q, c, s, gs=None, zeros=None:
-                                                          ORIG_DQ(q, c, s, gs, None if zeros is None else zeros[..., ::-1])
-                                                          if q == "int4zp_g128" else ORIG_DQ(q, c, s, gs, zeros))),
+    "global scale missing": ("dequant", lambda: (lambda q, c, s, gs=None, zeros=None, g_idx=None:
+                                                 ORIG_DQ(q, c, s, None if gs is None else 1.0, zeros, g_idx))),
+    "zero point ignored": ("dequant", lambda: (lambda q, c, s, gs=None, zeros=None, g_idx=None:
+                                               ORIG_DQ("int4_g128", c, s, None, None, g_idx) if q == "int4zp_g128"
+                                               else ORIG_DQ(q, c, s, gs, zeros, g_idx))),
+    "zero point sign flipped": ("dequant", lambda: (lambda q, c, s, gs=None, zeros=None, g_idx=None:
+                                             ORIG_DQ(q, c, s, gs, None if zeros is None else (16 - zeros.astype(np.int64)) % 16, g_idx)
+                                             if q == "int4zp_g128" else ORIG_DQ(q, c, s, gs, zeros, g_idx))),
+    "zero point of the wrong group": ("dequant", lambda: (lambda q, c, s, gs=None, zeros=None, g_idx=None:
+                                                          ORIG_DQ(q, c, s, gs, None if zeros is None else zeros[..., ::-1], g_idx)
+                                                          if q == "int4zp_g128" else ORIG_DQ(q, c, s, gs, zeros, g_idx))),
+    "act-order grouping ignored": ("dequant", lambda: (lambda q, c, s, gs=None, zeros=None, g_idx=None:
+                                                       ORIG_DQ(q, c, s, gs, zeros))),
+    "act-order group of the sorted position": ("dequant", lambda: (lambda q, c, s, gs=None, zeros=None, g_idx=None:
+                                                                   ORIG_DQ(q, c, s, gs, zeros, None if g_idx is None
+                                                                           else np.sort(g_idx)))),
 }
 ORIG_EF, ORIG_COMBINE, ORIG_NIB, ORIG_SW, ORIG_DQ = (O.expert_forward, O.combine, O._nibbles,
                                                       O.act_swiglu_alpha, O.dequant)
@@ -90,6 +95,8 @@ PINS = [
     (TL.test_dequant_matches_per_element_brute_force, dict(qtype="int4zp_g128", N=3, K=384)),
     (TL.test_dequant_asymmetric_int4_closed_forms, {}),
     (TL.test_dequant_asymmetric_int4_with_zero_point_8_is_uint4b8, {}),
+    (TL.test_dequant_act_order_brute_force_and_identity_grouping, dict(qtype="int4_g128")),
+    (TL.test_dequant_act_order_is_the_plain_format_on_sorted_columns, dict(qtype="int4zp_g128")),
     (TL.test_silu_mul_hand_values, {}),
     (TL.test_swiglu_alpha_hand_values, {}),
     (TL.test_relu2_hand_values, {}),

@@ -67,6 +67,7 @@ class Workload:
     routing: str = "uniform"   # or "zipf"
     zipf_s: float = 1.2
     seed: int = 0              # seed id of the weights (and default input seed)
+    act_order: bool = False    # int4 formats: a random g_idx per expert and projection
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -123,6 +124,7 @@ class ExpertWeights:
     N: int
     K: int
     zeros: Optional[np.ndarray] = None
+    g_idx: Optional[np.ndarray] = None   # int32 [E, K]: group of each input column (act-order)
 
 
 @dataclass
@@ -164,6 +166,14 @@ def _projection(rng: np.random.Generator, wl: Workload, E: int, N: int, K: int) 
     return ExpertWeights(codes, scales, gs, None, N, K, zeros)
 
 
+def make_g_idx(rng: np.random.Generator, E: int, K: int, group: int = 128) -> np.ndarray:
+    """int32 [E, K]: a random act-order grouping per expert, every group holding `group` columns."""
+    rank = np.argsort(rng.random((E, K)), axis=1, kind="stable")      # a random permutation per expert
+    g = np.empty((E, K), dtype=np.int32)
+    np.put_along_axis(g, rank, (np.arange(K) // group).astype(np.int32)[None, :].repeat(E, 0), axis=1)
+    return g
+
+
 def make_weights(wl: Workload) -> LayerWeights:
     """Canonical weights of the local experts (only these are ever passed on)."""
     E, H, I = wl.n_local, wl.H, wl.I
@@ -173,6 +183,14 @@ def make_weights(wl: Workload) -> LayerWeights:
     n13 = I if wl.act == "relu2" else 2 * I   # gate/up rows, or the non-gated projection
     w13 = _projection(rng, wl, E, n13, H)
     w2 = _projection(rng, wl, E, H, I)
+    if wl.act_order:
+        if wl.group != 128:
+            raise ValueError("act-order is defined for the int4 formats")
+        # GPTQ desc_act grouping: columns ranked by a random order, 128 consecutive ranks per
+        # group (drawn from a stream of its own: the other weights do not change)
+        ao = _rng(wl.seed, 1, _S_WEIGHTS)
+        w13.g_idx = make_g_idx(ao, E, H)
+        w2.g_idx = make_g_idx(ao, E, I)
     aux = _rng(wl.seed, 0, _S_AUX)
     if wl.bias:
         w13.bias = _to_bf16_bits(aux.normal(0.0, 0.1, size=(E, n13)).astype(np.float32))
@@ -237,6 +255,8 @@ def device_weights(lw: LayerWeights, device="cuda") -> tuple:
             d["bias"] = torch.from_numpy(p.bias.view(np.int16)).to(device).view(torch.bfloat16)
         if p.zeros is not None:
             d["zeros"] = torch.from_numpy(p.zeros).to(device)
+        if p.g_idx is not None:
+            d["g_idx"] = torch.from_numpy(p.g_idx).to(device)
         return d
     int4 = lw.w13.scales.dtype == np.uint16
     nw = None
