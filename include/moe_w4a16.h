@@ -116,6 +116,8 @@ int moe_align(const int32_t* topk_ids, int64_t M, int32_t top_k, int32_t expert_
 #define MOE_PREP_GATE_UP      0x1u  /* rows are a gate/up pair: N = 2I, gate rows [0, I), up [I, 2I) */
 #define MOE_PREP_INTERLEAVED  0x2u  /* with GATE_UP: rows arrive as gate0, up0, gate1, up1, ...   */
 #define MOE_PREP_PAD          0x4u  /* zero-pad K (and with GATE_UP each half of N) to a multiple of 64 */
+#define MOE_PREP_ACT_ORDER    0x8u  /* int4 formats: act-order grouping (g_idx); the prepared
+                                       columns are in group order, desc.perm gives their source */
 
 /* Prepared (device-resident) weights of one projection, filled by moe_w4a16_prepare.  Plain
  * data: it may be copied; the pointers are into the caller's `out` buffer. */
@@ -132,6 +134,9 @@ typedef struct moe_weights {
   const void* scales;     /* tiled group scales (and zero points)                      */
   const float* global_scale; /* [E] NVFP4 per-expert scale, else NULL                  */
   const uint16_t* bias;   /* bf16 [E, N] or NULL                                       */
+  const int32_t* perm;    /* act-order: int32 [E, K]; prepared column j of expert e is input
+                             column perm[e * K + j] (moe_permute_cols gathers the activations
+                             into this order); NULL without MOE_PREP_ACT_ORDER              */
 } moe_weights;
 
 /* Prepared dimensions and the number of bytes moe_w4a16_prepare writes.  Pure host function.
@@ -150,6 +155,13 @@ int moe_w4a16_prepared_size(moe_qtype q, int32_t E, int32_t N, int32_t K, uint32
  *   bias          device bf16 [E, N] or NULL (interleaved like the rows when INTERLEAVED)
  *   zeros         device uint8 [E, N, K/128], zero points 0..15 (MOE_Q_INT4ZP_G128 only, else
  *                 NULL; a value above 15 is an error of the caller and is used modulo 16)
+ *   g_idx         device int32 [E, K] with MOE_PREP_ACT_ORDER (int4 formats, K <= 16384), else
+ *                 NULL: the group of 128 whose scale (and zero point) input column k uses -- the
+ *                 g_idx of the Marlin MoE call in the "sglang PR 31552" summary, the GPTQ
+ *                 act-order grouping.  Every group must hold exactly 128 columns; otherwise the
+ *                 results are undefined (memory stays in bounds: out-of-range ids are ignored).
+ *                 The columns are stored sorted by group (stable), so that the GEMMs see the
+ *                 plain grouping, and desc->perm records the order.
  *   out           device buffer of at least `bytes` from moe_w4a16_prepared_size, 256-B aligned
  *   desc          host struct filled with the prepared dims and device pointers into `out`
  * Padded rows/columns get zero weights (zero codes, and zero points equal to the code for the
@@ -158,8 +170,24 @@ int moe_w4a16_prepared_size(moe_qtype q, int32_t E, int32_t N, int32_t K, uint32
  */
 int moe_w4a16_prepare(moe_qtype q, const uint8_t* codes, const void* scales,
                       const float* global_scale, const uint16_t* bias, const uint8_t* zeros,
-                      int32_t E, int32_t N, int32_t K, uint32_t flags, void* out, size_t out_bytes,
-                      moe_weights* desc, hipStream_t stream);
+                      const int32_t* g_idx, int32_t E, int32_t N, int32_t K, uint32_t flags,
+                      void* out, size_t out_bytes, moe_weights* desc, hipStream_t stream);
+
+/*
+ * Act-order activation gather: the rows a GEMM on act-order weights reads, with their columns
+ * in the prepared (group-sorted) order of the expert each row is routed to:
+ *   dst[r, j] = src[r / row_div, perm[e * K + j]],   e = slot_expert[r]
+ * for every r < rows with 0 <= e < E; other rows of dst are not written.
+ *   src          device bf16 [*, ld_src]: the layer input (row_div = top_k, rows = M * top_k,
+ *                one row per slot) or GEMM1's activated output (row_div = 1)
+ *   perm         desc.perm of the act-order projection (int32 [E, K])
+ *   slot_expert  device int32 [rows]: local expert of each slot (moe_align's slot_local_ids)
+ *   dst          device bf16 [rows, ld_dst], the GEMM's A with top_k = 1
+ * K % 8 == 0; ld_src, ld_dst >= K; src and dst must not overlap.  Errors: MOE_EINVAL.
+ */
+int moe_permute_cols(const uint16_t* src, int64_t ld_src, int32_t row_div, const int32_t* perm,
+                     int32_t K, int32_t E, const int32_t* slot_expert, int64_t rows, uint16_t* dst,
+                     int64_t ld_dst, hipStream_t stream);
 
 /* The post-expert norm's effective weight: out[h] = bf16(1 + w[h]) (round to nearest even),
  * as the experiment's prepare binds it once.  w, out: device bf16 [H]. */

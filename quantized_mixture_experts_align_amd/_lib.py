@@ -14,7 +14,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ESIZE, MOE_EHIP = 0, -1, -2, -3, -4
 QTYPE = {"int4_g128": 0, "nvfp4_g16": 1, "mxfp4_g32": 2, "int4zp_g128": 3}
 ACT = {"silu_mul": 0, "swiglu_alpha": 1, "relu2": 2}
 GATED = {"silu_mul": True, "swiglu_alpha": True, "relu2": False}
-PREP_GATE_UP, PREP_INTERLEAVED, PREP_PAD = 0x1, 0x2, 0x4
+PREP_GATE_UP, PREP_INTERLEAVED, PREP_PAD, PREP_ACT_ORDER = 0x1, 0x2, 0x4, 0x8
 GEMM_AUTO, GEMM_DECODE, GEMM_MFMA = 0, 1, 2
 
 
@@ -23,7 +23,7 @@ class MoeWeights(C.Structure):
         ("qtype", C.c_int32), ("n_experts", C.c_int32), ("N", C.c_int32), ("K", C.c_int32),
         ("N_logical", C.c_int32), ("K_logical", C.c_int32), ("flags", C.c_uint32),
         ("reserved", C.c_int32), ("codes", C.c_void_p), ("scales", C.c_void_p),
-        ("global_scale", C.c_void_p), ("bias", C.c_void_p),
+        ("global_scale", C.c_void_p), ("bias", C.c_void_p), ("perm", C.c_void_p),
     ]
 
 
@@ -48,8 +48,9 @@ SIGNATURES = {
     "moe_align": (C.c_int, [_P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "moe_w4a16_prepared_size": (C.c_int, [C.c_int, _I32, _I32, _I32, C.c_uint32, _I32,
                                           C.POINTER(_I32), C.POINTER(_I32), C.POINTER(_SZ)]),
-    "moe_w4a16_prepare": (C.c_int, [C.c_int, _P, _P, _P, _P, _P, _I32, _I32, _I32, C.c_uint32, _P,
+    "moe_w4a16_prepare": (C.c_int, [C.c_int, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, C.c_uint32, _P,
                                     _SZ, C.POINTER(MoeWeights), _P]),
+    "moe_permute_cols": (C.c_int, [_P, _I64, _I32, _P, _I32, _I32, _P, _I64, _P, _I64, _P]),
     "moe_norm_weight": (C.c_int, [_P, _I32, _P, _P]),
     "moe_choose_block_m": (C.c_int, [_I64, _I32, C.POINTER(_I32)]),
     "moe_gemm_choose": (C.c_int, [C.POINTER(MoeWeights), _I64, _I32, _I32, C.POINTER(MoeGemmConfig)]),

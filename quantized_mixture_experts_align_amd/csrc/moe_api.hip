@@ -33,7 +33,7 @@ using namespace moe;
 
 extern "C" const char* moe_last_error(void) { return g_err; }
 
-extern "C" int32_t moe_abi_version(void) { return 2; }
+extern "C" int32_t moe_abi_version(void) { return 3; }
 
 extern "C" int moe_align_capacity(int64_t M, int32_t top_k, int32_t n_local, int32_t block_m,
                                   int64_t* sorted_len, int64_t* blocks_len) {
@@ -55,8 +55,12 @@ extern "C" int moe_w4a16_prepared_size(moe_qtype q, int32_t E, int32_t N, int32_
   MOE_REQUIRE(q == MOE_Q_INT4_G128 || q == MOE_Q_NVFP4_G16 || q == MOE_Q_MXFP4_G32 || q == MOE_Q_INT4ZP_G128,
               MOE_EINVAL, "unknown qtype %d", (int)q);
   MOE_REQUIRE(E >= 1 && N >= 1 && K >= 1, MOE_EINVAL, "E=%d N=%d K=%d must be positive", E, N, K);
-  MOE_REQUIRE((flags & ~(MOE_PREP_GATE_UP | MOE_PREP_INTERLEAVED | MOE_PREP_PAD)) == 0, MOE_EINVAL,
-              "unknown prepare flags 0x%x", flags);
+  MOE_REQUIRE((flags & ~(MOE_PREP_GATE_UP | MOE_PREP_INTERLEAVED | MOE_PREP_PAD | MOE_PREP_ACT_ORDER)) == 0,
+              MOE_EINVAL, "unknown prepare flags 0x%x", flags);
+  MOE_REQUIRE(!(flags & MOE_PREP_ACT_ORDER) || pair_grouped(q), MOE_EUNSUPPORTED,
+              "MOE_PREP_ACT_ORDER (g_idx) is defined for the int4 formats only");
+  MOE_REQUIRE(!(flags & MOE_PREP_ACT_ORDER) || (K % 128 == 0 && K <= kMaxActOrderK), MOE_EUNSUPPORTED,
+              "MOE_PREP_ACT_ORDER: K=%d must be a multiple of 128 and at most %d", K, kMaxActOrderK);
   MOE_REQUIRE(!(flags & MOE_PREP_INTERLEAVED) || (flags & MOE_PREP_GATE_UP), MOE_EINVAL,
               "MOE_PREP_INTERLEAVED needs MOE_PREP_GATE_UP");
   const int g = group_of(q);
@@ -83,6 +87,7 @@ extern "C" int moe_w4a16_prepared_size(moe_qtype q, int32_t E, int32_t N, int32_
   total += align256(tiles * (size_t)scale_bytes_per_tile(q));
   if (q == MOE_Q_NVFP4_G16) total += align256((size_t)E * 4);
   if (has_bias) total += align256((size_t)E * nout * 2);
+  if (flags & MOE_PREP_ACT_ORDER) total += align256((size_t)E * K * 4);
   if (N_out) *N_out = nout;
   if (K_out) *K_out = kout;
   if (bytes) *bytes = total;

@@ -49,6 +49,9 @@ inline __host__ __device__ int scale_step_bytes(int q) {
 
 inline __host__ __device__ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// act-order (g_idx) weights: most input columns per expert (the grouping is staged in LDS)
+constexpr int kMaxActOrderK = 16384;
+
 // MFMA GEMM: align blocks per XCD workgroup group (launch order only, never results).  With a
 // short K (<= 1024) a workgroup is brief and an expert's whole weight set fits an XCD's L2, so
 // eight consecutive blocks -- mostly one expert's -- share one XCD (measured: int4 layers 5-10%

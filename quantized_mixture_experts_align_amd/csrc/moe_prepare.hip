@@ -31,8 +31,33 @@ __device__ __forceinline__ int src_row(const PrepGeom& g, int n) {
   return (g.flags & MOE_PREP_INTERLEAVED) ? 2 * j + half : half * g.I + j;
 }
 
+// Act-order: the stable sort of each expert's input columns by group (g_idx), i.e. prepared
+// column j of expert e is input column perm[e][j].  One workgroup per expert: the grouping is
+// staged in LDS, then thread t walks the columns in order and places those of group t (and
+// t + 256, ...) at group * 128 + rank.  Every group is expected to hold 128 columns; columns
+// with an out-of-range group and places beyond 128 per group are skipped, so a bad grouping
+// gives wrong (never out-of-bounds) results.
+__global__ __launch_bounds__(256) void prep_perm_kernel(const int32_t* __restrict__ g_idx,
+                                                        int32_t* __restrict__ perm, int K) {
+  __shared__ int32_t s_g[kMaxActOrderK];
+  const int e = blockIdx.x, G = K / 128;
+  const int32_t* gi = g_idx + (int64_t)e * K;
+  int32_t* pe = perm + (int64_t)e * K;
+  for (int k = threadIdx.x; k < K; k += blockDim.x) {
+    s_g[k] = gi[k];
+    pe[k] = 0;  // any unfilled place reads column 0 (in bounds)
+  }
+  __syncthreads();
+  for (int grp = threadIdx.x; grp < G; grp += blockDim.x) {
+    int cnt = 0;
+    for (int k = 0; k < K && cnt < 128; ++k)
+      if (s_g[k] == grp) pe[grp * 128 + cnt++] = k;
+  }
+}
+
 // one thread per output dword of codes
-__global__ void prep_codes_kernel(const uint8_t* __restrict__ src, uint32_t* __restrict__ dst, PrepGeom g) {
+__global__ void prep_codes_kernel(const uint8_t* __restrict__ src, uint32_t* __restrict__ dst, PrepGeom g,
+                                  const int32_t* __restrict__ perm) {
   const int NT = g.Nout / kTileN, KT = g.Kout / kTileK;
   const int64_t total = (int64_t)g.E * NT * KT * 128;
   const uint32_t zero = g.q == MOE_Q_INT4_G128 ? 0x88888888u : 0u;
@@ -48,8 +73,20 @@ __global__ void prep_codes_kernel(const uint8_t* __restrict__ src, uint32_t* __r
     const int r = src_row(g, n);
     uint32_t v = zero;
     if (r >= 0 && k < g.K) {
-      const uint8_t* p = src + ((int64_t)e * g.N + r) * (g.K / 2) + k / 2;
-      v = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+      const uint8_t* p = src + ((int64_t)e * g.N + r) * (g.K / 2);
+      if (perm) {  // act-order: gather the eight codes of prepared columns k .. k+7
+        const int32_t* pc = perm + (int64_t)e * g.K + k;
+        v = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = min(max(pc[j], 0), g.K - 1);
+          const uint32_t b = p[c >> 1];
+          v |= ((c & 1) ? (b >> 4) : (b & 0xFu)) << (4 * j);
+        }
+      } else {
+        p += k / 2;
+        v = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+      }
     }
     dst[d] = v;
   }
@@ -128,14 +165,57 @@ __global__ void prep_bias_kernel(const uint16_t* __restrict__ src, uint16_t* __r
 
 static int grid_for(int64_t n) { return (int)std::min<int64_t>((n + 255) / 256, 16384); }
 
+// Act-order gather: one thread per (row, 8 columns); rows of dead slots are skipped.
+__global__ void permute_cols_kernel(const uint16_t* __restrict__ src, int64_t ld_src, int row_div,
+                                    const int32_t* __restrict__ perm, int K, int E,
+                                    const int32_t* __restrict__ slot_expert, int64_t rows,
+                                    uint16_t* __restrict__ dst, int64_t ld_dst) {
+  const int chunks = K >> 3;
+  const int64_t total = rows * chunks;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = t / chunks;
+    const int j = (int)(t - r * chunks) << 3;
+    const int e = slot_expert[r];
+    if (e < 0 || e >= E) continue;
+    const uint16_t* s = src + (r / row_div) * ld_src;
+    const int32_t* pc = perm + (int64_t)e * K + j;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c0 = min(max(pc[2 * i], 0), K - 1), c1 = min(max(pc[2 * i + 1], 0), K - 1);
+      w[i] = (uint32_t)s[c0] | ((uint32_t)s[c1] << 16);
+    }
+    *reinterpret_cast<uint4*>(dst + r * ld_dst + j) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 }  // namespace moe
 
 using namespace moe;
 
+extern "C" int moe_permute_cols(const uint16_t* src, int64_t ld_src, int32_t row_div, const int32_t* perm,
+                                int32_t K, int32_t E, const int32_t* slot_expert, int64_t rows, uint16_t* dst,
+                                int64_t ld_dst, hipStream_t stream) {
+  MOE_REQUIRE(rows >= 0 && K >= 8 && K % 8 == 0 && E >= 1 && row_div >= 1, MOE_EINVAL,
+              "moe_permute_cols: rows=%lld K=%d E=%d row_div=%d", (long long)rows, K, E, row_div);
+  MOE_REQUIRE(ld_src >= K && ld_dst >= K && ld_dst % 8 == 0, MOE_EINVAL,
+              "moe_permute_cols: ld_src=%lld ld_dst=%lld (>= K, ld_dst a multiple of 8)",
+              (long long)ld_src, (long long)ld_dst);
+  if (rows == 0) return ok();
+  MOE_REQUIRE(src && perm && slot_expert && dst, MOE_EINVAL, "moe_permute_cols: null pointer");
+  MOE_REQUIRE(((uintptr_t)dst & 15) == 0, MOE_EINVAL, "moe_permute_cols: dst must be 16-byte aligned");
+  const int64_t total = rows * (K / 8);
+  const int grid = (int)std::min<int64_t>((total + 255) / 256, 16384);
+  hipLaunchKernelGGL(permute_cols_kernel, dim3(grid), dim3(256), 0, stream, src, ld_src, (int)row_div, perm,
+                     (int)K, (int)E, slot_expert, rows, dst, ld_dst);
+  return check_launch("moe_permute_cols");
+}
+
 extern "C" int moe_w4a16_prepare(moe_qtype q, const uint8_t* codes, const void* scales,
                                  const float* global_scale, const uint16_t* bias, const uint8_t* zeros,
-                                 int32_t E, int32_t N, int32_t K, uint32_t flags, void* out,
-                                 size_t out_bytes, moe_weights* desc, hipStream_t stream) {
+                                 const int32_t* g_idx, int32_t E, int32_t N, int32_t K, uint32_t flags,
+                                 void* out, size_t out_bytes, moe_weights* desc, hipStream_t stream) {
   int32_t Nout = 0, Kout = 0;
   size_t need = 0;
   int rc = moe_w4a16_prepared_size(q, E, N, K, flags, bias != nullptr, &Nout, &Kout, &need);
@@ -145,6 +225,8 @@ extern "C" int moe_w4a16_prepare(moe_qtype q, const uint8_t* codes, const void* 
               "moe_w4a16_prepare: a global scale is required for NVFP4 and only for NVFP4");
   MOE_REQUIRE((q == MOE_Q_INT4ZP_G128) == (zeros != nullptr), MOE_EINVAL,
               "moe_w4a16_prepare: zero points are required for asymmetric int4 and only for it");
+  MOE_REQUIRE(((flags & MOE_PREP_ACT_ORDER) != 0) == (g_idx != nullptr), MOE_EINVAL,
+              "moe_w4a16_prepare: g_idx is required with MOE_PREP_ACT_ORDER and only with it");
   MOE_REQUIRE(out_bytes >= need, MOE_ESIZE, "moe_w4a16_prepare: out has %zu bytes, %zu needed",
               out_bytes, need);
   MOE_REQUIRE(((uintptr_t)out & 255) == 0, MOE_EINVAL, "moe_w4a16_prepare: out must be 256-byte aligned");
@@ -156,9 +238,12 @@ extern "C" int moe_w4a16_prepare(moe_qtype q, const uint8_t* codes, const void* 
   uint8_t* p_scales = p_codes + align256(tiles * kTileBytes);
   uint8_t* p_gs = p_scales + align256(tiles * (size_t)scale_bytes_per_tile(q));
   uint8_t* p_bias = p_gs + (q == MOE_Q_NVFP4_G16 ? align256((size_t)E * 4) : 0);
+  int32_t* p_perm = reinterpret_cast<int32_t*>(p_bias + (bias ? align256((size_t)E * Nout * 2) : 0));
 
+  if (g_idx)
+    hipLaunchKernelGGL(prep_perm_kernel, dim3(E), dim3(256), 0, stream, g_idx, p_perm, K);
   hipLaunchKernelGGL(prep_codes_kernel, dim3(grid_for((int64_t)tiles * 128)), dim3(256), 0, stream,
-                     codes, reinterpret_cast<uint32_t*>(p_codes), g);
+                     codes, reinterpret_cast<uint32_t*>(p_codes), g, g_idx ? p_perm : nullptr);
   hipLaunchKernelGGL(prep_scales_kernel, dim3(grid_for((int64_t)tiles * 64)), dim3(256), 0, stream,
                      static_cast<const uint8_t*>(scales), zeros, p_scales, g);
   if (q == MOE_Q_NVFP4_G16) {
@@ -183,6 +268,7 @@ extern "C" int moe_w4a16_prepare(moe_qtype q, const uint8_t* codes, const void* 
   d.scales = p_scales;
   d.global_scale = q == MOE_Q_NVFP4_G16 ? reinterpret_cast<const float*>(p_gs) : nullptr;
   d.bias = bias ? reinterpret_cast<const uint16_t*>(p_bias) : nullptr;
+  d.perm = g_idx ? p_perm : nullptr;
   *desc = d;
   return ok();
 }

@@ -29,13 +29,16 @@ class Workspace:
     a: torch.Tensor
     out: torch.Tensor
     cfgs: Optional[tuple] = None    # (gate/up, down) GEMM launch configurations
+    perm: Optional[torch.Tensor] = None   # act-order: the gathered A of a GEMM [numel, max(H, I)]
 
 
 class MoELayer:
     """One GPU's slice of a W4A16 MoE expert layer (experts [expert_start, expert_start + n_local)).
 
     ``w13`` / ``w2``: dicts of device tensors in the canonical layouts: ``codes`` uint8
-    [E, N, K/2], ``scales`` [E, N, K/g], optional ``gs`` fp32 [E] (NVFP4) and ``bias`` bf16 [E, N].
+    [E, N, K/2], ``scales`` [E, N, K/g], optional ``gs`` fp32 [E] (NVFP4), ``bias`` bf16 [E, N],
+    ``zeros`` uint8 [E, N, K/128] (asymmetric int4) and ``g_idx`` int32 [E, K] (act-order int4:
+    the GEMM then reads its activations gathered into group order by moe_permute_cols).
     ``w13`` has 2I rows (gate, up) for the gated activations and I rows for ``relu2``.
     ``routed_scaling_factor`` multiplies the combined output.
     """
@@ -60,9 +63,10 @@ class MoELayer:
             f13 = L.PREP_PAD if pad else 0
         f2 = L.PREP_PAD if pad else 0
         self.W13 = ops.moe_w4a16_prepare(qtype, w13["codes"], w13["scales"], w13.get("gs"),
-                                         w13.get("bias"), f13, w13.get("zeros"))
+                                         w13.get("bias"), f13, w13.get("zeros"), w13.get("g_idx"))
         self.W2 = ops.moe_w4a16_prepare(qtype, w2["codes"], w2["scales"], w2.get("gs"),
-                                        w2.get("bias"), f2, w2.get("zeros"))
+                                        w2.get("bias"), f2, w2.get("zeros"), w2.get("g_idx"))
+        self.act_order = (bool(self.W13.desc.perm), bool(self.W2.desc.perm))
         self.I = self.W13.N // 2 if self.gated else self.W13.N
         if self.W2.K != self.I:
             raise ValueError(f"down projection K={self.W2.K} != intermediate {self.I}")
@@ -94,11 +98,14 @@ class MoELayer:
         numel = M * self.top_k
         i32 = dict(dtype=torch.int32, device=device)
         bf = dict(dtype=torch.bfloat16, device=device)
+        perm = None
+        if any(self.act_order):
+            perm = torch.empty(numel * max(self.W13.K, self.W2.K), **bf)
         return Workspace(M, B, torch.empty(s_len, **i32), torch.empty(b_len, **i32),
                          torch.empty(1, **i32), torch.empty((M, self.top_k), **i32),
                          torch.empty(numel * max(self.W13.N, self.H), **bf),
                          torch.empty((numel, self.I), **bf), torch.empty((M, self.H), **bf),
-                         self.configs(M, B))
+                         self.configs(M, B), perm)
 
     def forward(self, x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
                 ws: Optional[Workspace] = None, cfg13=None, cfg2=None,
@@ -119,8 +126,9 @@ class MoELayer:
             c13, c2 = ws.cfgs if ws.cfgs is not None else self.configs(M, B)
             cfg13 = cfg13 or c13
             cfg2 = cfg2 or c2
+        # (act-order gate/up weights need the slots' experts before GEMM1: no fused align)
         routable = (numel <= ops.FUSED_ALIGN_SLOTS and B <= 16 and cfg13.kernel == L.GEMM_DECODE
-                    and cfg13.gemv_rows == 0)
+                    and cfg13.gemv_rows == 0 and not self.act_order[0])
         if fused_align is None:
             fused_align = fused_act and routable
         if fused_align and not (fused_act and routable):
@@ -136,16 +144,25 @@ class MoELayer:
         else:
             sorted_ids, eids, ntpp, loc = ops.moe_align(topk_ids, self.expert_start, self.n_local, B,
                                                         out=align_out)
+            a1, k1 = x, self.top_k
+            if self.act_order[0]:   # one gathered row per slot, read with top_k = 1
+                a1 = ops.moe_permute_cols(x, self.W13, loc.view(-1), self.top_k,
+                                          out=ws.perm[: numel * self.W13.K].view(numel, self.W13.K))
+                k1 = 1
             if fused_act:
-                ops.moe_w4a16_gemm_act(self.act, x, self.W13, sorted_ids, eids, ntpp, numel, self.top_k,
+                ops.moe_w4a16_gemm_act(self.act, a1, self.W13, sorted_ids, eids, ntpp, numel, k1,
                                        B, self.alpha, self.limit, out=ws.a, cfg=cfg13)
             else:
                 h = ws.buf13[: numel * self.W13.N].view(numel, self.W13.N)
-                ops.moe_w4a16_gemm(x, self.W13, sorted_ids, eids, ntpp, numel, self.top_k, B, out=h,
+                ops.moe_w4a16_gemm(a1, self.W13, sorted_ids, eids, ntpp, numel, k1, B, out=h,
                                    cfg=cfg13)
                 ops.moe_act(self.act, h, self.I, loc.view(-1), self.alpha, self.limit, out=ws.a)
         y = ws.buf13[: numel * self.H].view(numel, self.H)
-        ops.moe_w4a16_gemm(ws.a, self.W2, sorted_ids, eids, ntpp, numel, 1, B, out=y, cfg=cfg2)
+        a2 = ws.a
+        if self.act_order[1]:
+            a2 = ops.moe_permute_cols(ws.a, self.W2, loc.view(-1), 1,
+                                      out=ws.perm[: numel * self.W2.K].view(numel, self.W2.K))
+        ops.moe_w4a16_gemm(a2, self.W2, sorted_ids, eids, ntpp, numel, 1, B, out=y, cfg=cfg2)
         return ops.moe_combine(y, topk_weights, loc, self.norm_w, self.eps, out=ws.out,
                                routed_scaling_factor=self.routed_scaling_factor)
 

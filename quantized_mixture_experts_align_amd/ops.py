@@ -96,9 +96,14 @@ def prepared_size(qtype: str, E: int, N: int, K: int, flags: int, has_bias: bool
 
 def moe_w4a16_prepare(qtype: str, codes: torch.Tensor, scales: torch.Tensor,
                       global_scale: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
-                      flags: int = 0, zeros: Optional[torch.Tensor] = None) -> PreparedWeights:
+                      flags: int = 0, zeros: Optional[torch.Tensor] = None,
+                      g_idx: Optional[torch.Tensor] = None) -> PreparedWeights:
     """Repack canonical [E, N, K/2] codes and [E, N, K/g] scales (and, for int4zp_g128, the
-    uint8 [E, N, K/128] zero points) into the tiled layout."""
+    uint8 [E, N, K/128] zero points; for act-order int4, the int32 [E, K] g_idx, which sets
+    MOE_PREP_ACT_ORDER) into the tiled layout."""
+    if g_idx is not None:
+        _need(g_idx, torch.int32, "g_idx")
+        flags |= L.PREP_ACT_ORDER
     _need(codes, torch.uint8, "codes")
     if not scales.is_cuda or not scales.is_contiguous():
         raise ValueError("scales must be a contiguous device tensor")
@@ -117,9 +122,28 @@ def moe_w4a16_prepare(qtype: str, codes: torch.Tensor, scales: torch.Tensor,
     buf = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
     desc = L.MoeWeights()
     L.check(L.lib().moe_w4a16_prepare(L.QTYPE[qtype], _ptr(codes), _ptr(scales), _ptr(global_scale),
-                                      _ptr(bias), _ptr(zeros), E, N, K, flags, _ptr(buf), nbytes, C.byref(desc),
+                                      _ptr(bias), _ptr(zeros), _ptr(g_idx), E, N, K, flags, _ptr(buf), nbytes,
+                                      C.byref(desc),
                                       _stream()), "moe_w4a16_prepare")
     return PreparedWeights(buf, desc)
+
+
+def moe_permute_cols(src: torch.Tensor, W: PreparedWeights, slot_expert: torch.Tensor, row_div: int,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Rows of A for a GEMM on act-order weights W: out[r, j] = src[r // row_div, perm_e[j]] for
+    every slot r (= len(slot_expert)) routed to a local expert e; other rows are not written."""
+    _need(src, torch.bfloat16, "src")
+    _need(slot_expert, torch.int32, "slot_expert")
+    if not W.desc.perm:
+        raise ValueError("moe_permute_cols: the weights were prepared without act-order")
+    rows, K = slot_expert.numel(), W.K
+    if out is None:
+        out = torch.empty((rows, K), dtype=torch.bfloat16, device=src.device)
+    _need(out, torch.bfloat16, "out")
+    L.check(L.lib().moe_permute_cols(_ptr(src), src.stride(0), row_div, W.desc.perm, K, W.n_experts,
+                                     _ptr(slot_expert), rows, _ptr(out), out.stride(0), _stream()),
+            "moe_permute_cols")
+    return out
 
 
 def moe_norm_weight(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:

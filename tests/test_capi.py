@@ -27,7 +27,18 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(lib, n), n
         assert n in L.SIGNATURES, f"{n} has no binding"
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
+
+
+def test_weights_descriptor_matches_the_c_struct():
+    # moe_weights in include/moe_w4a16.h: eight 32-bit fields, then five pointers
+    assert C.sizeof(L.MoeWeights) == 8 * 4 + 5 * 8
+    assert [L.MoeWeights.__dict__[f].offset for f in ("codes", "scales", "global_scale", "bias", "perm")] \
+        == [32, 40, 48, 56, 64]
+    text = open(os.path.join(ROOT, "include", "moe_w4a16.h")).read()
+    body = text[text.index("typedef struct moe_weights {"):text.index("} moe_weights;")]
+    fields = re.findall(r"\b(\w+);", re.sub(r"/\*.*?\*/", "", body, flags=re.S))
+    assert fields == [f for f, _ in L.MoeWeights._fields_]
 
 
 @pytest.mark.parametrize("M,k,E,B", [(0, 8, 32, 16), (1, 8, 32, 16), (123, 2, 8, 64), (4096, 8, 32, 128),
@@ -113,10 +124,31 @@ def test_entry_points_reject_bad_arguments_before_launch():
     # zero points: required for asymmetric int4 and only for it (checked before any launch)
     desc = L.MoeWeights()
     out = C.c_void_p(1 << 20)
-    assert lib.moe_w4a16_prepare(L.QTYPE["int4zp_g128"], s, s, None, None, None, 4, 64, 256, 0, out, 1 << 20,
+    assert lib.moe_w4a16_prepare(L.QTYPE["int4zp_g128"], s, s, None, None, None, None, 4, 64, 256, 0, out,
+                                 1 << 20, C.byref(desc), None) == L.MOE_EINVAL and b"zero points" in lib.moe_last_error()
+    assert lib.moe_w4a16_prepare(L.QTYPE["int4_g128"], s, s, None, None, s, None, 4, 64, 256, 0, out, 1 << 20,
                                  C.byref(desc), None) == L.MOE_EINVAL and b"zero points" in lib.moe_last_error()
-    assert lib.moe_w4a16_prepare(L.QTYPE["int4_g128"], s, s, None, None, s, 4, 64, 256, 0, out, 1 << 20,
-                                 C.byref(desc), None) == L.MOE_EINVAL and b"zero points" in lib.moe_last_error()
+    # act-order: g_idx exactly with the flag, int4 formats only, K a multiple of 128 up to 16384
+    assert lib.moe_w4a16_prepare(L.QTYPE["int4_g128"], s, s, None, None, None, None, 4, 64, 256,
+                                 L.PREP_ACT_ORDER, out, 1 << 20, C.byref(desc), None) == L.MOE_EINVAL
+    assert b"g_idx" in lib.moe_last_error()
+    assert lib.moe_w4a16_prepare(L.QTYPE["int4_g128"], s, s, None, None, None, s, 4, 64, 256, 0, out, 1 << 20,
+                                 C.byref(desc), None) == L.MOE_EINVAL and b"g_idx" in lib.moe_last_error()
+    assert lib.moe_w4a16_prepare(L.QTYPE["mxfp4_g32"], s, s, None, None, None, s, 4, 64, 256,
+                                 L.PREP_ACT_ORDER, out, 1 << 20, C.byref(desc), None) == L.MOE_EUNSUPPORTED
+    n, k, b = C.c_int32(), C.c_int32(), C.c_size_t()
+    assert lib.moe_w4a16_prepared_size(L.QTYPE["int4_g128"], 4, 64, 32768, L.PREP_ACT_ORDER, 0,
+                                       C.byref(n), C.byref(k), C.byref(b)) == L.MOE_EUNSUPPORTED
+    b0, b1 = C.c_size_t(), C.c_size_t()
+    assert lib.moe_w4a16_prepared_size(L.QTYPE["int4_g128"], 4, 64, 256, 0, 0, C.byref(n), C.byref(k), C.byref(b0)) == 0
+    assert lib.moe_w4a16_prepared_size(L.QTYPE["int4_g128"], 4, 64, 256, L.PREP_ACT_ORDER, 0, C.byref(n), C.byref(k),
+                                       C.byref(b1)) == 0
+    assert b1.value - b0.value == 4 * 256 * 4                    # the column order, int32 [E, K]
+    # the act-order gather checks its shapes before any launch; zero rows need no device
+    assert lib.moe_permute_cols(s, 256, 2, s, 252, 4, s, 8, s, 256, None) == L.MOE_EINVAL   # K % 8
+    assert lib.moe_permute_cols(s, 128, 2, s, 256, 4, s, 8, s, 256, None) == L.MOE_EINVAL   # ld_src < K
+    assert lib.moe_permute_cols(s, 256, 0, s, 256, 4, s, 8, s, 256, None) == L.MOE_EINVAL   # row_div
+    assert lib.moe_permute_cols(None, 256, 2, None, 256, 4, None, 0, None, 256, None) == L.MOE_OK
     # numel == 0 is a no-op that needs no device
     assert lib.moe_w4a16_gemm(None, 0, 4096, None, 8192, C.byref(W), None, None, None, 0, 8, 16, None, None) \
         == L.MOE_OK

@@ -167,7 +167,8 @@ def _sample(M, n, seed=0):
                                              (W.NVFP4_DECODE, 16, 5), (W.NVFP4_DECODE, 64, 5),
                                              (W.NVFP4_ZIPF, 256, 4), (W.NVFP4_ZIPF, 1024, 3), (W.NVFP4_ZIPF, 4096, 3),
                                              (W.MXFP4_SWIGLU, 1, 1), (W.MXFP4_SWIGLU, 32, 4),
-                                             (W.MXFP4_SWIGLU, 2048, 4), (W.INT4ZP, 1, 1), (W.INT4ZP, 2304, 2304)])
+                                             (W.MXFP4_SWIGLU, 2048, 4), (W.INT4ZP, 1, 1), (W.INT4ZP, 2304, 2304),
+                                             (W.INT4_ACT_ORDER, 1, 1), (W.INT4_ACT_ORDER, 2304, 2304)])
 def test_workload_layer_matches_oracle(name, M, n_sample):
     wl, lw, layer = _workload_layer(name)
     inp = W.make_inputs(wl, M)

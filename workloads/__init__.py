@@ -80,7 +80,7 @@ class Workload:
 # The workloads, by name: int4 layers of 8 experts (123 tokens; 2304 tokens with biases),
 # one GPU's NVFP4 slice of 32 of 256 experts (uniform decode batches; Zipf-routed prefill
 # batches, same weights), a 128-expert MXFP4 GPT-OSS-style layer, and the int4 layer's shapes
-# with asymmetric int4 (zero points) weights.
+# with asymmetric int4 (zero points) weights and with act-order (g_idx) int4 weights.
 WORKLOADS = {w.name: w for w in [
     Workload("int4_m123_e8_top2_h512_i1024", "int4_g128", 8, 0, 8, 2, 512, 1024,
              (123,), seed=0),
@@ -94,8 +94,10 @@ WORKLOADS = {w.name: w for w in [
              (1, 32, 2048), bias=True, act="swiglu_alpha", interleaved_w13=True, seed=4),
     Workload("int4zp_e8_top2_h512_i1024", "int4zp_g128", 8, 0, 8, 2, 512, 1024,
              (1, 2304), seed=5),
+    Workload("int4_actorder_bias_e8_top2_h512_i1024", "int4_g128", 8, 0, 8, 2, 512, 1024,
+             (1, 2304), bias=True, act_order=True, seed=6),
 ]}
-INT4_SMALL, INT4_BIAS, NVFP4_DECODE, NVFP4_ZIPF, MXFP4_SWIGLU, INT4ZP = WORKLOADS
+INT4_SMALL, INT4_BIAS, NVFP4_DECODE, NVFP4_ZIPF, MXFP4_SWIGLU, INT4ZP, INT4_ACT_ORDER = WORKLOADS
 HEADLINE = INT4_BIAS   # the layer bench.py measures by default
 
 
