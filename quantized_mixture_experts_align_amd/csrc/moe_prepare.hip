@@ -165,7 +165,57 @@ __global__ void prep_bias_kernel(const uint16_t* __restrict__ src, uint16_t* __r
 
 static int grid_for(int64_t n) { return (int)std::min<int64_t>((n + 255) / 256, 16384); }
 
-// Act-order gather: one thread per (row, 8 columns); rows of dead slots are skipped.
+// Act-order gather with the source row staged in LDS (K <= kPermLdsK): one wave per row, the
+// row read with coalesced 16-byte loads, then each lane gathers its 8 columns from LDS and
+// stores 16 bytes.  Rows of dead slots are skipped.
+constexpr int kPermLdsK = 4096;
+__global__ __launch_bounds__(256) void permute_cols_lds_kernel(
+    const uint16_t* __restrict__ src, int64_t ld_src, int row_div, const int32_t* __restrict__ perm,
+    int K, int E, const int32_t* __restrict__ slot_expert, int64_t rows, uint16_t* __restrict__ dst,
+    int64_t ld_dst) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_row[4][kPermLdsK];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint16_t* sr = s_row[w];
+  constexpr int J = kPermLdsK / 512;      // 8-column chunks per lane
+  for (int64_t r = (int64_t)blockIdx.x * 4 + w; r < rows; r += (int64_t)gridDim.x * 4) {
+    const int e = slot_expert[r];          // wave-uniform
+    if (e < 0 || e >= E) continue;
+    // the lane's column order first (16-byte loads), in flight together with the row's load
+    const int32_t* pe = perm + (int64_t)e * K;
+    uint4 pv[J][2];
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) {
+      const int j = lane * 8 + jj * 512;
+      if (j < K) {
+        pv[jj][0] = *reinterpret_cast<const uint4*>(pe + j);
+        pv[jj][1] = *reinterpret_cast<const uint4*>(pe + j + 4);
+      }
+    }
+    const uint16_t* s = src + (r / row_div) * ld_src;
+    for (int c = lane * 8; c < K; c += 512)
+      *reinterpret_cast<uint4*>(sr + c) = *reinterpret_cast<const uint4*>(s + c);
+    __builtin_amdgcn_s_waitcnt(0xc07f);    // this wave's LDS writes are done (lgkmcnt(0))
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) {
+      const int j = lane * 8 + jj * 512;
+      if (j < K) {
+        const int c[8] = {(int)pv[jj][0].x, (int)pv[jj][0].y, (int)pv[jj][0].z, (int)pv[jj][0].w,
+                          (int)pv[jj][1].x, (int)pv[jj][1].y, (int)pv[jj][1].z, (int)pv[jj][1].w};
+        uint32_t wv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c0 = min(max(c[2 * i], 0), K - 1), c1 = min(max(c[2 * i + 1], 0), K - 1);
+          wv[i] = (uint32_t)sr[c0] | ((uint32_t)sr[c1] << 16);
+        }
+        *reinterpret_cast<uint4*>(dst + r * ld_dst + j) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();       // every lane's LDS reads before the next row's writes
+  }
+}
+
+// Act-order gather, any K: one thread per (row, 8 columns); rows of dead slots are skipped.
 __global__ void permute_cols_kernel(const uint16_t* __restrict__ src, int64_t ld_src, int row_div,
                                     const int32_t* __restrict__ perm, int K, int E,
                                     const int32_t* __restrict__ slot_expert, int64_t rows,
@@ -205,6 +255,12 @@ extern "C" int moe_permute_cols(const uint16_t* src, int64_t ld_src, int32_t row
   if (rows == 0) return ok();
   MOE_REQUIRE(src && perm && slot_expert && dst, MOE_EINVAL, "moe_permute_cols: null pointer");
   MOE_REQUIRE(((uintptr_t)dst & 15) == 0, MOE_EINVAL, "moe_permute_cols: dst must be 16-byte aligned");
+  if (K <= kPermLdsK && ((uintptr_t)src & 15) == 0 && ld_src % 8 == 0) {
+    const int grid = (int)std::min<int64_t>((rows + 3) / 4, 16384);
+    hipLaunchKernelGGL(permute_cols_lds_kernel, dim3(grid), dim3(256), 0, stream, src, ld_src, (int)row_div,
+                       perm, (int)K, (int)E, slot_expert, rows, dst, ld_dst);
+    return check_launch("moe_permute_cols");
+  }
   const int64_t total = rows * (K / 8);
   const int grid = (int)std::min<int64_t>((total + 255) / 256, 16384);
   hipLaunchKernelGGL(permute_cols_kernel, dim3(grid), dim3(256), 0, stream, src, ld_src, (int)row_div, perm,

@@ -132,7 +132,8 @@ def moe_permute_cols(src: torch.Tensor, W: PreparedWeights, slot_expert: torch.T
                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Rows of A for a GEMM on act-order weights W: out[r, j] = src[r // row_div, perm_e[j]] for
     every slot r (= len(slot_expert)) routed to a local expert e; other rows are not written."""
-    _need(src, torch.bfloat16, "src")
+    if not src.is_cuda or src.dtype != torch.bfloat16 or src.dim() != 2 or src.stride(1) != 1:
+        raise ValueError("src must be a bf16 device matrix with unit column stride")
     _need(slot_expert, torch.int32, "slot_expert")
     if not W.desc.perm:
         raise ValueError("moe_permute_cols: the weights were prepared without act-order")

@@ -36,7 +36,9 @@ def test_prepared_column_order_is_the_stable_sort_of_g_idx(qtype):
         assert np.array_equal(got, want)
 
 
-def test_permute_cols_matches_a_gather():
+@pytest.mark.parametrize("offset", [0, 1])
+def test_permute_cols_matches_a_gather(offset):
+    # offset 0: rows staged in LDS; offset 1: a source view 2 bytes off alignment (direct gather)
     from quantized_mixture_experts_align_amd import moe_permute_cols
     wl = _act_order_workload("int4_g128")
     lw = W.make_weights(wl)
@@ -44,7 +46,8 @@ def test_permute_cols_matches_a_gather():
     E, H = lw.w13.g_idx.shape
     rng = np.random.default_rng(3)
     M, k = 23, 3
-    x = torch.from_numpy(rng.standard_normal((M, H)).astype(np.float32)).to(torch.bfloat16).cuda()
+    big = torch.from_numpy(rng.standard_normal((M, H + 8)).astype(np.float32)).to(torch.bfloat16).cuda()
+    x = big[:, offset: offset + H]
     slot_e = rng.integers(-1, E + 1, size=M * k).astype(np.int32)        # dead (-1) and off-range (E)
     out = torch.full((M * k, H), 7.0, dtype=torch.bfloat16, device="cuda")
     moe_permute_cols(x, layer.W13, torch.from_numpy(slot_e).cuda(), k, out=out)
