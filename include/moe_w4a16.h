@@ -57,15 +57,21 @@ typedef enum {
   MOE_Q_INT4_G128 = 0,    /* uint4b8: nibble u means u - 8; bf16 scale per 128 along K       */
   MOE_Q_NVFP4_G16 = 1,    /* E2M1 codes; float8 e4m3fn scale per 16 along K; fp32 global/expert */
   MOE_Q_MXFP4_G32 = 2,    /* E2M1 codes; E8M0 scale per 32 along K                            */
-  MOE_Q_INT4ZP_G128 = 3   /* asymmetric int4: unsigned nibble u, integer zero point z (0..15)
+  MOE_Q_INT4ZP_G128 = 3,  /* asymmetric int4: unsigned nibble u, integer zero point z (0..15)
                              and bf16 scale s per 128 along K; the weight is (u - z) * s     */
+  /* (range sentinels, never valid arguments: they make the type's range all of int32, so that
+     an unknown value reaches the library's validation and comes back as MOE_EINVAL)          */
+  MOE_Q_RANGE_MIN_ = -2147483647 - 1,
+  MOE_Q_RANGE_MAX_ = 2147483647
 } moe_qtype;
 
 typedef enum {
   MOE_ACT_SILU_MUL = 0,      /* gated: silu(gate) * up                                      */
   MOE_ACT_SWIGLU_ALPHA = 1,  /* gated: min(g,L) * sigmoid(alpha * min(g,L)) * (clamp(u,-L,L) + 1) */
-  MOE_ACT_RELU2 = 2          /* non-gated: relu(h)^2 (the sglang PR 31552 test's activation,
+  MOE_ACT_RELU2 = 2,         /* non-gated: relu(h)^2 (the sglang PR 31552 test's activation,
                                 is_gated=False; GEMM1 then has I rows, no gate/up halves)  */
+  MOE_ACT_RANGE_MIN_ = -2147483647 - 1,  /* range sentinels, as for moe_qtype */
+  MOE_ACT_RANGE_MAX_ = 2147483647
 } moe_act_kind;
 
 /* ----------------------------------------------------------------------------- errors */

@@ -85,7 +85,7 @@ __device__ __forceinline__ uint32_t requant4_finite(uint32_t d, float s, float r
 // PMAX = counts per lane (experts <= 64 * PMAX), U = items in flight per wave.
 template <int PMAX, int U>
 __global__ __launch_bounds__(kRqWaves * 64) void requant_kernel(
-    const uint8_t* __restrict__ x, uint8_t* out, const float* __restrict__ scales, int64_t sse,
+    const uint8_t* x, uint8_t* out, const float* __restrict__ scales, int64_t sse,  // out may be x
     int64_t ssm, int64_t ssg, const int32_t* __restrict__ masked_m,
     const float* __restrict__ tensor_scale, int E, int max_m, int K, int group, int chunks) {
   const int lane = threadIdx.x & 63;
