@@ -250,6 +250,8 @@ int moe_gemm_choose(const moe_weights* W, int64_t numel, int32_t block_m, int32_
  *   cfg      NULL for AUTO
  * Dequantised weights are rounded to bf16 before the bf16 x bf16 MFMA products (exact for
  * NVFP4 and MXFP4; int4 (u-8)*s is rounded like the Marlin kernel does).
+ * Act-order weights (W->perm != NULL) store their columns in group order: A must hold each
+ * slot's row with its columns in that order (moe_permute_cols, one row per slot, top_k = 1).
  */
 int moe_w4a16_gemm(const uint16_t* A, int64_t a_rows, int32_t lda, uint16_t* C, int32_t ldc,
                    const moe_weights* W, const int32_t* sorted_token_ids,
