@@ -103,3 +103,24 @@ def test_plain_grouping_as_act_order_equals_the_plain_layer(M):
     b = ao(*xs)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("variant", ["relu2", "interleaved"])
+def test_act_order_with_relu2_and_interleaved_rows(variant):
+    # the column order combined with the prepare's other row mappings: the non-gated relu2
+    # projection (GEMM1 has I rows), and gate/up rows arriving interleaved (gate j = row 2j)
+    kw = dict(act="relu2", routed_scaling_factor=0.625) if variant == "relu2" else dict(interleaved_w13=True)
+    wl = _act_order_workload("int4_g128", bias=True, **kw)
+    lw = W.make_weights(wl)
+    for M in (5, 300):
+        inp = W.make_inputs(wl, M, seed=11 + M)
+        layer = make_layer(wl, lw)
+        ws = layer.workspace(M)
+        announce(f"act-order {variant} M={M} block_m={ws.block_m}")
+        out = layer(*W.device_inputs(inp), ws=ws)
+        torch.cuda.synchronize()
+        got = W.bf16_to_float(out)
+        ref = oracle_layer(wl, lw, inp)
+        assert layer_violations(got, ref) == 0
+        assert rel_rms(got, ref) < 0.01
+
