@@ -116,7 +116,8 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
   constexpr int WB = 4 * NG * kTileBytes;                  //   weight tiles of the 4 waves,
   constexpr int SB = 4 * NG * 64;                          //   scales (64-B slot per tile)
   constexpr int STAGE = XB + WB + SB;
-  constexpr int LW = 3 * NG;                               // weight + scale loads per wave and step
+  constexpr int NWD = (NG + 1) / 2;                        // weight loads per wave and step
+  constexpr int LW = NWD + 1;                              // weight + scale loads per wave and step
   constexpr int kStages = stages_for<MG>();
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * STAGE];
   __shared__ int s_crow[BM];
@@ -171,7 +172,25 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
     sbase[g] = uniform_ptr(a.scales + ((int64_t)e * NT + ntile[g]) * (pair_grouped(QT) ? KT / 2 : KT) *
                                           scale_step_bytes(QT));
   }
-  const uint32_t loff = (uint32_t)lane * 4;  // a lane's dword of a 256-B weight or scale row
+  // One 16-byte-per-lane load fills two weight tiles of the wave (lanes 0-31 the 512 bytes of tile
+  // 2p, lanes 32-63 those of tile 2p+1, through their offset from tile 2p's base; with NG = 1
+  // lanes 32-63 stay idle), and one load brings the group scales of all NG tiles (lanes
+  // 16g .. 16g + SLANES - 1 those of tile g).  The bytes land where the tiles' LDS slots are
+  // contiguous: weights (w*NG + g) * 512, scales (w*NG + g) * 64.  Tile bases never decrease with
+  // g, so every offset is a non-negative distance inside one projection's buffer.
+  uint32_t woff[NWD];
+#pragma unroll
+  for (int p = 0; p < NWD; ++p) {
+    const uint32_t d = 2 * p + 1 < NG ? (uint32_t)(wbase[2 * p + 1] - wbase[2 * p]) : 0u;
+    woff[p] = lane < 32 ? (uint32_t)lane * 16 : d + (uint32_t)(lane - 32) * 16;
+  }
+  const int sg = lane >> 4, sr = lane & 15;
+  const bool s_act = sg < NG && sr < SLANES;
+  uint32_t sdist = 0;
+#pragma unroll
+  for (int g = 1; g < NG; ++g)
+    if (sg == g) sdist = (uint32_t)(sbase[g] - sbase[0]);
+  const uint32_t soffl = sdist + (uint32_t)sr * 4;
   auto issue = [&](int kt, int stage) {
     uint8_t* st = stage_ptr(stage);
     if (xwave) {
@@ -180,15 +199,12 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
         dma_to_lds<16>(xbase + kt * (kTileK * 2), xoff[l], st + (l * 256 + w * 64) * 16);
     }
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      uint8_t* wt = st + XB + (w * NG + g) * kTileBytes;
-      const uint8_t* src = wbase[g] + (int64_t)kt * kTileBytes;
-      dma_to_lds<4>(src, loff, wt);
-      dma_to_lds<4>(src + 256, loff, wt + 256);
-      const int64_t soff = (int64_t)(pair_grouped(QT) ? kt >> 1 : kt) * scale_step_bytes(QT);
-      if (lane < SLANES)
-        dma_to_lds<4>(sbase[g] + soff, loff, st + XB + WB + (w * NG + g) * 64);
+    for (int p = 0; p < NWD; ++p) {
+      uint8_t* wt = st + XB + (w * NG + 2 * p) * kTileBytes;
+      if (NG > 1 || lane < 32) dma_to_lds<16>(wbase[2 * p] + (int64_t)kt * kTileBytes, woff[p], wt);
     }
+    const int64_t soff = (int64_t)(pair_grouped(QT) ? kt >> 1 : kt) * scale_step_bytes(QT);
+    if (s_act) dma_to_lds<4>(sbase[0] + soff, soffl, st + XB + WB + (w * NG) * 64);
   };
 
   f32x4_t acc[NG][MG];
