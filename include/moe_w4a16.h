@@ -219,7 +219,8 @@ typedef enum {
  * (cfg NULL or kernel 0) picks one from the shapes. */
 typedef struct moe_gemm_config {
   int32_t kernel;         /* moe_gemm_kernel                                               */
-  int32_t ng;             /* 16-row weight tiles per wave: 1, 2 or 4                       */
+  int32_t ng;             /* 16-row weight tiles per wave: 1, 2 or 4 (2 or 4 with a fused
+                             gated activation: gate and up tiles in pairs; else MOE_EINVAL)   */
   int32_t ksplit;         /* DECODE: waves splitting K in one workgroup: 1, 2, 4 (or 8 when
                              gemv_rows = 0); capped at K/64 by the streaming kernel           */
   int32_t gemv_rows;      /* DECODE: blocks with at most this many live slots use dot

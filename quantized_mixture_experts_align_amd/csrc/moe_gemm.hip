@@ -70,6 +70,8 @@ static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64
     if (rc) return rc;
     if (paired && c.ng < 2) c.ng = 2;  // the fused gated epilogue needs gate/up tile pairs
   }
+  MOE_REQUIRE(!paired || c.ng == 2 || c.ng == 4, MOE_EINVAL,
+              "moe_w4a16_gemm_act: a fused gated activation needs ng 2 or 4 (gate/up tile pairs), got %d", c.ng);
   if (topk_ids) {
     MOE_REQUIRE(c.kernel == MOE_GEMM_DECODE && c.gemv_rows == 0, MOE_EUNSUPPORTED,
                 "moe_w4a16_gemm_act_routed: the fused align runs in the streaming decode kernel "
@@ -88,6 +90,7 @@ static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64
   const bool bias = W->bias != nullptr;
   if (c.kernel == MOE_GEMM_DECODE) {
     MOE_REQUIRE(block_m <= 16, MOE_EUNSUPPORTED, "moe_w4a16_gemm: decode kernel needs block_m <= 16");
+    MOE_REQUIRE(c.ksplit >= 1 && c.ksplit <= 8, MOE_EINVAL, "moe_w4a16_gemm: decode ksplit=%d (1..8)", c.ksplit);
     MOE_REQUIRE(c.gemv_rows >= 0 && c.gemv_rows <= 4, MOE_EINVAL, "moe_w4a16_gemm: gemv_rows=%d (0..4)",
                 c.gemv_rows);
     MOE_REQUIRE((int64_t)c.gemv_rows * W->K * 2 <= 32768, MOE_EUNSUPPORTED,

@@ -102,6 +102,18 @@ def test_entry_points_reject_bad_arguments_before_launch():
     cfg = L.MoeGemmConfig(L.GEMM_DECODE, 0, 3, 4)
     assert lib.moe_w4a16_gemm(s, 8, 4096, s, 8192, C.byref(W), s, s, s, 8, 8, 16, C.byref(cfg), None) \
         != L.MOE_OK
+    # explicit configurations no kernel can run are rejected before any arithmetic on them: a fused
+    # gated activation with one tile per wave (no gate/up pair), a decode K split of 0
+    a16 = C.c_void_p(4096)
+    for kernel, block_m in ((L.GEMM_MFMA, 64), (L.GEMM_DECODE, 16)):
+        cfg = L.MoeGemmConfig(kernel, 1, 1, 0)
+        assert lib.moe_w4a16_gemm_act(L.ACT["silu_mul"], 1.0, 1.0, a16, 8, 4096, a16, 4096, C.byref(W), s, s, s,
+                                      8, 8, block_m, C.byref(cfg), None) == L.MOE_EINVAL
+        assert b"ng 2 or 4" in lib.moe_last_error()
+    for gemv_rows in (0, 4):
+        cfg = L.MoeGemmConfig(L.GEMM_DECODE, 1, 0, gemv_rows)
+        assert lib.moe_w4a16_gemm(a16, 8, 4096, a16, 8192, C.byref(W), s, s, s, 8, 8, 16, C.byref(cfg),
+                                  None) == L.MOE_EINVAL and b"ksplit" in lib.moe_last_error()
     # relu2 takes a plain projection, the gated kinds a gate/up pair
     assert lib.moe_w4a16_gemm_act(L.ACT["relu2"], 1.0, 1.0, s, 8, 4096, s, 8192, C.byref(W), s, s, s, 8, 8, 16,
                                   None, None) == L.MOE_EINVAL and b"non-gated" in lib.moe_last_error()
