@@ -192,6 +192,7 @@ def run_cell(name: str, M: int, steps: int, warmup: int, want_cpu: bool, seed=No
     import quantized_mixture_experts_align_amd.ops as ops
     calls = {}
     orig, orig_act, orig_routed = ops.moe_w4a16_gemm, ops.moe_w4a16_gemm_act, ops.moe_w4a16_gemm_act_routed
+    orig_cmb = ops.moe_w4a16_gemm_combine
 
     def record(fn, key):
         def wrapper(*a, **kw):
@@ -203,10 +204,12 @@ def run_cell(name: str, M: int, steps: int, warmup: int, want_cpu: bool, seed=No
     ops.moe_w4a16_gemm_act = record(orig_act, "gemm13")
     ops.moe_w4a16_gemm_act_routed = record(orig_routed, "gemm13")
     ops.moe_w4a16_gemm = record(orig, "gemm2")
+    ops.moe_w4a16_gemm_combine = record(orig_cmb, "gemm2")  # (decode without norm: the weighted sum fused in)
     try:
         layer(x, ids, gw, ws=ws)
     finally:
         ops.moe_w4a16_gemm, ops.moe_w4a16_gemm_act, ops.moe_w4a16_gemm_act_routed = orig, orig_act, orig_routed
+        ops.moe_w4a16_gemm_combine = orig_cmb
     torch.cuda.synchronize()
     dur = {}
     for key, (fn, a, kw) in calls.items():
@@ -254,6 +257,7 @@ def run_cell(name: str, M: int, steps: int, warmup: int, want_cpu: bool, seed=No
                   "weight_GBps": round((bytes_13 + bytes_2) / step_s / 1e9, 1),
                   "TFLOPs": round((flops_13 + flops_2) / step_s / 1e12, 2),
                   "gemm13_us": round(d13 * 1e6, 2), "gemm2_us": round(dur["gemm2"] * 1e6, 2),
+                  "gemm2_fused_combine": calls["gemm2"][0] is orig_cmb,
                   "weight_bytes": bytes_13 + bytes_2, "flops": flops_13 + flops_2},
         "cold": {"ms_per_step": round(cold_s * 1e3, 4), "tokens_per_s": round(M / cold_s, 1),
                  "replays": len(cold), "note": "median graph replay after reading 1 GiB",

@@ -297,6 +297,36 @@ int moe_w4a16_gemm_act_routed(moe_act_kind kind, float alpha, float limit, const
                               int32_t* expert_ids, int32_t* num_tokens_post_padded,
                               int32_t* slot_local_ids, const moe_gemm_config* cfg, hipStream_t stream);
 
+/*
+ * The down GEMM with the no-norm top-k weighted sum fused in (the second half of the epilogue
+ * fusion the Muse Spark experiment's kernel_fn leaves to fused_post_expert_norm_weighted_sum; its
+ * "no norm" branch): one launch computes what moe_w4a16_gemm(A, M * top_k, lda, y, ldy, W, ...,
+ * numel = M * top_k, top_k = 1, ...) followed by moe_combine(y, topk_weights, slot_local_ids,
+ * NULL, 0, routed_scaling, M, top_k, N, out) computes, bit for bit (y is still written; the
+ * summation order and roundings are the combine's).  Decode batches only: block_m <= 16 and the
+ * streaming kernel (cfg NULL or AUTO, or kernel DECODE with gemv_rows 0).
+ *   A, lda, y, ldy, W, sorted/expert ids, num_tokens_post_padded, block_m: as moe_w4a16_gemm
+ *     (A row = slot; W a plain projection, not MOE_PREP_GATE_UP)
+ *   M, top_k        tokens and slots per token (numel = M * top_k, top_k <= 64)
+ *   topk_weights    device fp32 [M, top_k]; slot_local_ids device int32 [M, top_k] (moe_align's)
+ *   routed_scaling  multiplies every output (1 = none)
+ *   counters        device int32 [n_counters], n_counters >= M * ceil(N / (16 * ng)) (M * N / 16
+ *                   suffices for every ng): arrival counts per (token, strip of output columns).
+ *                   They must be zero on entry and are left zero by every completed call (clear
+ *                   them once after allocation); two calls that overlap in time must not share them
+ *   out             device bf16 [M, ldo], ldo >= N: every row written (zeros for tokens with no
+ *                   live slot)
+ * The last workgroup to store a token's rows of a column strip sums them (release fence, counter
+ * increment, acquire fence), so no second launch is needed.  Errors: MOE_EUNSUPPORTED for
+ * block_m > 16 or another kernel, MOE_ESIZE for too few counters, else as moe_w4a16_gemm.
+ */
+int moe_w4a16_gemm_combine(const uint16_t* A, int64_t a_rows, int32_t lda, uint16_t* y, int32_t ldy,
+                           const moe_weights* W, const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                           const int32_t* num_tokens_post_padded, int64_t M, int32_t top_k, int32_t block_m,
+                           const float* topk_weights, const int32_t* slot_local_ids, float routed_scaling,
+                           int32_t* counters, int64_t n_counters, uint16_t* out, int32_t ldo,
+                           const moe_gemm_config* cfg, hipStream_t stream);
+
 /* ----------------------------------------------------------------------------- act */
 
 /*

@@ -63,6 +63,9 @@ SIGNATURES = {
                                             C.POINTER(MoeGemmConfig), _P]),
     "moe_act": (C.c_int, [C.c_int, _P, _I32, _P, _I32, _I64, _I32, _P, _F, _F, _P]),
     "moe_combine": (C.c_int, [_P, _P, _P, _P, _F, _F, _I64, _I32, _I32, _P, _P]),
+    "moe_w4a16_gemm_combine": (C.c_int, [_P, _I64, _I32, _P, _I32, C.POINTER(MoeWeights), _P, _P, _P,
+                                         _I64, _I32, _I32, _P, _P, _F, _P, _I64, _P, _I32,
+                                         C.POINTER(MoeGemmConfig), _P]),
     "moe_fp8_requant_choose": (C.c_int, [_I32, _I32, _I32, _I32, _I32, C.POINTER(MoeRequantConfig)]),
     "moe_fp8_requant": (C.c_int, [_P, _P, _I64, _I64, _I64, _P, _P, _I32, _I32, _I32, _I32, _P,
                                   C.POINTER(MoeRequantConfig), _P]),

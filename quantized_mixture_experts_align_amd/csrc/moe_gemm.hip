@@ -26,11 +26,25 @@ static bool al(const void* p, uintptr_t n) { return ((uintptr_t)p & (n - 1)) == 
 // Routed mode (topk_ids set): the align of the numel <= kFusedAlignSlots slots is computed inside
 // the streaming kernel, and sorted_token_ids / expert_ids / num_tokens_post_padded / slot_local
 // are its outputs instead of inputs.
+// Fused weighted sum (moe_w4a16_gemm_combine): the combine's inputs and output.
+struct CombineSpec {
+  const float* gw;
+  const int32_t* live;
+  uint16_t* out;
+  int64_t ldo;
+  int32_t* cnt;
+  int64_t cnt_len;
+  int32_t k;
+  int64_t M;
+  float rsf;
+};
+
 static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64_t a_rows, int32_t lda,
                      uint16_t* C, int32_t ldc, const moe_weights* W, const int32_t* sorted_token_ids,
                      const int32_t* expert_ids, const int32_t* num_tokens_post_padded, int64_t numel,
                      int32_t top_k, int32_t block_m, const moe_gemm_config* cfg, hipStream_t stream,
-                     const int32_t* topk_ids = nullptr, int32_t expert_start = 0, int32_t* slot_local = nullptr) {
+                     const int32_t* topk_ids = nullptr, int32_t expert_start = 0, int32_t* slot_local = nullptr,
+                     const CombineSpec* cmb = nullptr) {
   MOE_REQUIRE(W, MOE_EINVAL, "moe_w4a16_gemm: null weights");
   MOE_REQUIRE(W->qtype >= 0 && W->qtype <= 3, MOE_EINVAL, "moe_w4a16_gemm: bad qtype %d", W->qtype);
   MOE_REQUIRE(W->n_experts >= 1 && W->N >= kTileN && W->N % kTileN == 0 && W->K >= kTileK &&
@@ -88,6 +102,24 @@ static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64
              topk_ids, expert_start, (int32_t)cap, (int32_t)cap_blocks, const_cast<int32_t*>(sorted_token_ids),
              const_cast<int32_t*>(expert_ids), const_cast<int32_t*>(num_tokens_post_padded), slot_local};
   const bool bias = W->bias != nullptr;
+  if (cmb) {
+    MOE_REQUIRE(c.kernel == MOE_GEMM_DECODE && c.gemv_rows == 0, MOE_EUNSUPPORTED,
+                "moe_w4a16_gemm_combine: the fused weighted sum runs in the streaming decode kernel "
+                "(block_m <= 16; kernel DECODE, gemv_rows 0)");
+    MOE_REQUIRE(c.ng == 1 || c.ng == 2 || c.ng == 4, MOE_EINVAL, "moe_w4a16_gemm_combine: ng=%d", c.ng);
+    const int64_t strips = (W->N / kTileN + c.ng - 1) / c.ng;
+    MOE_REQUIRE(cmb->cnt_len >= cmb->M * strips, MOE_ESIZE,
+                "moe_w4a16_gemm_combine: %lld counters, need %lld", (long long)cmb->cnt_len,
+                (long long)(cmb->M * strips));
+    a.cmb_gw = cmb->gw;
+    a.cmb_live = cmb->live;
+    a.cmb_out = cmb->out;
+    a.cmb_cnt = cmb->cnt;
+    a.cmb_k = cmb->k;
+    a.cmb_ntok = (int32_t)cmb->M;
+    a.cmb_ldo = cmb->ldo;
+    a.cmb_rsf = cmb->rsf;
+  }
   if (c.kernel == MOE_GEMM_DECODE) {
     MOE_REQUIRE(block_m <= 16, MOE_EUNSUPPORTED, "moe_w4a16_gemm: decode kernel needs block_m <= 16");
     MOE_REQUIRE(c.ksplit >= 1 && c.ksplit <= 8, MOE_EINVAL, "moe_w4a16_gemm: decode ksplit=%d (1..8)", c.ksplit);
@@ -139,6 +171,40 @@ extern "C" int moe_w4a16_gemm(const uint16_t* A, int64_t a_rows, int32_t lda, ui
                               const moe_gemm_config* cfg, hipStream_t stream) {
   return gemm_impl(kActNone, 0.f, 0.f, A, a_rows, lda, C, ldc, W, sorted_token_ids, expert_ids,
                    num_tokens_post_padded, numel, top_k, block_m, cfg, stream);
+}
+
+extern "C" int moe_w4a16_gemm_combine(const uint16_t* A, int64_t a_rows, int32_t lda, uint16_t* y, int32_t ldy,
+                                      const moe_weights* W, const int32_t* sorted_token_ids,
+                                      const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                                      int64_t M, int32_t top_k, int32_t block_m, const float* topk_weights,
+                                      const int32_t* slot_local_ids, float routed_scaling, int32_t* counters,
+                                      int64_t n_counters, uint16_t* out, int32_t ldo,
+                                      const moe_gemm_config* cfg, hipStream_t stream) {
+  MOE_REQUIRE(M >= 0 && M < (1 << 30) && top_k >= 1 && top_k <= 64, MOE_EINVAL,
+              "moe_w4a16_gemm_combine: M=%lld top_k=%d", (long long)M, top_k);
+  MOE_REQUIRE(W, MOE_EINVAL, "moe_w4a16_gemm_combine: null weights");
+  MOE_REQUIRE(!(W->flags & MOE_PREP_GATE_UP), MOE_EINVAL,
+              "moe_w4a16_gemm_combine: the weighted sum follows the down projection, not a gate/up pair");
+  MOE_REQUIRE(block_m >= 1 && block_m <= 16, MOE_EUNSUPPORTED,
+              "moe_w4a16_gemm_combine: block_m=%d outside 1..16 (the streaming decode kernel)", block_m);
+  if (M == 0) return ok();
+  MOE_REQUIRE(topk_weights && slot_local_ids && out && counters && y, MOE_EINVAL,
+              "moe_w4a16_gemm_combine: null pointer");
+  MOE_REQUIRE(ldo >= W->N && ((uintptr_t)out & 1) == 0, MOE_EINVAL,
+              "moe_w4a16_gemm_combine: ldo=%d below N=%d or misaligned out", ldo, W->N);
+  MOE_REQUIRE(((uintptr_t)counters & 3) == 0 && n_counters >= 0, MOE_EINVAL,
+              "moe_w4a16_gemm_combine: misaligned counters or negative count");
+  const int64_t numel = M * top_k;
+  moe_gemm_config c{};
+  if (cfg && cfg->kernel != MOE_GEMM_AUTO) {
+    c = *cfg;
+  } else {
+    int rc = moe_gemm_choose(W, numel, block_m, device_cu_count(), &c);
+    if (rc) return rc;
+  }
+  const CombineSpec cmb{topk_weights, slot_local_ids, out, ldo, counters, n_counters, top_k, M, routed_scaling};
+  return gemm_impl(kActNone, 0.f, 0.f, A, a_rows, lda, y, ldy, W, sorted_token_ids, expert_ids,
+                   num_tokens_post_padded, numel, 1, block_m, &c, stream, nullptr, 0, nullptr, &cmb);
 }
 
 extern "C" int moe_w4a16_gemm_act_routed(moe_act_kind kind, float alpha, float limit, const uint16_t* A,

@@ -42,6 +42,16 @@ struct GemmArgs {
   int32_t* eids_out;
   int32_t* ntpp_out;
   int32_t* slot_local_out;
+  // Fused top-k weighted sum without norm (streaming kernel, plain projection, top_k = 1 rows):
+  // with cmb_out set, the output rows C are still written, and the last item to finish a (token,
+  // column strip) sums the token's live rows of that strip into cmb_out.
+  const float* cmb_gw;     // [cmb_ntok, cmb_k] top-k weights
+  const int32_t* cmb_live; // [cmb_ntok, cmb_k] local expert id of each slot, -1 = dead
+  uint16_t* cmb_out;       // [cmb_ntok, cmb_ldo]
+  int32_t* cmb_cnt;        // [cmb_ntok, strips] arrival counters: zero on entry, left zero
+  int32_t cmb_k, cmb_ntok;
+  int64_t cmb_ldo;
+  float cmb_rsf;           // routed scaling factor
 };
 constexpr int kFusedAlignSlots = 64;  // one slot per lane of one wave
 

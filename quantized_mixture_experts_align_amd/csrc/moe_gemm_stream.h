@@ -85,9 +85,10 @@ __device__ int fused_align(const GemmArgs& a, int* f_rows, int* f_be, int* f_nbl
   return nb;
 }
 
-template <int QT, bool BIAS, int NG, int KS, int ACT, bool FA>
+template <int QT, bool BIAS, int NG, int KS, int ACT, bool FA, bool CMB>
 __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   static_assert(!act_paired<ACT>() || NG % 2 == 0, "the fused gated epilogue pairs gate and up tiles");
+  static_assert(!CMB || (ACT == kActNone && !FA), "the fused weighted sum follows a plain projection");
   constexpr int NGA = act_paired<ACT>() ? NG / 2 : NG;
   constexpr int D = NG >= 4 ? 4 : 8;  // ring depth (k-steps): about 9 KB of weights per wave
   __shared__ int t_e[kWin];
@@ -107,6 +108,14 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   __shared__ int f_nblk;
   const int nblocks = FA ? fused_align(a, f_rows, f_be, &f_nblk) : *a.ntpp / B;
   const int items = nblocks * NS;
+  if constexpr (CMB) {  // a token without a live slot sums to zero: no item ever reaches it
+    for (int t = blockIdx.x; t < a.cmb_ntok; t += gridDim.x) {
+      bool any = false;
+      for (int j = 0; j < a.cmb_k; ++j) any |= a.cmb_live[(int64_t)t * a.cmb_k + j] >= 0;
+      if (!any)
+        for (int c = tid; c < a.N; c += 64 * KS) a.cmb_out[(int64_t)t * a.cmb_ldo + c] = 0;
+    }
+  }
   // items split evenly over the whole grid (every workgroup gets floor or ceil of the mean, at
   // most kWin by the launch), so that no workgroup idles while others take an extra item
   const int i0 = (int)((int64_t)blockIdx.x * items / (int)gridDim.x);
@@ -193,6 +202,51 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     int cq = 0, cs = 0;
+    // Fused weighted sum (wave 0, once the workgroup's items are all stored): publish the rows
+    // (one release fence: a fence waits for every load in flight, so it is kept out of the
+    // streaming loop), count each item's arrival at its tokens' (token, strip) counters, and let
+    // the arrival that completes a token's live slots sum them, in slot order, exactly as the
+    // combine kernel does.  Release fence -> counter RMW -> acquire fence: every earlier arrival's
+    // rows are visible to the completing wave, whichever XCD wrote them.  The completing lane
+    // resets its counter.
+    auto combine_all = [&](int nq) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const int g = lane >> 4, r = lane & 15;  // lane -> column (tile g of the strip, row r)
+      for (int q = 0; q < nq; ++q) {
+        const int strip = (wb + q) % NS, e = t_e[q], s = t_row[q][m];
+        bool done = false;
+        int tok = 0;
+        if (lane < 16 && e >= 0 && s >= 0) {
+          tok = s / a.cmb_k;
+          int live = 0;
+          for (int j = 0; j < a.cmb_k; ++j) live += a.cmb_live[(int64_t)tok * a.cmb_k + j] >= 0;
+          int* c = a.cmb_cnt + (int64_t)tok * NS + strip;
+          if (__hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == live - 1) {
+            done = true;
+            __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+        uint64_t dm = __ballot(done);
+        if (dm == 0) continue;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        const bool col_ok = g < NG && strip * NG + g < NT;
+        const int col = (strip * NG + g) * kTileN + r;
+        while (dm) {
+          const int src = __ffsll((unsigned long long)dm) - 1;
+          dm &= dm - 1;
+          const int t = __shfl(tok, src);
+          if (!col_ok) continue;
+          float acc = 0.f;
+          for (int j = 0; j < a.cmb_k; ++j) {
+            const int64_t slot = (int64_t)t * a.cmb_k + j;
+            if (a.cmb_live[slot] < 0) continue;
+            acc = fmaf(a.cmb_gw[slot], bf16_to_f32(a.C[slot * a.ldc + col]), acc);
+          }
+          acc *= a.cmb_rsf;
+          a.cmb_out[(int64_t)t * a.cmb_ldo + col] = f32_to_bf16(acc);
+        }
+      }
+    };
     auto finish = [&](int q) {  // the item's partial sums are complete in every wave
       if constexpr (KS > 1) {
         if (w > 0)
@@ -258,29 +312,32 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
         }
       }
     }
+    if constexpr (CMB) {
+      if (w == 0) combine_all(wn);
+    }
   }
 }
 
-template <int QT, bool BIAS, int NG, int ACT, bool FA>
+template <int QT, bool BIAS, int NG, int ACT, bool FA, bool CMB>
 static int launch_stream_ng(const GemmArgs& a, int ks, int grid, hipStream_t st) {
   switch (ks) {
-    case 1: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 1, ACT, FA>), dim3(grid), dim3(64), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 2, ACT, FA>), dim3(grid), dim3(128), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 4, ACT, FA>), dim3(grid), dim3(256), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 8, ACT, FA>), dim3(grid), dim3(512), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 1, ACT, FA, CMB>), dim3(grid), dim3(64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 2, ACT, FA, CMB>), dim3(grid), dim3(128), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 4, ACT, FA, CMB>), dim3(grid), dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 8, ACT, FA, CMB>), dim3(grid), dim3(512), 0, st, a); break;
     default: return fail(MOE_EINVAL, "moe_w4a16_gemm: ksplit=%d (1, 2, 4 or 8)", ks);
   }
   return check_launch("moe_w4a16_gemm (decode stream)");
 }
 
-template <int QT, bool BIAS, int ACT, bool FA>
+template <int QT, bool BIAS, int ACT, bool FA, bool CMB = false>
 static int launch_stream_b(const GemmArgs& a, const moe_gemm_config& c, int grid, hipStream_t st) {
   if constexpr (!act_paired<ACT>()) {
-    if (c.ng == 1) return launch_stream_ng<QT, BIAS, 1, ACT, FA>(a, c.ksplit, grid, st);
+    if (c.ng == 1) return launch_stream_ng<QT, BIAS, 1, ACT, FA, CMB>(a, c.ksplit, grid, st);
   }
   switch (c.ng) {
-    case 2: return launch_stream_ng<QT, BIAS, 2, ACT, FA>(a, c.ksplit, grid, st);
-    case 4: return launch_stream_ng<QT, BIAS, 4, ACT, FA>(a, c.ksplit, grid, st);
+    case 2: return launch_stream_ng<QT, BIAS, 2, ACT, FA, CMB>(a, c.ksplit, grid, st);
+    case 4: return launch_stream_ng<QT, BIAS, 4, ACT, FA, CMB>(a, c.ksplit, grid, st);
     default: return fail(MOE_EINVAL, "moe_w4a16_gemm: decode ng=%d (1, 2 or 4; 2 or 4 with a fused gated activation)", c.ng);
   }
 }
@@ -289,8 +346,9 @@ static int launch_stream_b(const GemmArgs& a, const moe_gemm_config& c, int grid
 template <int QT, bool BIAS, int ACT>
 static int launch_stream_fa(const GemmArgs& a, const moe_gemm_config& c, int grid, hipStream_t st) {
   if constexpr (ACT == kActNone) {
-    return a.topk_ids ? fail(MOE_EUNSUPPORTED, "moe_w4a16_gemm: the fused align needs a fused activation")
-                      : launch_stream_b<QT, BIAS, ACT, false>(a, c, grid, st);
+    if (a.topk_ids) return fail(MOE_EUNSUPPORTED, "moe_w4a16_gemm: the fused align needs a fused activation");
+    return a.cmb_out ? launch_stream_b<QT, BIAS, ACT, false, true>(a, c, grid, st)
+                     : launch_stream_b<QT, BIAS, ACT, false>(a, c, grid, st);
   } else {
     return a.topk_ids ? launch_stream_b<QT, BIAS, ACT, true>(a, c, grid, st)
                       : launch_stream_b<QT, BIAS, ACT, false>(a, c, grid, st);

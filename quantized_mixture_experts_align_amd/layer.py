@@ -30,6 +30,7 @@ class Workspace:
     out: torch.Tensor
     cfgs: Optional[tuple] = None    # (gate/up, down) GEMM launch configurations
     perm: Optional[torch.Tensor] = None   # act-order: the gathered A of a GEMM [numel, max(H, I)]
+    counters: Optional[torch.Tensor] = None  # fused weighted sum: arrival counters, kept zero
 
 
 class MoELayer:
@@ -107,14 +108,24 @@ class MoELayer:
                          torch.empty((numel, self.I), **bf), torch.empty((M, self.H), **bf),
                          self.configs(M, B), perm)
 
+    def _combinable(self, B: int, cfg2) -> bool:
+        # the weighted sum fuses into the streaming decode kernel's down GEMM when there is no norm
+        return (self.norm_w is None and B <= 16 and cfg2.kernel == L.GEMM_DECODE
+                and cfg2.gemv_rows == 0)
+
     def forward(self, x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
                 ws: Optional[Workspace] = None, cfg13=None, cfg2=None,
-                fused_act: bool = True, fused_align: Optional[bool] = None) -> torch.Tensor:
+                fused_act: bool = True, fused_align: Optional[bool] = None,
+                fused_combine: bool = False) -> torch.Tensor:
         """align -> gate/up GEMM -> activation -> down GEMM -> combine.  With fused_act the
         activation runs in the GEMM1 epilogue (bitwise the same result, one launch and one
         [numel, N13] round trip less); for a gated activation cfg13 then needs ng 2 or 4.
         With fused_align (default: whenever it applies -- at most 64 slots, the streaming decode
-        kernel, fused_act) the align runs inside that same launch as well (bitwise the same)."""
+        kernel, fused_act) the align runs inside that same launch as well (bitwise the same).
+        With fused_combine (no norm, the streaming decode kernel for the down GEMM) the weighted
+        sum runs in the down GEMM's launch (bitwise the same; counters are added to the workspace
+        on first use).  It is off by default: measured on MI355X, its cross-XCD release/acquire
+        fences cost more than the combine launch they save."""
         M = x.shape[0]
         if ws is None:
             ws = self.workspace(M, device=x.device)
@@ -162,6 +173,16 @@ class MoELayer:
         if self.act_order[1]:
             a2 = ops.moe_permute_cols(ws.a, self.W2, loc.view(-1), 1,
                                       out=ws.perm[: numel * self.W2.K].view(numel, self.W2.K))
+        if fused_combine:
+            if not self._combinable(B, cfg2):
+                raise ValueError("fused_combine needs no norm, block_m <= 16 and the streaming decode "
+                                 "kernel for the down GEMM")
+            counters = ws.counters
+            if counters is None or counters.numel() < M * (self.W2.N // 16):
+                counters = ws.counters = ops.combine_counters(M, self.W2, x.device)
+            return ops.moe_w4a16_gemm_combine(a2, self.W2, sorted_ids, eids, ntpp, topk_weights, loc, B,
+                                              counters, y, out=ws.out,
+                                              routed_scaling_factor=self.routed_scaling_factor, cfg=cfg2)
         ops.moe_w4a16_gemm(a2, self.W2, sorted_ids, eids, ntpp, numel, 1, B, out=y, cfg=cfg2)
         return ops.moe_combine(y, topk_weights, loc, self.norm_w, self.eps, out=ws.out,
                                routed_scaling_factor=self.routed_scaling_factor)

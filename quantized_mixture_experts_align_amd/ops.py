@@ -250,6 +250,39 @@ def moe_act(kind: str, h: torch.Tensor, I: int, slot_local_ids: Optional[torch.T
     return out
 
 
+def combine_counters(M: int, W: PreparedWeights, device) -> torch.Tensor:
+    """Zeroed arrival counters for moe_w4a16_gemm_combine (M * N / 16, enough for every ng); every
+    completed call leaves them zero, so one buffer serves calls of up to M tokens in turn."""
+    return torch.zeros(max(1, M * (W.N // 16)), dtype=torch.int32, device=device)
+
+
+def moe_w4a16_gemm_combine(A: torch.Tensor, W: PreparedWeights, sorted_token_ids: torch.Tensor,
+                           expert_ids: torch.Tensor, num_tokens_post_padded: torch.Tensor,
+                           topk_weights: torch.Tensor, slot_local_ids: torch.Tensor, block_m: int,
+                           counters: torch.Tensor, y: torch.Tensor, out: Optional[torch.Tensor] = None,
+                           routed_scaling_factor: float = 1.0,
+                           cfg: Optional[L.MoeGemmConfig] = None) -> torch.Tensor:
+    """Down GEMM (A row = slot) with the no-norm top-k weighted sum fused in: y[slot] as
+    moe_w4a16_gemm, out[t] = rsf * sum_s g[t, s] * y[t * k + s] over live slots; out is [M, N]."""
+    _need(A, torch.bfloat16, "A")
+    _need(y, torch.bfloat16, "y")
+    _need(topk_weights, torch.float32, "topk_weights")
+    _need(slot_local_ids, torch.int32, "slot_local_ids")
+    _need(counters, torch.int32, "counters")
+    M, k = topk_weights.shape
+    if out is None:
+        out = torch.empty((M, W.N), dtype=torch.bfloat16, device=A.device)
+    _need(out, torch.bfloat16, "out")
+    L.check(L.lib().moe_w4a16_gemm_combine(_ptr(A), A.shape[0], A.stride(0), _ptr(y), y.stride(0),
+                                           C.byref(W.desc), _ptr(sorted_token_ids), _ptr(expert_ids),
+                                           _ptr(num_tokens_post_padded), M, k, block_m, _ptr(topk_weights),
+                                           _ptr(slot_local_ids), routed_scaling_factor, _ptr(counters),
+                                           counters.numel(), _ptr(out), out.stride(0),
+                                           None if cfg is None else C.byref(cfg), _stream()),
+            "moe_w4a16_gemm_combine")
+    return out
+
+
 def moe_combine(y: torch.Tensor, topk_weights: torch.Tensor, slot_local_ids: torch.Tensor,
                 norm_w: Optional[torch.Tensor] = None, eps: float = 1e-8,
                 out: Optional[torch.Tensor] = None, routed_scaling_factor: float = 1.0) -> torch.Tensor:

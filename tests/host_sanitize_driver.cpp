@@ -146,7 +146,7 @@ int main() {
   CHECK(moe_permute_cols(s16, 256, 2, g32, 256, 4, g32, 8, d16 + 1, 256, nullptr) == MOE_EINVAL);
   CHECK(moe_permute_cols(nullptr, 256, 2, nullptr, 256, 4, nullptr, 0, nullptr, 256, nullptr) == MOE_OK);
 
-  CHECK(moe_abi_version() == 3);
+  CHECK(moe_abi_version() == 4);
   if (failures) {
     std::printf("%d checks failed\n", failures);
     return 1;
