@@ -77,12 +77,18 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     // prefix) and total, then the padded totals scanned over the lanes; one barrier instead of three
     if (w == 0) {
       int t = 0;
-      if (lane < n_local)
-        for (int v = 0; v < nwv; ++v) {
-          const int c = cnt[v * n_local + lane];
+      if (lane < n_local) {
+        // all counts first, then the prefixes: interleaved, every read would wait for the
+        // previous write (the compiler cannot tell the rows apart)
+        int c[kAlignWaves];
+#pragma unroll
+        for (int v = 0; v < kAlignWaves; ++v) c[v] = cnt[v * n_local + lane];
+#pragma unroll
+        for (int v = 0; v < kAlignWaves; ++v) {
           cnt[v * n_local + lane] = t;
-          t += c;
+          t += c[v];
         }
+      }
       const int p = lane < n_local ? (t + B - 1) / B * B : 0;
       int incl = p;
       for (int d = 1; d < 64; d <<= 1) {
