@@ -114,6 +114,23 @@ def test_entry_points_reject_bad_arguments_before_launch():
         cfg = L.MoeGemmConfig(L.GEMM_DECODE, 1, 0, gemv_rows)
         assert lib.moe_w4a16_gemm(a16, 8, 4096, a16, 8192, C.byref(W), s, s, s, 8, 8, 16, C.byref(cfg),
                                   None) == L.MOE_EINVAL and b"ksplit" in lib.moe_last_error()
+    # the fused weighted sum: decode block sizes, a plain projection, enough counters, every buffer
+    Wd = L.MoeWeights(1, 32, 4096, 4096, 4096, 4096, 0, 0, 256, 256, None, None)    # NVFP4 down proj.
+    Wd.global_scale = 256
+    cmb = lib.moe_w4a16_gemm_combine
+    def call(W=Wd, M=2, k=8, B=16, cnt=a16, n_cnt=2 * 256, out=a16, ldo=4096, gw=a16, cfg=None):
+        return cmb(a16, M * k, 4096, a16, 4096, C.byref(W), s, s, s, M, k, B, gw, a16, 1.0, cnt, n_cnt, out, ldo,
+                   cfg, None)
+    assert call(B=32) == L.MOE_EUNSUPPORTED and b"block_m" in lib.moe_last_error()
+    assert call(W=W) == L.MOE_EINVAL and b"gate/up" in lib.moe_last_error()          # W: a gate/up pair
+    assert call(M=-1) == L.MOE_EINVAL
+    assert call(k=65) == L.MOE_EINVAL
+    assert call(gw=None) == L.MOE_EINVAL and b"null" in lib.moe_last_error()
+    assert call(ldo=2048) == L.MOE_EINVAL
+    assert call(n_cnt=2 * 256 // 4 - 1, cfg=C.byref(L.MoeGemmConfig(L.GEMM_DECODE, 4, 1, 0))) == L.MOE_ESIZE
+    assert b"counters" in lib.moe_last_error()
+    assert call(cfg=C.byref(L.MoeGemmConfig(L.GEMM_DECODE, 2, 1, 4))) == L.MOE_EUNSUPPORTED  # dot-product path
+    assert call(M=0, gw=None, cnt=None, out=None) == L.MOE_OK                          # nothing to do
     # relu2 takes a plain projection, the gated kinds a gate/up pair
     assert lib.moe_w4a16_gemm_act(L.ACT["relu2"], 1.0, 1.0, s, 8, 4096, s, 8192, C.byref(W), s, s, s, 8, 8, 16,
                                   None, None) == L.MOE_EINVAL and b"non-gated" in lib.moe_last_error()
