@@ -119,7 +119,8 @@ def cpu_baseline(wl, lw, inp, budget_s: float = 12.0) -> dict:
 _LAYERS: dict = {}   # prepared weights reused across cells of one weight set
 
 
-def run_cell(name: str, M: int, steps: int, warmup: int, want_cpu: bool, seed=None) -> dict:
+def run_cell(name: str, M: int, steps: int, warmup: int, want_cpu: bool, seed=None,
+             fused_combine: bool = False) -> dict:
     import torch
     import workloads as W
     from quantized_mixture_experts_align_amd import MoELayer
@@ -153,12 +154,12 @@ def run_cell(name: str, M: int, steps: int, warmup: int, want_cpu: bool, seed=No
 
     stream = torch.cuda.current_stream()
     for _ in range(3):
-        layer(x, ids, gw, ws=ws)
+        layer(x, ids, gw, ws=ws, fused_combine=fused_combine)
     torch.cuda.synchronize()
     # ---- value: graph replay of one step
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        layer(x, ids, gw, ws=ws)
+        layer(x, ids, gw, ws=ws, fused_combine=fused_combine)
     torch.cuda.synchronize()
     for _ in range(warmup):
         g.replay()
@@ -206,7 +207,7 @@ def run_cell(name: str, M: int, steps: int, warmup: int, want_cpu: bool, seed=No
     ops.moe_w4a16_gemm = record(orig, "gemm2")
     ops.moe_w4a16_gemm_combine = record(orig_cmb, "gemm2")  # (decode without norm: the weighted sum fused in)
     try:
-        layer(x, ids, gw, ws=ws)
+        layer(x, ids, gw, ws=ws, fused_combine=fused_combine)
     finally:
         ops.moe_w4a16_gemm, ops.moe_w4a16_gemm_act, ops.moe_w4a16_gemm_act_routed = orig, orig_act, orig_routed
         ops.moe_w4a16_gemm_combine = orig_cmb
@@ -251,7 +252,8 @@ def run_cell(name: str, M: int, steps: int, warmup: int, want_cpu: bool, seed=No
         "data": "synthetic",
         "config": {"workload": wl.name, "qtype": wl.qtype, "M": M, "top_k": wl.top_k,
                    "n_local": wl.n_local, "n_global": wl.n_global, "H": wl.H, "I": wl.I,
-                   "block_m": ws.block_m, "live_slots": live, "touched_experts": touched},
+                   "block_m": ws.block_m, "live_slots": live, "touched_experts": touched,
+                   "fused_combine": fused_combine},
         "roofline": roof,
         "layer": {**layer_fracs(bytes_13 + bytes_2, flops_13 + flops_2, step_s),
                   "weight_GBps": round((bytes_13 + bytes_2) / step_s / 1e9, 1),
@@ -388,6 +390,8 @@ def main() -> int:
     ap.add_argument("--M", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="one line per configuration cell")
+    ap.add_argument("--fused-combine", action="store_true",
+                    help="decode layers without norm: the weighted sum fused into the down GEMM")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only copy a buffer of this many MiB 10 times (reference kernel of known "
                          "traffic for calibrating the HBM byte counters)")
@@ -426,7 +430,7 @@ def main() -> int:
         print(f"unknown workload {name!r}; one of {list(W.WORKLOADS)}", file=sys.stderr)
         return 2
     M = a.M or W.WORKLOADS[name].Ms[0]
-    r = run_cell(name, M, a.steps, a.warmup, not a.no_cpu_baseline)
+    r = run_cell(name, M, a.steps, a.warmup, not a.no_cpu_baseline, fused_combine=a.fused_combine)
     print(json.dumps(r), flush=True)
     return 0
 
