@@ -231,10 +231,12 @@ typedef struct moe_gemm_config {
 } moe_gemm_config;
 
 /* Host heuristics (pure host functions).  moe_choose_block_m: block_m for the align from the
- * slot count.  moe_gemm_choose: the GEMM configuration for projection W; `numel` is the number
+ * slot count numel = M * top_k, the local experts, the slots expected to be live on this slice
+ * (expected_live <= 0: all of them) and the gate/up reduction length K (<= 0: unknown, taken as
+ * long).  moe_gemm_choose: the GEMM configuration for projection W; `numel` is the number
  * of slots expected to be live (M * top_k when unknown, or the expected local share of it -- a
  * launch hint only, never a correctness input), num_cus <= 0 means 256. */
-int moe_choose_block_m(int64_t numel, int32_t n_local, int32_t* block_m);
+int moe_choose_block_m(int64_t numel, int32_t n_local, int64_t expected_live, int32_t K, int32_t* block_m);
 int moe_gemm_choose(const moe_weights* W, int64_t numel, int32_t block_m, int32_t num_cus,
                     moe_gemm_config* cfg);
 

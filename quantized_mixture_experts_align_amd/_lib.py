@@ -52,7 +52,7 @@ SIGNATURES = {
                                     _SZ, C.POINTER(MoeWeights), _P]),
     "moe_permute_cols": (C.c_int, [_P, _I64, _I32, _P, _I32, _I32, _P, _I64, _P, _I64, _P]),
     "moe_norm_weight": (C.c_int, [_P, _I32, _P, _P]),
-    "moe_choose_block_m": (C.c_int, [_I64, _I32, C.POINTER(_I32)]),
+    "moe_choose_block_m": (C.c_int, [_I64, _I32, _I64, _I32, C.POINTER(_I32)]),
     "moe_gemm_choose": (C.c_int, [C.POINTER(MoeWeights), _I64, _I32, _I32, C.POINTER(MoeGemmConfig)]),
     "moe_w4a16_gemm": (C.c_int, [_P, _I64, _I32, _P, _I32, C.POINTER(MoeWeights), _P, _P, _P,
                                  _I64, _I32, _I32, C.POINTER(MoeGemmConfig), _P]),

@@ -33,7 +33,7 @@ using namespace moe;
 
 extern "C" const char* moe_last_error(void) { return g_err; }
 
-extern "C" int32_t moe_abi_version(void) { return 4; }
+extern "C" int32_t moe_abi_version(void) { return 5; }
 
 extern "C" int moe_align_capacity(int64_t M, int32_t top_k, int32_t n_local, int32_t block_m,
                                   int64_t* sorted_len, int64_t* blocks_len) {
@@ -96,19 +96,29 @@ extern "C" int moe_w4a16_prepared_size(moe_qtype q, int32_t E, int32_t N, int32_
 
 // BLOCK_SIZE_M for the align.  The Muse Spark experiment picks from (8, 16, 32, 48, 64) by the
 // expected rows per expert; here the choice also selects the kernel: up to 16 rows per local
-// expert (if every slot were local) go to the decode kernel, larger counts to MFMA tiles of
-// 32/64/128 rows.  Counting every slot (not only the expected local share) keeps skewed routing,
-// where a few local experts take most slots, on the MFMA tiles that share weight reads.
+// expert (if every slot were local) go to the streaming decode kernel, larger counts to MFMA
+// tiles of 32/64/128 rows.  Counting every slot (not only the expected local share) keeps skewed
+// routing, where a few local experts take most slots, on the MFMA tiles that share weight reads.
 // 128-row tiles halve the dequantisation per flop against 64-row ones but leave half as many
 // workgroups; measured, they pay once an expert averages 256 rows and there are at least 8192
 // slots (64 full blocks), below that the smaller grid and the padding cost more.
-extern "C" int moe_choose_block_m(int64_t numel, int32_t n_local, int32_t* block_m) {
+// Within the decode range, once about 32 slots are expected live the MFMA kernel with 32-row
+// blocks streams the weights faster than the streaming kernel (measured, whole layer: MXFP4 with
+// 32 live slots 105.2 -> 96.5 us, 128 -> 217 from 256 us; the NVFP4 slice with 32 and 64 live
+// 155 -> 147 and 160 -> 153 us; with 16 live slots the streaming kernel still wins, 59 against
+// 74 and 95 against 113 us).  For a short K (<= 1024, int4 here) the streaming kernel with the
+// align fused in (<= 64 slots) stays ahead up to 64 slots (22.6 against 25.5 us at 64).
+extern "C" int moe_choose_block_m(int64_t numel, int32_t n_local, int64_t expected_live, int32_t K,
+                                  int32_t* block_m) {
   MOE_REQUIRE(block_m && numel >= 0 && n_local >= 1, MOE_EINVAL, "moe_choose_block_m: bad arguments");
   const double rows = (double)numel / n_local;
+  const int64_t live = expected_live > 0 ? std::min(expected_live, numel) : numel;
   int b = 16;
   if (rows > 16) b = 32;
   if (rows > 48) b = 64;
   if (rows >= 256 && numel >= 8192) b = 128;
+  const bool short_k_fused = K > 0 && K <= 1024 && numel <= 64;
+  if (b == 16 && live >= 32 && !short_k_fused) b = 32;
   *block_m = b;
   return ok();
 }

@@ -85,7 +85,7 @@ class MoELayer:
         return max(1, -(-numel * self.n_local // self.n_global))
 
     def block_m(self, M: int) -> int:
-        return ops.choose_block_m(M * self.top_k, self.n_local)
+        return ops.choose_block_m(M * self.top_k, self.n_local, self.expected_local_slots(M), self.W13.K)
 
     def configs(self, M: int, block_m: int):
         """GEMM launch configurations (gate/up, down) for a batch of M tokens."""

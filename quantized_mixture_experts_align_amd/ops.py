@@ -39,9 +39,11 @@ def align_capacity(M: int, top_k: int, n_local: int, block_m: int):
     return s.value, b.value
 
 
-def choose_block_m(numel: int, n_local: int) -> int:
+def choose_block_m(numel: int, n_local: int, expected_live: int = 0, K: int = 0) -> int:
+    """block_m for the align: numel = M * top_k, expected_live = slots expected on this slice
+    (0: all), K = the gate/up reduction length (0: unknown)."""
     b = C.c_int32()
-    L.check(L.lib().moe_choose_block_m(numel, n_local, C.byref(b)), "moe_choose_block_m")
+    L.check(L.lib().moe_choose_block_m(numel, n_local, expected_live, K, C.byref(b)), "moe_choose_block_m")
     return b.value
 
 

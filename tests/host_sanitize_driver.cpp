@@ -92,7 +92,7 @@ int main() {
   // ---- heuristics
   int32_t bm = 0, prev = 0;
   for (int64_t numel = 0; numel <= (1 << 18); numel = numel ? numel * 2 : 1) {
-    CHECK(moe_choose_block_m(numel, 32, &bm) == MOE_OK);
+    CHECK(moe_choose_block_m(numel, 32, numel / 4, 4096, &bm) == MOE_OK);
     CHECK(bm == 16 || bm == 32 || bm == 64 || bm == 128);
     CHECK(bm >= prev);
     prev = bm;
@@ -146,7 +146,7 @@ int main() {
   CHECK(moe_permute_cols(s16, 256, 2, g32, 256, 4, g32, 8, d16 + 1, 256, nullptr) == MOE_EINVAL);
   CHECK(moe_permute_cols(nullptr, 256, 2, nullptr, 256, 4, nullptr, 0, nullptr, 256, nullptr) == MOE_OK);
 
-  CHECK(moe_abi_version() == 4);
+  CHECK(moe_abi_version() == 5);
   if (failures) {
     std::printf("%d checks failed\n", failures);
     return 1;

@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(lib, n), n
         assert n in L.SIGNATURES, f"{n} has no binding"
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
 
 
 def test_weights_descriptor_matches_the_c_struct():
@@ -192,6 +192,18 @@ def test_block_m_heuristic_is_monotone_and_picks_kernels():
     assert P.choose_block_m(8, 32) == 16            # decode slice
     assert P.choose_block_m(4608, 8) == 64          # int4 prefill, 576 rows per expert
     assert P.choose_block_m(32768, 32) == 128       # NVFP4 slice, 1024 rows per expert
+    # decode range: 16-slot streaming blocks up to about 32 expected live slots, then 32-slot MFMA
+    # blocks; a short K keeps the streaming kernel (with its fused align) up to 64 slots
+    assert P.choose_block_m(128, 32, 16, 4096) == 16     # NVFP4 slice M=16: 16 live
+    assert P.choose_block_m(256, 32, 32, 4096) == 32     # NVFP4 slice M=32: 32 live
+    assert P.choose_block_m(16, 128, 16, 2880) == 16     # MXFP4 M=4
+    assert P.choose_block_m(32, 128, 32, 2880) == 32     # MXFP4 M=8
+    assert P.choose_block_m(1024, 128, 1024, 2880) == 32  # MXFP4 M=256: 8 rows per expert
+    assert P.choose_block_m(64, 8, 64, 512) == 16        # int4 M=32: the fused align range
+    assert P.choose_block_m(96, 8, 96, 512) == 32        # int4 M=48
+    assert P.choose_block_m(64, 8, 64, 0) == 32          # K unknown: taken as long
+    for numel in range(0, 300, 7):                       # expected_live is capped by numel
+        assert P.choose_block_m(numel, 64, 1 << 40, 4096) == P.choose_block_m(numel, 64, 0, 4096)
 
 
 def _W(q, E, N, K):

@@ -85,7 +85,8 @@ def test_gemm_matches_oracle(qtype, kind, which):
     B, cfg = CFGS[kind]
     M = 5 if kind.startswith("decode") else 61
     if B is None:
-        B = P.choose_block_m(M * W.small_workload(qtype).top_k, W.small_workload(qtype).n_local)
+        wl = W.small_workload(qtype)
+        B = P.choose_block_m(M * wl.top_k, wl.n_local, 0, wl.H)
     print(f"gemm {qtype} {kind} W{which} M={M} B={B}", flush=True)
     got, ref, _ = _gemm_case(qtype, which, M, B, cfg)
     err = np.abs(got - ref)
