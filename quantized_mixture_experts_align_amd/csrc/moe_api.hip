@@ -102,12 +102,11 @@ extern "C" int moe_w4a16_prepared_size(moe_qtype q, int32_t E, int32_t N, int32_
 // 128-row tiles halve the dequantisation per flop against 64-row ones but leave half as many
 // workgroups; measured, they pay once an expert averages 256 rows and there are at least 8192
 // slots (64 full blocks), below that the smaller grid and the padding cost more.
-// Within the decode range, once about 32 slots are expected live the MFMA kernel with 32-row
-// blocks streams the weights faster than the streaming kernel (measured, whole layer: MXFP4 with
-// 32 live slots 105.2 -> 96.5 us, 128 -> 217 from 256 us; the NVFP4 slice with 32 and 64 live
-// 155 -> 147 and 160 -> 153 us; with 16 live slots the streaming kernel still wins, 59 against
-// 74 and 95 against 113 us).  For a short K (<= 1024, int4 here) the streaming kernel with the
-// align fused in (<= 64 slots) stays ahead up to 64 slots (22.6 against 25.5 us at 64).
+// Within the decode range the kernel is chosen by moe_gemm_choose (16-slot blocks run either the
+// streaming kernel or the MFMA kernel); only a short K (<= 1024, int4 here) beyond the fused-align
+// range (> 64 slots) with about 32 or more live slots takes 32-slot MFMA blocks (measured, whole
+// int4 layer: 22.6 us streaming against 25.5 us MFMA at 64 slots, tie at 96, 27.8 against 25.7 at
+// 128; the streaming kernel there also takes the align fused in).
 extern "C" int moe_choose_block_m(int64_t numel, int32_t n_local, int64_t expected_live, int32_t K,
                                   int32_t* block_m) {
   MOE_REQUIRE(block_m && numel >= 0 && n_local >= 1, MOE_EINVAL, "moe_choose_block_m: bad arguments");
@@ -117,11 +116,29 @@ extern "C" int moe_choose_block_m(int64_t numel, int32_t n_local, int64_t expect
   if (rows > 16) b = 32;
   if (rows > 48) b = 64;
   if (rows >= 256 && numel >= 8192) b = 128;
-  const bool short_k_fused = K > 0 && K <= 1024 && numel <= 64;
-  if (b == 16 && live >= 32 && !short_k_fused) b = 32;
+  if (b == 16 && live >= 32 && K > 0 && K <= 1024 && numel > 64) b = 32;
   *block_m = b;
   return ok();
 }
+
+namespace moe {
+// The streaming decode kernel over min(numel, E) live blocks.  Measured (cold weights, NVFP4 and
+// MXFP4 slices): four 16-row tiles per wave once about 8 blocks are live, else two; then the
+// smallest K split that gives at least 24 waves per CU.  The one-column MFMA streams faster than
+// the dot-product path (gemv_rows > 0), which stays available.
+moe_gemm_config stream_config(const moe_weights* W, int64_t numel, int num_cus) {
+  moe_gemm_config c{};
+  c.kernel = MOE_GEMM_DECODE;
+  c.gemv_rows = 0;
+  const int64_t nt = W->N / kTileN;
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(numel, W->n_experts));
+  c.ng = blocks >= 8 ? 4 : 2;
+  const int64_t items = blocks * ((nt + c.ng - 1) / c.ng);
+  c.ksplit = 1;
+  while (c.ksplit < 8 && items * c.ksplit < 24ll * (num_cus > 0 ? num_cus : 256)) c.ksplit *= 2;
+  return c;
+}
+}  // namespace moe
 
 extern "C" int moe_gemm_choose(const moe_weights* W, int64_t numel, int32_t block_m, int32_t num_cus,
                                moe_gemm_config* cfg) {
@@ -130,18 +147,17 @@ extern "C" int moe_gemm_choose(const moe_weights* W, int64_t numel, int32_t bloc
   if (num_cus <= 0) num_cus = 256;
   moe_gemm_config c{};
   const int nt = W->N / kTileN;
-  if (block_m <= 16) {
-    // decode: the streaming kernel over min(numel, E) live blocks.  Measured (cold weights, NVFP4
-    // and MXFP4 slices): four 16-row tiles per wave once about 8 blocks are live, else two; then
-    // the smallest K split that gives at least 24 waves per CU.  The one-column MFMA streams
-    // faster than the dot-product path (gemv_rows > 0), which stays available.
-    c.kernel = MOE_GEMM_DECODE;
-    c.gemv_rows = 0;
-    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(numel, W->n_experts));
-    c.ng = blocks >= 8 ? 4 : 2;
-    const int64_t items = blocks * ((nt + c.ng - 1) / c.ng);
-    c.ksplit = 1;
-    while (c.ksplit < 8 && items * c.ksplit < 24ll * num_cus) c.ksplit *= 2;
+  if (block_m <= 16 && W->K >= 2048 && numel >= 32) {
+    // 16-slot blocks with about 32 or more live slots of long-K weights: the MFMA kernel (its
+    // global->LDS stream, two tiles per wave) outruns the streaming kernel.  Measured, whole
+    // layers: NVFP4 slice with 32 / 64 live slots 153.5 -> 130.9 / 160.0 -> 145.8 us, MXFP4 with
+    // 128 live 255 -> 210 us (32-slot MFMA blocks: 149 / 160 / 218 us; four tiles per wave 146 /
+    // 157 / 227 us); with 16 live slots the streaming kernel still wins (94 against 107 us).
+    c.kernel = MOE_GEMM_MFMA;
+    c.ng = 2;
+    c.group_m = default_group_m(W->K, block_m);
+  } else if (block_m <= 16) {
+    c = stream_config(W, numel, num_cus);
   } else {
     // prefill: with 128-row blocks four 16-row tiles per wave (the dequantised weights then
     // feed 32 MFMAs per k-step), else two; one when two would not give every CU a workgroup

@@ -199,8 +199,7 @@ extern "C" int moe_w4a16_gemm_combine(const uint16_t* A, int64_t a_rows, int32_t
   if (cfg && cfg->kernel != MOE_GEMM_AUTO) {
     c = *cfg;
   } else {
-    int rc = moe_gemm_choose(W, numel, block_m, device_cu_count(), &c);
-    if (rc) return rc;
+    c = stream_config(W, numel, device_cu_count());  // the fused weighted sum runs in the streaming kernel
   }
   const CombineSpec cmb{topk_weights, slot_local_ids, out, ldo, counters, n_counters, top_k, M, routed_scaling};
   return gemm_impl(kActNone, 0.f, 0.f, A, a_rows, lda, y, ldy, W, sorted_token_ids, expert_ids,
@@ -245,11 +244,8 @@ extern "C" int moe_w4a16_gemm_act_routed(moe_act_kind kind, float alpha, float l
   if (cfg && cfg->kernel != MOE_GEMM_AUTO) {
     c = *cfg;
   } else {
-    rc = moe_gemm_choose(W13, numel, block_m, device_cu_count(), &c);
-    if (rc) return rc;
+    c = stream_config(W13, numel, device_cu_count());  // the fused align runs in the streaming kernel
     if (act_paired(act) && c.ng < 2) c.ng = 2;
-    c.kernel = MOE_GEMM_DECODE;
-    c.gemv_rows = 0;
   }
   return gemm_impl(act, alpha, limit, A, a_rows, lda, out, ldo, W13, sorted_token_ids, expert_ids,
                    num_tokens_post_padded, numel, top_k, block_m, &c, stream, topk_ids, expert_start,

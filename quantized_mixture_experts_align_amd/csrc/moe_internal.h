@@ -60,6 +60,10 @@ constexpr int kMaxActOrderK = 16384;
 // GEMMs 0.5-6% faster than 1, 4 and 8 are slower); 128-slot blocks keep 1.
 inline int default_group_m(int K, int block_m) { return K <= 1024 ? 8 : (block_m == 64 ? 2 : 1); }
 
+// Launch configuration of the streaming decode kernel for about `numel` live slots (the fused
+// align and the fused weighted sum run only there).
+moe_gemm_config stream_config(const moe_weights* W, int64_t numel, int num_cus);
+
 // ---------------------------------------------------------------------------- device math
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

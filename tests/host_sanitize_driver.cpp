@@ -108,8 +108,10 @@ int main() {
     for (int32_t block : {16, 64, 128}) {
       CHECK(moe_gemm_choose(&w, numel, block, 256, &cfg) == MOE_OK);
       CHECK(cfg.ng == 1 || cfg.ng == 2 || cfg.ng == 4);
-      CHECK(block > 16 || (cfg.kernel == MOE_GEMM_DECODE && cfg.ksplit >= 1 && cfg.ksplit <= 8));
-      CHECK(block <= 16 || (cfg.kernel == MOE_GEMM_MFMA && cfg.group_m >= 1 && cfg.group_m <= 8));
+      // 16-slot blocks: the streaming kernel, or the MFMA kernel from 32 live slots of long-K weights
+      const bool stream = block <= 16 && numel < 32;
+      CHECK(!stream || (cfg.kernel == MOE_GEMM_DECODE && cfg.ksplit >= 1 && cfg.ksplit <= 8));
+      CHECK(stream || (cfg.kernel == MOE_GEMM_MFMA && cfg.group_m >= 1 && cfg.group_m <= 8));
     }
   }
   CHECK(moe_gemm_choose(nullptr, 8, 16, 256, &cfg) == MOE_EINVAL);

@@ -192,16 +192,15 @@ def test_block_m_heuristic_is_monotone_and_picks_kernels():
     assert P.choose_block_m(8, 32) == 16            # decode slice
     assert P.choose_block_m(4608, 8) == 64          # int4 prefill, 576 rows per expert
     assert P.choose_block_m(32768, 32) == 128       # NVFP4 slice, 1024 rows per expert
-    # decode range: 16-slot streaming blocks up to about 32 expected live slots, then 32-slot MFMA
-    # blocks; a short K keeps the streaming kernel (with its fused align) up to 64 slots
+    # decode range: 16-slot blocks (streaming or MFMA kernel, chosen by moe_gemm_choose); a short K
+    # beyond the fused-align range with about 32 live slots or more takes 32-slot MFMA blocks
     assert P.choose_block_m(128, 32, 16, 4096) == 16     # NVFP4 slice M=16: 16 live
-    assert P.choose_block_m(256, 32, 32, 4096) == 32     # NVFP4 slice M=32: 32 live
-    assert P.choose_block_m(16, 128, 16, 2880) == 16     # MXFP4 M=4
-    assert P.choose_block_m(32, 128, 32, 2880) == 32     # MXFP4 M=8
-    assert P.choose_block_m(1024, 128, 1024, 2880) == 32  # MXFP4 M=256: 8 rows per expert
+    assert P.choose_block_m(256, 32, 32, 4096) == 16     # NVFP4 slice M=32: 32 live (MFMA kernel)
+    assert P.choose_block_m(32, 128, 32, 2880) == 16     # MXFP4 M=8
+    assert P.choose_block_m(1024, 128, 1024, 2880) == 16  # MXFP4 M=256: 8 rows per expert
     assert P.choose_block_m(64, 8, 64, 512) == 16        # int4 M=32: the fused align range
     assert P.choose_block_m(96, 8, 96, 512) == 32        # int4 M=48
-    assert P.choose_block_m(64, 8, 64, 0) == 32          # K unknown: taken as long
+    assert P.choose_block_m(96, 8, 96, 0) == 16          # K unknown: taken as long
     for numel in range(0, 300, 7):                       # expected_live is capped by numel
         assert P.choose_block_m(numel, 64, 1 << 40, 4096) == P.choose_block_m(numel, 64, 0, 4096)
 
@@ -213,8 +212,11 @@ def _W(q, E, N, K):
 @pytest.mark.parametrize("N,K,E", [(8192, 4096, 32), (4096, 4096, 32), (5760, 2880, 128), (512, 1024, 8)])
 def test_gemm_choose_contract(N, K, E):
     W = _W(1, E, N, K)
-    for numel in [1, 8, 64, 512]:
+    for numel in [1, 8, 31, 32, 64, 512]:
         c = P.gemm_choose(W, numel, 16, 256)
+        if K >= 2048 and numel >= 32:   # long-K weights, about 32 live slots or more: MFMA, 2 tiles
+            assert c.kernel == L.GEMM_MFMA and c.ng == 2 and c.group_m >= 1
+            continue
         assert c.kernel == L.GEMM_DECODE and c.ksplit in (1, 2, 4, 8) and 0 <= c.gemv_rows <= 4
         assert c.gemv_rows * K * 2 <= 65536
     last = 4
