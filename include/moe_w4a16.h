@@ -304,9 +304,12 @@ int moe_w4a16_gemm_act_routed(moe_act_kind kind, float alpha, float limit, const
  * fusion the Muse Spark experiment's kernel_fn leaves to fused_post_expert_norm_weighted_sum; its
  * "no norm" branch): one launch computes what moe_w4a16_gemm(A, M * top_k, lda, y, ldy, W, ...,
  * numel = M * top_k, top_k = 1, ...) followed by moe_combine(y, topk_weights, slot_local_ids,
- * NULL, 0, routed_scaling, M, top_k, N, out) computes, bit for bit (y is still written; the
- * summation order and roundings are the combine's).  Decode batches only: block_m <= 16 and the
- * streaming kernel (cfg NULL or AUTO, or kernel DECODE with gemv_rows 0).
+ * NULL, 0, routed_scaling, M, top_k, N, out) computes, bit for bit, when that GEMM runs the same
+ * streaming-kernel configuration (y is still written; the summation order and roundings are the
+ * combine's).  Decode batches only: block_m <= 16 and the streaming kernel: cfg kernel DECODE
+ * with gemv_rows 0, or cfg NULL / AUTO for the streaming kernel's default configuration (which
+ * moe_gemm_choose also returns below about 32 live slots or for K < 2048; above, it picks the
+ * MFMA kernel, whose fp32 summation order differs).
  *   A, lda, y, ldy, W, sorted/expert ids, num_tokens_post_padded, block_m: as moe_w4a16_gemm
  *     (A row = slot; W a plain projection, not MOE_PREP_GATE_UP)
  *   M, top_k        tokens and slots per token (numel = M * top_k, top_k <= 64)
