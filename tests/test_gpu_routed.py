@@ -102,3 +102,32 @@ def test_layer_with_fused_align(qtype, M):
     assert torch.equal(got_f.view(torch.int16), got_u.view(torch.int16))
     ref = oracle_layer(wl, lw, inp)
     assert layer_violations(W.bf16_to_float(got_f), ref) == 0
+
+
+def test_routed_auto_config_on_long_k_weights():
+    # 40 slots of K = 2048 weights: for these moe_gemm_choose picks the MFMA kernel, while the fused
+    # align runs only in the streaming kernel, which then takes its own default configuration
+    wl = W.small_workload("nvfp4_g16", H=2048)
+    lw = W.make_weights(wl)
+    w13, _, _ = W.device_weights(lw)
+    W13 = P.moe_w4a16_prepare("nvfp4_g16", w13["codes"], w13["scales"], w13.get("gs"), w13.get("bias"),
+                              L.PREP_GATE_UP, w13.get("zeros"))
+    M, k = 5, wl.top_k
+    assert M * k >= 32 and P.gemm_choose(W13, M * k, 16, 256).kernel == L.GEMM_MFMA
+    inp = W.make_inputs(wl, M, seed=900)
+    x, ids, _ = W.device_inputs(inp)
+    print(f"routed auto config nvfp4 K=2048 M={M} k={k}", flush=True)
+    got, (s2, e2, n2, loc2) = P.moe_w4a16_gemm_act_routed(wl.act, x, W13, ids, wl.expert_start, 16, wl.alpha,
+                                                           wl.limit)
+    s, e, n, loc = P.moe_align(ids, wl.expert_start, W13.desc.n_experts, 16)
+    ref = P.moe_w4a16_gemm_act(wl.act, x, W13, s, e, n, M * k, k, 16, wl.alpha, wl.limit)   # MFMA kernel
+    torch.cuda.synchronize()
+    assert int(n2.item()) == int(n.item())
+    assert torch.equal(s2, s) and torch.equal(e2, e) and torch.equal(loc2, loc)
+    live = torch.nonzero(loc.view(-1) >= 0).view(-1)
+    assert live.numel() > 0
+    g, r = W.bf16_to_float(got[live]), W.bf16_to_float(ref[live])
+    # the same products in another fp32 summation order: gate and up each rounded to bf16, then the
+    # activation, rounded again
+    rms = float(np.sqrt(np.mean(r * r)))
+    assert np.all(np.abs(g - r) <= 2.0 ** -6 * np.abs(r) + 2e-3 * rms), float(np.max(np.abs(g - r)))
