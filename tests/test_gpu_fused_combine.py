@@ -129,3 +129,32 @@ def test_layer_with_fused_combine(qtype, M):
     assert int(ws.counters.abs().sum().item()) == 0
     ref = oracle_layer(wl, lw, inp)
     assert layer_violations(W.bf16_to_float(got_f), ref) == 0
+
+
+def test_fused_combine_auto_config_on_long_k_weights():
+    # 40 slots of K = 2048 down-projection weights: moe_gemm_choose picks the MFMA kernel there; the
+    # fused weighted sum runs only in the streaming kernel, which then takes its own configuration
+    wl = W.small_workload("mxfp4_g32", I=2048, norm=False)
+    lw = W.make_weights(wl)
+    _, w2, _ = W.device_weights(lw)
+    W2 = P.moe_w4a16_prepare("mxfp4_g32", w2["codes"], w2["scales"], w2.get("gs"), w2.get("bias"), 0,
+                             w2.get("zeros"))
+    M, k = 10, wl.top_k
+    assert M * k >= 32 and P.gemm_choose(W2, M * k, 16, 256).kernel == L.GEMM_MFMA
+    inp = W.make_inputs(wl, M, seed=950)
+    rng = np.random.default_rng(950)
+    a = torch.from_numpy(W._to_bf16_bits(rng.standard_normal((M * k, W2.K)).astype(np.float32)).view(np.int16))
+    a = a.cuda().view(torch.bfloat16)
+    gw = torch.from_numpy(inp.topk_weights).cuda()
+    ids = torch.from_numpy(inp.topk_ids).cuda()
+    print(f"fused combine auto config mxfp4 K=2048 M={M} k={k}", flush=True)
+    s, e, n, loc = P.moe_align(ids, wl.expert_start, W2.desc.n_experts, 16)
+    y = torch.empty((M * k, W2.N), dtype=torch.bfloat16, device="cuda")
+    got = P.moe_w4a16_gemm_combine(a, W2, s, e, n, gw, loc, 16, P.combine_counters(M, W2, "cuda"), y)
+    ref = P.moe_combine(P.moe_w4a16_gemm(a, W2, s, e, n, M * k, 1, 16), gw, loc)         # MFMA kernel
+    torch.cuda.synchronize()
+    g, r = W.bf16_to_float(got), W.bf16_to_float(ref)
+    rms = float(np.sqrt(np.mean(r * r)))
+    assert rms > 0
+    # the same products in another fp32 summation order, y rounded to bf16, then the weighted sum
+    assert np.all(np.abs(g - r) <= 2.0 ** -6 * np.abs(r) + 2e-3 * rms), float(np.max(np.abs(g - r)))
