@@ -1,5 +1,7 @@
-// moe_w4a16_gemm: argument validation, launch-configuration choice and dispatch to the decode
-// (moe_gemm_decode.hip) or MFMA (moe_gemm_mfma.hip) kernel.
+// moe_w4a16_gemm: argument validation, launch-configuration choice and dispatch to the
+// streaming decode kernel (moe_gemm_stream.h), the dot-product decode kernel (moe_gemm_decode.h)
+// or the MFMA kernel (moe_gemm_mfma.h), instantiated per format in moe_gemm_{int4,int4zp,nvfp4,
+// mxfp4}.hip and moe_gemm_stream_*.hip.
 //
 // The computation is that of moe_wna16_marlin_gemm in the Muse Spark experiment and of the
 // Marlin template in the "sglang PR 31552" summary: for each block of sorted slots of one

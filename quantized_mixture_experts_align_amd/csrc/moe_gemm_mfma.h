@@ -48,7 +48,10 @@ __device__ __forceinline__ void wait_step(int later) {
   wait_vm<0>();
 }
 
-__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// All waves meet.  The wave's own LDS reads of the previous step are waited for first
+// (lgkmcnt(0)), so the global->LDS loads issued right after the barrier into that step's stage
+// can never overtake them, whatever the compiler schedules before the barrier.
+__device__ __forceinline__ void block_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Direct global -> LDS load of BYTES (4 or 16) per lane: lane l's data lands at lds + l*BYTES.
 // The address is a wave-uniform 64-bit base in scalar registers + the lane's 32-bit byte offset,
@@ -78,26 +81,8 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const void* p) {
   return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
 }
 
-// Workgroups go to the 8 XCDs round-robin by launch index, and each XCD has its own L2.  The
-// launch index is mapped to a logical (align block, column block) so that workgroups sharing
-// data run on one XCD: a group is GM consecutive align blocks x all nblk column blocks (column
-// block outer, so the GM workgroups reading the same weight tiles are adjacent; all of them read
-// the group's activation rows), and whole groups go round-robin over the XCDs.  The map is a
-// bijection on [0, gridDim.x): a trailing partial round keeps the identity.
-constexpr int kXcds = 8;
 __device__ __forceinline__ void grouped_block(int nblk, int gm_max, int& mb, int& nb) {
-  const int G = (int)gridDim.x, P = (int)blockIdx.x;
-  const int C = gm_max * nblk;
-  const int full = (G / (kXcds * C)) * (kXcds * C);
-  int L = P;
-  if (P < full) {
-    const int x = P % kXcds, j = P / kXcds;
-    L = ((j / C) * kXcds + x) * C + j % C;
-  }
-  const int g = L / C, r = L - g * C;
-  const int gm = min(gm_max, G / nblk - g * gm_max);
-  mb = g * gm_max + r % gm;
-  nb = r / gm;
+  xcd_grouped_block((int)gridDim.x, (int)blockIdx.x, nblk, gm_max, mb, nb);
 }
 
 template <int QT, bool BIAS, int MG, int NG, int ACT>

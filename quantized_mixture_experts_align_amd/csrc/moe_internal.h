@@ -60,6 +60,30 @@ constexpr int kMaxActOrderK = 16384;
 // GEMMs 0.5-6% faster than 1, 4 and 8 are slower); 128-slot blocks keep 1.
 inline int default_group_m(int K, int block_m) { return K <= 1024 ? 8 : (block_m == 64 ? 2 : 1); }
 
+// Workgroups go to the 8 XCDs round-robin by launch index, and each XCD has its own L2.  The
+// MFMA GEMM maps launch index P of a grid of G = nblk * (align blocks) workgroups to a logical
+// (align block mb, column block nb) so that workgroups sharing data run on one XCD: a group is
+// gm_max consecutive align blocks x all nblk column blocks (column block outer, so the
+// workgroups reading the same weight tiles are adjacent; all of them read the group's
+// activation rows), and whole groups go round-robin over the XCDs.  The map is a bijection on
+// [0, G) (a trailing partial round of groups keeps the identity order; the last group may hold
+// fewer than gm_max blocks).
+constexpr int kXcds = 8;
+__host__ __device__ inline void xcd_grouped_block(int G, int P, int nblk, int gm_max, int& mb, int& nb) {
+  const int C = gm_max * nblk;
+  const int full = (G / (kXcds * C)) * (kXcds * C);
+  int L = P;
+  if (P < full) {
+    const int x = P % kXcds, j = P / kXcds;
+    L = ((j / C) * kXcds + x) * C + j % C;
+  }
+  const int g = L / C, r = L - g * C;
+  const int rest = G / nblk - g * gm_max;
+  const int gm = gm_max < rest ? gm_max : rest;
+  mb = g * gm_max + r % gm;
+  nb = r / gm;
+}
+
 // Launch configuration of the streaming decode kernel for about `numel` live slots (the fused
 // align and the fused weighted sum run only there).
 moe_gemm_config stream_config(const moe_weights* W, int64_t numel, int num_cus);

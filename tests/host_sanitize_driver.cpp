@@ -7,7 +7,10 @@
 #include <cstdio>
 #include <cstring>
 
+#include <vector>
+
 #include "moe_w4a16.h"
+#include "moe_internal.h"
 
 namespace moe {
 int device_cu_count() { return 256; }  // (the GEMM sources that define it are not linked here)
@@ -147,6 +150,39 @@ int main() {
   CHECK(moe_permute_cols(s16, 256, 0, g32, 256, 4, g32, 8, d16, 256, nullptr) == MOE_EINVAL);
   CHECK(moe_permute_cols(s16, 256, 2, g32, 256, 4, g32, 8, d16 + 1, 256, nullptr) == MOE_EINVAL);
   CHECK(moe_permute_cols(nullptr, 256, 2, nullptr, 256, 4, nullptr, 0, nullptr, 256, nullptr) == MOE_OK);
+
+  // ---- the MFMA GEMM's XCD-aware launch order: a bijection from launch index to (align block,
+  // column block) on every grid it is launched with (nblk column blocks x any number of align
+  // blocks, any group size), including grids whose last round of groups is partial
+  for (int nblk : {1, 2, 3, 5, 8, 16, 32, 33})
+    for (int blocks = 1; blocks <= 97; blocks += (blocks < 20 ? 1 : 7))
+      for (int gm : {1, 2, 3, 4, 8, 16}) {
+        const int G = nblk * blocks;
+        std::vector<char> seen((size_t)G, 0);
+        bool in_range = true, once = true;
+        for (int P = 0; P < G; ++P) {
+          int mb = -1, nb = -1;
+          moe::xcd_grouped_block(G, P, nblk, gm, mb, nb);
+          if (mb < 0 || mb >= blocks || nb < 0 || nb >= nblk) { in_range = false; break; }
+          char& v = seen[(size_t)mb * nblk + nb];
+          if (v) once = false;
+          v = 1;
+        }
+        CHECK(in_range && once);
+      }
+  // whole groups of gm blocks go to one XCD (launch index mod 8) while full rounds last
+  {
+    const int nblk = 4, blocks = 64, gm = 2, G = nblk * blocks;
+    bool same_xcd = true;
+    for (int P = 0; P < G; ++P)
+      for (int Q = 0; Q < G; ++Q) {
+        int mb1, nb1, mb2, nb2;
+        moe::xcd_grouped_block(G, P, nblk, gm, mb1, nb1);
+        moe::xcd_grouped_block(G, Q, nblk, gm, mb2, nb2);
+        if (mb1 / gm == mb2 / gm && P % 8 != Q % 8) same_xcd = false;
+      }
+    CHECK(same_xcd);
+  }
 
   CHECK(moe_abi_version() == 5);
   if (failures) {

@@ -354,6 +354,82 @@ def test_layer_int4_relu2_non_gated_bias_closed_form():
     assert np.allclose(out, 1.5 * 0.625 * y, rtol=1e-14)
 
 
+def _rne_bf16(v):
+    """Nearest value with 8 significant bits (bf16), ties to the even one -- written from the
+    format's definition with frexp (Python's round() breaks ties to even), independently of
+    the oracle's rounding routine.  Normal magnitudes only."""
+    if v == 0.0:
+        return 0.0
+    m, e = math.frexp(v)            # v = m * 2^e, 0.5 <= |m| < 1
+    return math.ldexp(round(m * 256), e - 8)
+
+
+def test_layer_int4_bf16_intermediates_closed_form():
+    # The tensors stored between the experiment's kernels (cache1 = h, cache2 = a, cache13 = y)
+    # are bf16; with bf16_intermediates=True the oracle rounds there.  One token, one expert,
+    # H = I = 128 (one int4 group), constant codes, chosen so that each of the three roundings
+    # moves the output:
+    #   gate row code 12 -> 4, up row code 5 -> -3, scale 2^-7, x = 0.5:
+    #   h_gate = 4 * 2^-7 * 128 * 0.5 + 7 * 2^-9 = 2.013671875 = 128.875 ulps of 2^-6 -> 2.015625
+    #   h_up   = -1.5 - 6 * 2^-9 = -1.51171875 = -193.5 ulps of 2^-7, a tie -> even -194 -> -1.515625
+    #   a = silu(2.015625) * -1.515625 = -2.69575681 = -172.53 ulps of 2^-6 -> -2.703125
+    #   down row code 11 -> 3, scale 2^-6: y = 3 * 2^-6 * 128 * a + 2^-5 = 6a + 2^-5
+    #     = -16.1875 = -129.5 ulps of 2^-3, a tie -> even -130 -> -16.25
+    #   out = 0.75 * y = -12.1875
+    H = I = 128
+    w13 = _const_proj([12] * I + [5] * I, H, _bf16(2.0 ** -7), np.uint16, 128,
+                      bias=[_bf16(7 * 2.0 ** -9)] * I + [_bf16(-6 * 2.0 ** -9)] * I)
+    w2 = _const_proj([11] * H, I, _bf16(2.0 ** -6), np.uint16, 128, bias=[_bf16(2.0 ** -5)] * H)
+    x = np.full((1, H), _bf16(0.5), np.uint16)
+    out = O.moe_layer("int4_g128", x, np.array([[0]], np.int32), np.array([[0.75]], np.float32),
+                      w13, w2, expert_start=0, n_local=1, bf16_intermediates=True)
+    assert np.all(out == -12.1875)
+    # the same chain evaluated with math and the frexp rounding gives that value, and leaving out
+    # any one rounding (or rounding h before its bias) gives another one
+    hg, hu = 4 * 2.0 ** -7 * H * 0.5 + 7 * 2.0 ** -9, -3 * 2.0 ** -7 * H * 0.5 - 6 * 2.0 ** -9
+
+    def chain(rh=True, ra=True, ry=True, h_before_bias=False):
+        g = _rne_bf16(hg) if rh else hg
+        u = _rne_bf16(hu) if rh else hu
+        if h_before_bias:
+            g, u = _rne_bf16(hg - 7 * 2.0 ** -9) + 7 * 2.0 ** -9, _rne_bf16(hu + 6 * 2.0 ** -9) - 6 * 2.0 ** -9
+        a = _silu(g) * u
+        a = _rne_bf16(a) if ra else a
+        y = 6 * a + 2.0 ** -5
+        return 0.75 * (_rne_bf16(y) if ry else y)
+    assert chain() == -12.1875
+    for alt in (chain(rh=False), chain(ra=False), chain(ry=False), chain(h_before_bias=True)):
+        assert abs(alt - chain()) > 0.04
+
+
+def test_layer_relu2_bf16_intermediates_closed_form():
+    # non-gated relu2 with stored bf16 intermediates: a = bf16(relu(bf16(h))^2), y = bf16(W2 a + b2)
+    #   code 12 -> 4, scale 2^-7, x = 0.25: h = 4 * 2^-7 * 128 * 0.25 + 5 * 2^-9 = 1.009765625
+    #     = 129.25 ulps of 2^-7 -> 1.0078125
+    #   a = 1.0078125^2 = 1.01568603515625 = 130.008 ulps of 2^-7 -> 1.015625
+    #   down code 9 -> 1, scale 2^-5: y = 4a - 6 * 2^-7 = 4.015625 = 128.5 ulps of 2^-5, a tie
+    #     -> even 128 -> 4.0
+    #   out = 1.5 (routed scaling) * 0.625 * y = 3.75
+    H = I = 128
+    w13 = _const_proj([12] * I, H, _bf16(2.0 ** -7), np.uint16, 128, bias=[_bf16(5 * 2.0 ** -9)] * I)
+    w2 = _const_proj([9] * H, I, _bf16(2.0 ** -5), np.uint16, 128, bias=[_bf16(-6 * 2.0 ** -7)] * H)
+    x = np.full((1, H), _bf16(0.25), np.uint16)
+    out = O.moe_layer("int4_g128", x, np.array([[0]], np.int32), np.array([[0.625]], np.float32),
+                      w13, w2, expert_start=0, n_local=1, act="relu2", routed_scaling_factor=1.5,
+                      bf16_intermediates=True)
+    assert np.all(out == 3.75)
+    h = 4 * 2.0 ** -7 * H * 0.25 + 5 * 2.0 ** -9
+
+    def chain(rh=True, ra=True, ry=True):
+        v = _rne_bf16(h) if rh else h
+        a = _rne_bf16(v * v) if ra else v * v
+        y = 4 * a - 6 * 2.0 ** -7
+        return 1.5 * 0.625 * (_rne_bf16(y) if ry else y)
+    assert chain() == 3.75
+    for alt in (chain(rh=False), chain(ra=False), chain(ry=False)):
+        assert abs(alt - chain()) > 0.01
+
+
 def _small(qtype, M=None, **kw):
     wl = W.small_workload(qtype, **kw)
     lw = W.make_weights(wl)

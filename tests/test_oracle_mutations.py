@@ -45,6 +45,35 @@ def _align_reversed_segments(topk_ids, expert_start, n_local, block_m):
     return s, e, n, loc
 
 
+
+def _expert_forward_variant(skip="", h_before_bias=False):
+    """The oracle's expert step with one of its bf16 roundings (of h, a or y) left out, or with
+    h rounded before its bias is added."""
+    def f(xrows, W13, b13, W2, b2, act, alpha, limit, interleaved, bf16_intermediates=True):
+        rnd = O.round_to_bf16 if bf16_intermediates else (lambda v: v)
+        h = xrows @ W13.T
+        if h_before_bias:
+            h = rnd(h)
+        if b13 is not None:
+            h = h + b13[None, :]
+        if skip != "h" and not h_before_bias:
+            h = rnd(h)
+        if act == "relu2":
+            a = O.act_relu2(h)
+        else:
+            gate, up = O.split_gate_up(h, interleaved)
+            a = O.act_silu_mul(gate, up) if act == "silu_mul" else O.act_swiglu_alpha(gate, up, alpha, limit)
+        if skip != "a":
+            a = rnd(a)
+        y = a @ W2.T
+        if b2 is not None:
+            y = y + b2[None, :]
+        if skip != "y":
+            y = rnd(y)
+        return {"h": h, "a": a, "y": y}
+    return f
+
+
 ORIG = {"moe_align": O.moe_align}
 
 MUTATIONS = {
@@ -68,6 +97,10 @@ MUTATIONS = {
     "relu without the square": ("act_relu2", lambda: (lambda h: np.maximum(h, 0.0))),
     "square without the relu": ("act_relu2", lambda: (lambda h: np.square(h))),
     "segments reversed": ("moe_align", lambda: _align_reversed_segments),
+    "h not rounded to bf16": ("expert_forward", lambda: _expert_forward_variant(skip="h")),
+    "a not rounded to bf16": ("expert_forward", lambda: _expert_forward_variant(skip="a")),
+    "y not rounded to bf16": ("expert_forward", lambda: _expert_forward_variant(skip="y")),
+    "h rounded before its bias": ("expert_forward", lambda: _expert_forward_variant(h_before_bias=True)),
     "off-slice kept": ("route_local", lambda: (lambda ids, start, n: (np.asarray(ids) % n).astype(np.int32))),
     "global scale missing": ("dequant", lambda: (lambda q, c, s, gs=None, zeros=None, g_idx=None:
                                                  ORIG_DQ(q, c, s, None if gs is None else 1.0, zeros, g_idx))),
@@ -108,6 +141,8 @@ PINS = [
     (TL.test_layer_mxfp4_swiglu_interleaved_bias_closed_form, dict(limit=math.inf)),
     (TL.test_layer_mxfp4_swiglu_interleaved_bias_closed_form, dict(limit=1.0)),
     (TL.test_layer_int4_relu2_non_gated_bias_closed_form, {}),
+    (TL.test_layer_int4_bf16_intermediates_closed_form, {}),
+    (TL.test_layer_relu2_bf16_intermediates_closed_form, {}),
     (TA.test_golden_small, {}),
     (TA.test_matches_sort_brute_force, dict(M=64, k=8, E_glob=256, start=32, n_local=32, B=8)),
     (TA.test_route_local_brute_force, {}),
