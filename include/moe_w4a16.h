@@ -332,6 +332,31 @@ int moe_w4a16_gemm_combine(const uint16_t* A, int64_t a_rows, int32_t lda, uint1
                            int32_t* counters, int64_t n_counters, uint16_t* out, int32_t ldo,
                            const moe_gemm_config* cfg, hipStream_t stream);
 
+/*
+ * moe_w4a16_gemm_combine for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same computation and
+ * result, bit for bit, with the arrival counters taken from a scratch array inside the library
+ * instead of a caller workspace.  Nothing is allocated: no hipMalloc / hipFree and no allocating
+ * library routine, here or in any call it makes.
+ *   Arguments as moe_w4a16_gemm_combine without counters / n_counters.
+ *   Limit: M * ceil(N / (16 * ng)) <= MOE_NOALLOC_MAX_COUNTERS (262144 int32, 1 MiB per device;
+ *   e.g. M <= 1024 tokens for N = 4096 at ng = 2); beyond it MOE_ESIZE, nothing launched.
+ * The scratch array lives in the library's device memory, one copy per GPU the library runs on,
+ * held until the process ends; its device address is looked up on the first call on each
+ * device (with that device current).  Each call first clears the counters it uses with a small
+ * fill kernel on `stream` (no memset node, so the call may be captured in a graph), so no state
+ * carries over from an earlier call.  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (other streams, other threads) race and give wrong results --
+ * order them on one stream or use moe_w4a16_gemm_combine with separate counters.
+ */
+#define MOE_NOALLOC_MAX_COUNTERS 262144
+int moe_w4a16_gemm_combine_noalloc(const uint16_t* A, int64_t a_rows, int32_t lda, uint16_t* y, int32_t ldy,
+                                   const moe_weights* W, const int32_t* sorted_token_ids,
+                                   const int32_t* expert_ids, const int32_t* num_tokens_post_padded, int64_t M,
+                                   int32_t top_k, int32_t block_m, const float* topk_weights,
+                                   const int32_t* slot_local_ids, float routed_scaling, uint16_t* out,
+                                   int32_t ldo, const moe_gemm_config* cfg, hipStream_t stream);
+
 /* ----------------------------------------------------------------------------- act */
 
 /*

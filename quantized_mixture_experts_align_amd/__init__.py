@@ -9,7 +9,8 @@ from .ops import (align_capacity, choose_block_m, gemm_choose, gemm_config, moe_
                   moe_combine, moe_norm_weight, moe_w4a16_gemm, moe_w4a16_gemm_act,
                   moe_w4a16_gemm_act_routed, moe_w4a16_prepare, prepared_size,
                   PreparedWeights, moe_fp8_requant, requant_choose, requant_config, moe_permute_cols,
-                  moe_w4a16_gemm_combine, combine_counters)
+                  moe_w4a16_gemm_combine, combine_counters,
+                  moe_w4a16_gemm_combine_noalloc)
 from .layer import MoELayer, Workspace
 
 __all__ = [
@@ -18,4 +19,5 @@ __all__ = [
     "moe_w4a16_gemm_act_routed", "moe_w4a16_prepare", "prepared_size",
     "PreparedWeights", "MoELayer", "Workspace", "moe_fp8_requant", "requant_choose",
     "requant_config", "moe_permute_cols", "moe_w4a16_gemm_combine", "combine_counters",
+    "moe_w4a16_gemm_combine_noalloc",
 ]

@@ -16,6 +16,7 @@ ACT = {"silu_mul": 0, "swiglu_alpha": 1, "relu2": 2}
 GATED = {"silu_mul": True, "swiglu_alpha": True, "relu2": False}
 PREP_GATE_UP, PREP_INTERLEAVED, PREP_PAD, PREP_ACT_ORDER = 0x1, 0x2, 0x4, 0x8
 GEMM_AUTO, GEMM_DECODE, GEMM_MFMA = 0, 1, 2
+NOALLOC_MAX_COUNTERS = 262144   # MOE_NOALLOC_MAX_COUNTERS
 
 
 class MoeWeights(C.Structure):
@@ -66,6 +67,9 @@ SIGNATURES = {
     "moe_w4a16_gemm_combine": (C.c_int, [_P, _I64, _I32, _P, _I32, C.POINTER(MoeWeights), _P, _P, _P,
                                          _I64, _I32, _I32, _P, _P, _F, _P, _I64, _P, _I32,
                                          C.POINTER(MoeGemmConfig), _P]),
+    "moe_w4a16_gemm_combine_noalloc": (C.c_int, [_P, _I64, _I32, _P, _I32, C.POINTER(MoeWeights), _P, _P, _P,
+                                                 _I64, _I32, _I32, _P, _P, _F, _P, _I32,
+                                                 C.POINTER(MoeGemmConfig), _P]),
     "moe_fp8_requant_choose": (C.c_int, [_I32, _I32, _I32, _I32, _I32, C.POINTER(MoeRequantConfig)]),
     "moe_fp8_requant": (C.c_int, [_P, _P, _I64, _I64, _I64, _P, _P, _I32, _I32, _I32, _I32, _P,
                                   C.POINTER(MoeRequantConfig), _P]),

@@ -7,6 +7,8 @@
 // Marlin template in the "sglang PR 31552" summary: for each block of sorted slots of one
 // expert, C[slot] = dequant(W[e]) . A[slot / top_k] with fp32 accumulation, the per-expert bias
 // added at the end (kHasBias there, a template parameter here) and bf16 results.
+#include <mutex>
+
 #include "moe_gemm_common.h"
 
 namespace moe {
@@ -39,7 +41,48 @@ struct CombineSpec {
   int32_t k;
   int64_t M;
   float rsf;
+  bool clear;   // zero the first M * strips counters right before the GEMM launch
 };
+
+// ---------------------------------------------------------------------------- library scratch
+// Arrival counters of moe_w4a16_gemm_combine_noalloc, for callers that cannot allocate: one
+// array per device, in the library's own device memory, held until the process ends.  Host code
+// never uses the array's name as an address (on the host it is only a stand-in): its device
+// address is looked up once per device with hipGetSymbolAddress and kept in g_scratch_ptr.
+static __device__ __align__(256) int32_t scratch[kNoAllocCounters];
+static std::mutex g_scratch_mu;
+static int32_t* g_scratch_ptr[64];
+
+// The current device's copy of `scratch` (looked up on the first call on each device).
+static int scratch_counters(int32_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_EHIP, "moe_w4a16_gemm_combine_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  MOE_REQUIRE(dev >= 0 && dev < 64, MOE_EUNSUPPORTED, "moe_w4a16_gemm_combine_noalloc: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_EHIP, "moe_w4a16_gemm_combine_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+// A plain fill kernel (no memset node, so the clear may be captured in a HIP graph).
+__global__ void zero_counters_kernel(int32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+static int zero_counters(int32_t* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return ok();
+  const int64_t blocks = std::min<int64_t>(256, (n + 255) / 256);
+  hipLaunchKernelGGL(zero_counters_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
+  return check_launch("moe_w4a16_gemm_combine_noalloc (counter clear)");
+}
 
 static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64_t a_rows, int32_t lda,
                      uint16_t* C, int32_t ldc, const moe_weights* W, const int32_t* sorted_token_ids,
@@ -130,6 +173,11 @@ static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64
     MOE_REQUIRE((int64_t)c.gemv_rows * W->K * 2 <= 32768, MOE_EUNSUPPORTED,
                 "moe_w4a16_gemm: gemv_rows=%d x K=%d exceeds the 32 KiB activation stage", c.gemv_rows, W->K);
     if (c.gemv_rows == 0) {  // one-column MFMA on every block: the streaming kernel
+      if (cmb && cmb->clear) {  // (every argument has been checked: the launches follow)
+        const int64_t strips = (W->N / kTileN + c.ng - 1) / c.ng;
+        int rcz = zero_counters(cmb->cnt, cmb->M * strips, stream);
+        if (rcz) return rcz;
+      }
       switch (W->qtype) {
         case MOE_Q_INT4_G128: return launch_gemm_stream<MOE_Q_INT4_G128>(bias, act, a, c, (int)cap_blocks, cus, stream);
         case MOE_Q_NVFP4_G16: return launch_gemm_stream<MOE_Q_NVFP4_G16>(bias, act, a, c, (int)cap_blocks, cus, stream);
@@ -175,6 +223,54 @@ extern "C" int moe_w4a16_gemm(const uint16_t* A, int64_t a_rows, int32_t lda, ui
                    num_tokens_post_padded, numel, top_k, block_m, cfg, stream);
 }
 
+static int gemm_combine_impl(const uint16_t* A, int64_t a_rows, int32_t lda, uint16_t* y, int32_t ldy,
+                             const moe_weights* W, const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                             const int32_t* num_tokens_post_padded, int64_t M, int32_t top_k, int32_t block_m,
+                             const float* topk_weights, const int32_t* slot_local_ids, float routed_scaling,
+                             int32_t* counters, int64_t n_counters, bool noalloc, uint16_t* out, int32_t ldo,
+                             const moe_gemm_config* cfg, hipStream_t stream) {
+  const char* fn = noalloc ? "moe_w4a16_gemm_combine_noalloc" : "moe_w4a16_gemm_combine";
+  MOE_REQUIRE(M >= 0 && M < (1 << 30) && top_k >= 1 && top_k <= 64, MOE_EINVAL,
+              "%s: M=%lld top_k=%d", fn, (long long)M, top_k);
+  MOE_REQUIRE(W, MOE_EINVAL, "%s: null weights", fn);
+  MOE_REQUIRE(!(W->flags & MOE_PREP_GATE_UP), MOE_EINVAL,
+              "%s: the weighted sum follows the down projection, not a gate/up pair", fn);
+  MOE_REQUIRE(block_m >= 1 && block_m <= 16, MOE_EUNSUPPORTED,
+              "%s: block_m=%d outside 1..16 (the streaming decode kernel)", fn, block_m);
+  moe_gemm_config c{};
+  if (cfg && cfg->kernel != MOE_GEMM_AUTO) {
+    c = *cfg;
+  } else {
+    c = stream_config(W, M * top_k, device_cu_count());  // the fused weighted sum runs in the streaming kernel
+  }
+  if (noalloc) {
+    MOE_REQUIRE(c.ng == 1 || c.ng == 2 || c.ng == 4, MOE_EINVAL, "%s: ng=%d", fn, c.ng);
+    const int64_t need = M * ((W->N / kTileN + c.ng - 1) / c.ng);
+    MOE_REQUIRE(need <= kNoAllocCounters, MOE_ESIZE,
+                "%s: M=%lld tokens x %lld column strips need %lld arrival counters; the library's "
+                "scratch holds %lld (use moe_w4a16_gemm_combine with caller counters)",
+                fn, (long long)M, (long long)(need / (M > 0 ? M : 1)), (long long)need,
+                (long long)kNoAllocCounters);
+  }
+  if (M == 0) return ok();
+  MOE_REQUIRE(topk_weights && slot_local_ids && out && y, MOE_EINVAL, "%s: null pointer", fn);
+  MOE_REQUIRE(noalloc || counters, MOE_EINVAL, "%s: null counters", fn);
+  MOE_REQUIRE(ldo >= W->N && ((uintptr_t)out & 1) == 0, MOE_EINVAL,
+              "%s: ldo=%d below N=%d or misaligned out", fn, ldo, W->N);
+  MOE_REQUIRE(((uintptr_t)counters & 3) == 0 && n_counters >= 0, MOE_EINVAL,
+              "%s: misaligned counters or negative count", fn);
+  if (noalloc) {
+    int rc = scratch_counters(&counters);
+    if (rc) return rc;
+    n_counters = kNoAllocCounters;
+  }
+  const int64_t numel = M * top_k;
+  const CombineSpec cmb{topk_weights, slot_local_ids, out, ldo, counters, n_counters, top_k, M, routed_scaling,
+                        noalloc};
+  return gemm_impl(kActNone, 0.f, 0.f, A, a_rows, lda, y, ldy, W, sorted_token_ids, expert_ids,
+                   num_tokens_post_padded, numel, 1, block_m, &c, stream, nullptr, 0, nullptr, &cmb);
+}
+
 extern "C" int moe_w4a16_gemm_combine(const uint16_t* A, int64_t a_rows, int32_t lda, uint16_t* y, int32_t ldy,
                                       const moe_weights* W, const int32_t* sorted_token_ids,
                                       const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
@@ -182,30 +278,21 @@ extern "C" int moe_w4a16_gemm_combine(const uint16_t* A, int64_t a_rows, int32_t
                                       const int32_t* slot_local_ids, float routed_scaling, int32_t* counters,
                                       int64_t n_counters, uint16_t* out, int32_t ldo,
                                       const moe_gemm_config* cfg, hipStream_t stream) {
-  MOE_REQUIRE(M >= 0 && M < (1 << 30) && top_k >= 1 && top_k <= 64, MOE_EINVAL,
-              "moe_w4a16_gemm_combine: M=%lld top_k=%d", (long long)M, top_k);
-  MOE_REQUIRE(W, MOE_EINVAL, "moe_w4a16_gemm_combine: null weights");
-  MOE_REQUIRE(!(W->flags & MOE_PREP_GATE_UP), MOE_EINVAL,
-              "moe_w4a16_gemm_combine: the weighted sum follows the down projection, not a gate/up pair");
-  MOE_REQUIRE(block_m >= 1 && block_m <= 16, MOE_EUNSUPPORTED,
-              "moe_w4a16_gemm_combine: block_m=%d outside 1..16 (the streaming decode kernel)", block_m);
-  if (M == 0) return ok();
-  MOE_REQUIRE(topk_weights && slot_local_ids && out && counters && y, MOE_EINVAL,
-              "moe_w4a16_gemm_combine: null pointer");
-  MOE_REQUIRE(ldo >= W->N && ((uintptr_t)out & 1) == 0, MOE_EINVAL,
-              "moe_w4a16_gemm_combine: ldo=%d below N=%d or misaligned out", ldo, W->N);
-  MOE_REQUIRE(((uintptr_t)counters & 3) == 0 && n_counters >= 0, MOE_EINVAL,
-              "moe_w4a16_gemm_combine: misaligned counters or negative count");
-  const int64_t numel = M * top_k;
-  moe_gemm_config c{};
-  if (cfg && cfg->kernel != MOE_GEMM_AUTO) {
-    c = *cfg;
-  } else {
-    c = stream_config(W, numel, device_cu_count());  // the fused weighted sum runs in the streaming kernel
-  }
-  const CombineSpec cmb{topk_weights, slot_local_ids, out, ldo, counters, n_counters, top_k, M, routed_scaling};
-  return gemm_impl(kActNone, 0.f, 0.f, A, a_rows, lda, y, ldy, W, sorted_token_ids, expert_ids,
-                   num_tokens_post_padded, numel, 1, block_m, &c, stream, nullptr, 0, nullptr, &cmb);
+  return gemm_combine_impl(A, a_rows, lda, y, ldy, W, sorted_token_ids, expert_ids, num_tokens_post_padded, M,
+                           top_k, block_m, topk_weights, slot_local_ids, routed_scaling, counters, n_counters,
+                           false, out, ldo, cfg, stream);
+}
+
+extern "C" int moe_w4a16_gemm_combine_noalloc(const uint16_t* A, int64_t a_rows, int32_t lda, uint16_t* y,
+                                              int32_t ldy, const moe_weights* W, const int32_t* sorted_token_ids,
+                                              const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                                              int64_t M, int32_t top_k, int32_t block_m,
+                                              const float* topk_weights, const int32_t* slot_local_ids,
+                                              float routed_scaling, uint16_t* out, int32_t ldo,
+                                              const moe_gemm_config* cfg, hipStream_t stream) {
+  return gemm_combine_impl(A, a_rows, lda, y, ldy, W, sorted_token_ids, expert_ids, num_tokens_post_padded, M,
+                           top_k, block_m, topk_weights, slot_local_ids, routed_scaling, nullptr, 0, true, out,
+                           ldo, cfg, stream);
 }
 
 extern "C" int moe_w4a16_gemm_act_routed(moe_act_kind kind, float alpha, float limit, const uint16_t* A,

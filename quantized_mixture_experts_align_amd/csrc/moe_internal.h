@@ -49,6 +49,9 @@ inline __host__ __device__ int scale_step_bytes(int q) {
 
 inline __host__ __device__ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// moe_w4a16_gemm_combine_noalloc: arrival counters in the library's scratch array per device
+constexpr int64_t kNoAllocCounters = MOE_NOALLOC_MAX_COUNTERS;
+
 // act-order (g_idx) weights: most input columns per expert (the grouping is staged in LDS)
 constexpr int kMaxActOrderK = 16384;
 

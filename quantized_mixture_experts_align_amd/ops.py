@@ -285,6 +285,29 @@ def moe_w4a16_gemm_combine(A: torch.Tensor, W: PreparedWeights, sorted_token_ids
     return out
 
 
+def moe_w4a16_gemm_combine_noalloc(A: torch.Tensor, W: PreparedWeights, sorted_token_ids: torch.Tensor,
+                                   expert_ids: torch.Tensor, num_tokens_post_padded: torch.Tensor,
+                                   topk_weights: torch.Tensor, slot_local_ids: torch.Tensor, block_m: int,
+                                   y: torch.Tensor, out: torch.Tensor, routed_scaling_factor: float = 1.0,
+                                   cfg: Optional[L.MoeGemmConfig] = None) -> torch.Tensor:
+    """moe_w4a16_gemm_combine with its arrival counters in the library's scratch memory (no
+    caller workspace, nothing allocated: `y` and `out` must be given)."""
+    _need(A, torch.bfloat16, "A")
+    _need(y, torch.bfloat16, "y")
+    _need(out, torch.bfloat16, "out")
+    _need(topk_weights, torch.float32, "topk_weights")
+    _need(slot_local_ids, torch.int32, "slot_local_ids")
+    M, k = topk_weights.shape
+    L.check(L.lib().moe_w4a16_gemm_combine_noalloc(_ptr(A), A.shape[0], A.stride(0), _ptr(y), y.stride(0),
+                                                   C.byref(W.desc), _ptr(sorted_token_ids), _ptr(expert_ids),
+                                                   _ptr(num_tokens_post_padded), M, k, block_m,
+                                                   _ptr(topk_weights), _ptr(slot_local_ids),
+                                                   routed_scaling_factor, _ptr(out), out.stride(0),
+                                                   None if cfg is None else C.byref(cfg), _stream()),
+            "moe_w4a16_gemm_combine_noalloc")
+    return out
+
+
 def moe_combine(y: torch.Tensor, topk_weights: torch.Tensor, slot_local_ids: torch.Tensor,
                 norm_w: Optional[torch.Tensor] = None, eps: float = 1e-8,
                 out: Optional[torch.Tensor] = None, routed_scaling_factor: float = 1.0) -> torch.Tensor:
