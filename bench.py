@@ -137,7 +137,7 @@ _LAYERS: dict = {}   # prepared weights reused across cells of one weight set
 
 
 def run_cell(name: str, M: int, steps: int, warmup: int, want_cpu: bool, seed=None,
-             fused_combine: bool = False) -> dict:
+             fused_combine: bool = False, block_m=None) -> dict:
     import torch
     import workloads as W
     from quantized_mixture_experts_align_amd import MoELayer
@@ -159,7 +159,7 @@ def run_cell(name: str, M: int, steps: int, warmup: int, want_cpu: bool, seed=No
     lw, layer = _LAYERS["lw"], _LAYERS["layer"]
     inp = W.make_inputs(wl, M, seed)
     x, ids, gw = W.device_inputs(inp, dev)
-    ws = layer.workspace(M, device=dev)
+    ws = layer.workspace(M, block_m, device=dev)
     numel = M * wl.top_k
     local = (inp.topk_ids >= wl.expert_start) & (inp.topk_ids < wl.expert_start + wl.n_local)
     live = int(local.sum())
@@ -261,7 +261,7 @@ def run_cell(name: str, M: int, steps: int, warmup: int, want_cpu: bool, seed=No
         ach = bytes_13 / d13 / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4)}
-    roof["kernel"] = gemm13_kernel_name(layer, M, calls["gemm13"][0] is orig_routed)
+    roof["kernel"] = gemm13_kernel_name(layer, M, ws.block_m, calls["gemm13"][0] is orig_routed)
     roof["traffic"] = load_traffic("moe_gemm13", wl.name + f"_m{M}")
     roof["avg_launch_us"] = round(d13 * 1e6, 2)
 
@@ -391,9 +391,9 @@ def layer_fracs(nbytes: float, flops: float, t: float) -> dict:
             "roof_frac": round(max(t_hbm, t_mfma) / t, 4)}
 
 
-def gemm13_kernel_name(layer, M, routed: bool) -> str:
+def gemm13_kernel_name(layer, M, block_m, routed: bool) -> str:
     from quantized_mixture_experts_align_amd import _lib as L
-    c = layer.configs(M, layer.block_m(M))[0]
+    c = layer.configs(M, block_m)[0]
     if c.kernel == L.GEMM_MFMA:
         name = "gemm_mfma_kernel"
     else:
@@ -410,6 +410,8 @@ def main() -> int:
                     "with Zipf routing, M=4096); one of the names in workloads.WORKLOADS")
     ap.add_argument("--M", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--block-m", type=int, default=None,
+                    help="align block size (default: the library's choice); a launch option only")
     ap.add_argument("--sweep", action="store_true", help="one line per configuration cell")
     ap.add_argument("--fused-combine", action="store_true",
                     help="decode layers without norm: the weighted sum fused into the down GEMM")
@@ -451,7 +453,8 @@ def main() -> int:
         print(f"unknown workload {name!r}; one of {list(W.WORKLOADS)}", file=sys.stderr)
         return 2
     M = a.M or (W.HEADLINE_M if name == W.HEADLINE else W.WORKLOADS[name].Ms[0])
-    r = run_cell(name, M, a.steps, a.warmup, not a.no_cpu_baseline, fused_combine=a.fused_combine)
+    r = run_cell(name, M, a.steps, a.warmup, not a.no_cpu_baseline, fused_combine=a.fused_combine,
+                 block_m=a.block_m)
     print(json.dumps(r), flush=True)
     return 0
 

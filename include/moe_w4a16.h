@@ -241,6 +241,30 @@ int moe_gemm_choose(const moe_weights* W, int64_t numel, int32_t block_m, int32_
                     moe_gemm_config* cfg);
 
 /*
+ * Residency of the MFMA GEMM kernel that moe_w4a16_gemm launches for projection W with this
+ * block_m (16, 32, 64 or 128): resident[i] = workgroups (of four waves) that fit one compute unit
+ * at once with 1, 2 and 4 weight tiles per wave, as the HIP occupancy API computes them on the
+ * current device from each kernel variant's register and LDS use.  gated != 0: the variant with a
+ * fused gated activation (its resident[0] is 0: it has no one-tile form).  Asked once per device
+ * and variant, then cached.  Errors: MOE_EINVAL for bad arguments, MOE_EHIP when no device
+ * answers.  This is what moe_gemm_choose weighs the tile counts of the prefill GEMMs with (the
+ * occupancy-driven part of the launch choice, [PR31552]'s determine_exec_config role).
+ */
+int moe_gemm_occupancy(const moe_weights* W, int32_t block_m, int32_t gated, int32_t resident[3]);
+
+/*
+ * moe_gemm_choose with the MFMA residency given instead of asked of the device (resident[i] at
+ * 1, 2, 4 tiles per wave, as moe_gemm_occupancy returns it).  moe_gemm_choose calls this with the
+ * current device's residency (two per CU, the kernels' launch bound, when no device answers).
+ * For the prefill block sizes (32 to 128 slots): two tiles per wave; four when the weights stream
+ * through long K loops (64-slot blocks with K >= 2048) or the blocks hold 128 slots, the four-tile
+ * grid gives every CU a workgroup, and it needs no more rounds of resident workgroups than the
+ * two-tile grid; one tile when the two-tile grid has fewer workgroups than CUs.  Pure host function.
+ */
+int moe_gemm_choose_occ(const moe_weights* W, int64_t numel, int32_t block_m, int32_t num_cus,
+                        const int32_t resident[3], moe_gemm_config* cfg);
+
+/*
  * Grouped W4A16 GEMM over the align blocks (moe_wna16_marlin_gemm with mul_topk_weights=False,
  * fp32 accumulation).  For every sorted entry s < numel of block b (expert e = expert_ids[b]):
  *     C[s, n] = bf16( gs[e] * sum_k dequant(W[e])[n, k] * A[s / top_k, k]  (+ bias[e, n]) )

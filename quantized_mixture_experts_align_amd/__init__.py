@@ -5,7 +5,7 @@ this package only marshals torch tensors into it.  Importing the package does no
 library; the first call does, and fails loudly if it has not been built.
 """
 from . import _lib
-from .ops import (align_capacity, choose_block_m, gemm_choose, gemm_config, moe_act, moe_align,
+from .ops import (align_capacity, choose_block_m, gemm_choose, gemm_occupancy, gemm_config, moe_act, moe_align,
                   moe_combine, moe_norm_weight, moe_w4a16_gemm, moe_w4a16_gemm_act,
                   moe_w4a16_gemm_act_routed, moe_w4a16_prepare, prepared_size,
                   PreparedWeights, moe_fp8_requant, requant_choose, requant_config, moe_permute_cols,
@@ -14,7 +14,7 @@ from .ops import (align_capacity, choose_block_m, gemm_choose, gemm_config, moe_
 from .layer import MoELayer, Workspace
 
 __all__ = [
-    "align_capacity", "choose_block_m", "gemm_choose", "gemm_config", "moe_act", "moe_align",
+    "align_capacity", "choose_block_m", "gemm_choose", "gemm_occupancy", "gemm_config", "moe_act", "moe_align",
     "moe_combine", "moe_norm_weight", "moe_w4a16_gemm", "moe_w4a16_gemm_act",
     "moe_w4a16_gemm_act_routed", "moe_w4a16_prepare", "prepared_size",
     "PreparedWeights", "MoELayer", "Workspace", "moe_fp8_requant", "requant_choose",

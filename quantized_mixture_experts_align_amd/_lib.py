@@ -55,6 +55,9 @@ SIGNATURES = {
     "moe_norm_weight": (C.c_int, [_P, _I32, _P, _P]),
     "moe_choose_block_m": (C.c_int, [_I64, _I32, _I64, _I32, C.POINTER(_I32)]),
     "moe_gemm_choose": (C.c_int, [C.POINTER(MoeWeights), _I64, _I32, _I32, C.POINTER(MoeGemmConfig)]),
+    "moe_gemm_choose_occ": (C.c_int, [C.POINTER(MoeWeights), _I64, _I32, _I32, C.POINTER(_I32 * 3),
+                                      C.POINTER(MoeGemmConfig)]),
+    "moe_gemm_occupancy": (C.c_int, [C.POINTER(MoeWeights), _I32, _I32, C.POINTER(_I32 * 3)]),
     "moe_w4a16_gemm": (C.c_int, [_P, _I64, _I32, _P, _I32, C.POINTER(MoeWeights), _P, _P, _P,
                                  _I64, _I32, _I32, C.POINTER(MoeGemmConfig), _P]),
     "moe_w4a16_gemm_act": (C.c_int, [C.c_int, _F, _F, _P, _I64, _I32, _P, _I32, C.POINTER(MoeWeights), _P,

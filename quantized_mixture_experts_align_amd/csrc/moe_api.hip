@@ -115,7 +115,12 @@ extern "C" int moe_choose_block_m(int64_t numel, int32_t n_local, int64_t expect
   int b = 16;
   if (rows > 16) b = 32;
   if (rows > 48) b = 64;
-  if (rows >= 256 && numel >= 8192) b = 128;
+  // 128-slot blocks from 8192 slots once an expert averages 256 rows, or once the slots expected
+  // live average 48 per expert: then most experts fit one 128-slot block, whose unused 16-slot
+  // groups the MFMA kernel skips, and each expert's weights are dequantised once instead of in
+  // two 64-slot blocks (measured: MXFP4 M=2048, 64 live rows per expert, 591 us against 623 us;
+  // the NVFP4 slice at M=256, 8 expected live rows per expert, keeps 64: 328 against 387 us)
+  if (numel >= 8192 && (rows >= 256 || (double)live / n_local >= 48)) b = 128;
   if (b == 16 && live >= 32 && K > 0 && K <= 1024 && numel > 64) b = 32;
   *block_m = b;
   return ok();
@@ -140,9 +145,9 @@ moe_gemm_config stream_config(const moe_weights* W, int64_t numel, int num_cus) 
 }
 }  // namespace moe
 
-extern "C" int moe_gemm_choose(const moe_weights* W, int64_t numel, int32_t block_m, int32_t num_cus,
-                               moe_gemm_config* cfg) {
-  MOE_REQUIRE(W && cfg, MOE_EINVAL, "moe_gemm_choose: null pointer");
+extern "C" int moe_gemm_choose_occ(const moe_weights* W, int64_t numel, int32_t block_m, int32_t num_cus,
+                                   const int32_t resident[3], moe_gemm_config* cfg) {
+  MOE_REQUIRE(W && cfg && resident, MOE_EINVAL, "moe_gemm_choose: null pointer");
   MOE_REQUIRE(block_m >= 1 && numel >= 0, MOE_EINVAL, "moe_gemm_choose: bad block_m/numel");
   if (num_cus <= 0) num_cus = 256;
   moe_gemm_config c{};
@@ -159,23 +164,46 @@ extern "C" int moe_gemm_choose(const moe_weights* W, int64_t numel, int32_t bloc
   } else if (block_m <= 16) {
     c = stream_config(W, numel, num_cus);
   } else {
-    // prefill: with 128-row blocks four 16-row tiles per wave (the dequantised weights then
-    // feed 32 MFMAs per k-step), else two; one when two would not give every CU a workgroup
-    // (measured on the int4 down GEMM at M = 2304, 320 workgroups with two tiles: 16.3 us
-    // against 18.2 us with one tile and twice the workgroups).
-    // With 64-row blocks and a long K (the weights stream from HBM through long K loops) four
-    // tiles as well.  Measured on the int4, NVFP4 and MXFP4 prefill shapes: MXFP4 M=2048 gate/up
-    // 565 -> 428 us and down 291 -> 242 us, NVFP4 M=256 down 163 -> 141 us and gate/up
-    // 271 -> 232 us, NVFP4 M=1024 (64-row blocks) gate/up 583 -> 507 us; the int4 GEMMs
-    // (K <= 1024) are faster with two.
+    // prefill.  Two 16-row tiles per wave by default.  Four (the dequantised weights then feed
+    // twice the MFMAs per load of the block's activations) when the weights stream from HBM
+    // through long K loops (64-slot blocks and K >= 2048) or the blocks hold 128 slots, and the
+    // four-tile grid needs no more rounds of resident workgroups than the two-tile one -- the
+    // residency per CU of each variant is the kernel's own (registers and LDS, from the
+    // occupancy API: 2 for the 128-slot four-tile kernels, 4 for the 64-slot ones).  One tile
+    // when two would not give every CU a workgroup.  Measured on the int4, NVFP4 and MXFP4
+    // prefill shapes: MXFP4 M=2048 gate/up 565 -> 428 us and down 291 -> 242 us, NVFP4 M=256
+    // down 163 -> 141 us and gate/up 271 -> 232 us, NVFP4 M=1024 (64-row blocks) gate/up
+    // 583 -> 507 us with four tiles; the int4 GEMMs (K <= 1024, 64-slot blocks) are faster with
+    // two, and the int4 down GEMM at M = 2304 (320 workgroups with two tiles) 16.3 us against
+    // 18.2 us with one tile and twice the workgroups.
     c.kernel = MOE_GEMM_MFMA;
     const int64_t mblocks = numel / block_m + std::min<int64_t>(numel, W->n_experts);
     const bool streamed = block_m >= 64 && W->K >= 2048;
+    auto grid = [&](int ng) { return (int64_t)((nt + 4 * ng - 1) / (4 * ng)) * mblocks; };
+    auto rounds = [&](int ng, int res) {
+      const int64_t slots = (int64_t)std::max(1, res) * num_cus;
+      return (grid(ng) + slots - 1) / slots;
+    };
     c.ng = 2;
-    if ((block_m >= 128 || streamed) && ((int64_t)(nt + 15) / 16) * mblocks >= 2 * num_cus) c.ng = 4;
-    if (((int64_t)(nt + 7) / 8) * mblocks < num_cus) c.ng = 1;
+    if ((block_m >= 128 || streamed) && grid(4) >= num_cus && rounds(4, resident[2]) <= rounds(2, resident[1]))
+      c.ng = 4;
+    if (grid(2) < num_cus) c.ng = 1;
     c.group_m = default_group_m(W->K, block_m);
   }
   *cfg = c;
   return ok();
+}
+
+extern "C" int moe_gemm_choose(const moe_weights* W, int64_t numel, int32_t block_m, int32_t num_cus,
+                               moe_gemm_config* cfg) {
+  MOE_REQUIRE(W && cfg, MOE_EINVAL, "moe_gemm_choose: null pointer");
+  // the MFMA kernels' residency on this device; without one, the two workgroups per CU their
+  // launch bound guarantees
+  int32_t resident[3] = {2, 2, 2};
+  if (block_m == 32 || block_m == 64 || block_m == 128) {
+    int32_t r[3];
+    if (moe_gemm_occupancy(W, block_m, (W->flags & MOE_PREP_GATE_UP) != 0, r) == MOE_OK)
+      for (int j = 0; j < 3; ++j) resident[j] = r[j];
+  }
+  return moe_gemm_choose_occ(W, numel, block_m, num_cus, resident, cfg);
 }

@@ -27,6 +27,20 @@ int device_cu_count() {
 
 static bool al(const void* p, uintptr_t n) { return ((uintptr_t)p & (n - 1)) == 0; }
 
+// Residency of the MFMA kernel variants, per device: the occupancy API is asked once per
+// (device, format, bias, gated, block_m) and the answer kept.
+struct ResidencyKey {
+  int dev, qtype, bias, gated, block_m;
+  bool operator==(const ResidencyKey& o) const {
+    return dev == o.dev && qtype == o.qtype && bias == o.bias && gated == o.gated && block_m == o.block_m;
+  }
+};
+static std::mutex g_res_mu;
+static ResidencyKey g_res_key[256];
+static int g_res_val[256][3];
+static int g_res_n;
+
+
 // Routed mode (topk_ids set): the align of the numel <= kFusedAlignSlots slots is computed inside
 // the streaming kernel, and sorted_token_ids / expert_ids / num_tokens_post_padded / slot_local
 // are its outputs instead of inputs.
@@ -213,6 +227,42 @@ static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64
 }  // namespace moe
 
 using namespace moe;
+
+extern "C" int moe_gemm_occupancy(const moe_weights* W, int32_t block_m, int32_t gated, int32_t resident[3]) {
+  MOE_REQUIRE(W && resident, MOE_EINVAL, "moe_gemm_occupancy: null pointer");
+  MOE_REQUIRE(W->qtype >= 0 && W->qtype <= 3, MOE_EINVAL, "moe_gemm_occupancy: bad qtype %d", W->qtype);
+  MOE_REQUIRE(block_m == 16 || block_m == 32 || block_m == 64 || block_m == 128, MOE_EINVAL,
+              "moe_gemm_occupancy: block_m=%d (16, 32, 64 or 128)", block_m);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MOE_EHIP, "moe_gemm_occupancy: hipGetDevice: %s", hipGetErrorString(e));
+  }
+  const ResidencyKey key{dev, W->qtype, W->bias != nullptr, gated != 0, block_m};
+  std::lock_guard<std::mutex> lock(g_res_mu);
+  for (int i = 0; i < g_res_n; ++i)
+    if (g_res_key[i] == key) {
+      for (int j = 0; j < 3; ++j) resident[j] = g_res_val[i][j];
+      return ok();
+    }
+  int r[3] = {0, 0, 0};
+  const bool bias = W->bias != nullptr;
+  switch (W->qtype) {
+    case MOE_Q_INT4_G128: mfma_residency<MOE_Q_INT4_G128>(bias, gated, block_m, r); break;
+    case MOE_Q_NVFP4_G16: mfma_residency<MOE_Q_NVFP4_G16>(bias, gated, block_m, r); break;
+    case MOE_Q_INT4ZP_G128: mfma_residency<MOE_Q_INT4ZP_G128>(bias, gated, block_m, r); break;
+    default: mfma_residency<MOE_Q_MXFP4_G32>(bias, gated, block_m, r); break;
+  }
+  MOE_REQUIRE(r[1] > 0 && r[2] > 0, MOE_EHIP, "moe_gemm_occupancy: the occupancy API gave no answer");
+  if (g_res_n < 256) {
+    g_res_key[g_res_n] = key;
+    for (int j = 0; j < 3; ++j) g_res_val[g_res_n][j] = r[j];
+    ++g_res_n;
+  }
+  for (int j = 0; j < 3; ++j) resident[j] = r[j];
+  return ok();
+}
 
 extern "C" int moe_w4a16_gemm(const uint16_t* A, int64_t a_rows, int32_t lda, uint16_t* C, int32_t ldc,
                               const moe_weights* W, const int32_t* sorted_token_ids,

@@ -221,6 +221,8 @@ int launch_gemm_stream(bool bias, int act, const GemmArgs& a, const moe_gemm_con
 template <int QT>
 int launch_gemm_mfma(bool bias, int act, const GemmArgs& a, const moe_gemm_config& c, int cap_blocks,
                      hipStream_t st);
+template <int QT>
+int mfma_residency(bool bias, bool gated, int block_m, int* resident);
 int device_cu_count();
 
 }  // namespace moe

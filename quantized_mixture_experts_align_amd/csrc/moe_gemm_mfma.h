@@ -18,6 +18,8 @@
 // tiles I/16 tiles further down, so each lane holds gate and up of the same (slot, column).
 #pragma once
 
+#include <type_traits>
+
 #include "moe_gemm_common.h"
 
 namespace moe {
@@ -124,6 +126,18 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
     s_crow[tid] = (s >= 0 && s < a.numel) ? s : -1;
   }
   __syncthreads();
+  // Live 16-slot groups of this block: up to the group of its last live row.  An expert's slots
+  // fill its blocks from the front, so only its last block has padding, and there the MFMAs of
+  // the all-padding groups are skipped: the tail of each expert runs as a 16/32/.../112-slot
+  // tile, chosen here from the expert's row count (results are the same bit for bit).
+  int lg;
+  {
+    const uint64_t m0 = __ballot(lane < BM && s_crow[lane < BM ? lane : 0] >= 0);
+    const uint64_t m1 = BM > 64 ? __ballot(s_crow[BM > 64 ? 64 + lane : 0] >= 0) : 0ull;
+    const int last = m1 ? 127 - __clzll((long long)m1) : (m0 ? 63 - __clzll((long long)m0) : -1);
+    lg = __builtin_amdgcn_readfirstlane((last + 16) >> 4);
+  }
+  if (lg == 0) return;  // (uniform over the workgroup: no barrier follows for anyone)
 
   // activation fragment f = l*256 + tid -> k-step i, m-group g, MFMA lane fl: row g*16 + fl%16,
   // columns 32 i + 8 (fl/16) + 0..7 of the step; stage slot f (wave-contiguous for the DMA)
@@ -202,8 +216,11 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
   for (int s = 0; s < kStages - 1; ++s)
     if (s < KT) issue(s, s);
 
-  // one K step: wait for its operands, prefetch a later step, dequantise and multiply
-  auto step = [&](int kt, int u) {
+  // one K step: wait for its operands, prefetch a later step, dequantise and multiply.  With
+  // PARTIAL (an expert's last block), the 16-slot groups from lg on are all padding and their
+  // MFMAs are skipped; full blocks run the loop without those branches.
+  auto step = [&](auto partial, int kt, int u) {
+    constexpr bool PARTIAL = decltype(partial)::value;
     // this wave's loads of step kt have landed once only later steps' loads are pending
     const int later = min(kStages - 2, KT - 1 - kt);
     if (xwave) wait_step<XL + LW, kStages>(later); else wait_step<LW, kStages>(later);
@@ -226,6 +243,9 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
       for (int g = 0; g < NG; ++g) af[g] = dequant8<QT>(wq[g][i], sc[g].s(i, lane), sc[g].m(i, lane));
 #pragma unroll
       for (int h = 0; h < MG; ++h) {
+        if constexpr (PARTIAL) {
+          if (h >= lg) break;
+        }
         const u32x4_t bf = xs[(i * MG + h) * 64 + lane];
 #pragma unroll
         for (int g = 0; g < NG; ++g) acc[g][h] = mfma(af[g], bf, acc[g][h]);
@@ -234,14 +254,18 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
   };
   // whole rounds of kStages steps (stage index = compile-time constant), then the remaining steps;
   // no early exit inside the unrolled round, which would make the accumulators change registers
-  int kt0 = 0;
-  for (; kt0 + kStages <= KT; kt0 += kStages) {
+  auto k_loop = [&](auto partial) {
+    int kt0 = 0;
+    for (; kt0 + kStages <= KT; kt0 += kStages) {
 #pragma unroll
-    for (int u = 0; u < kStages; ++u) step(kt0 + u, u);
-  }
+      for (int u = 0; u < kStages; ++u) step(partial, kt0 + u, u);
+    }
 #pragma unroll
-  for (int u = 0; u < kStages - 1; ++u)
-    if (kt0 + u < KT) step(kt0 + u, u);
+    for (int u = 0; u < kStages - 1; ++u)
+      if (kt0 + u < KT) step(partial, kt0 + u, u);
+  };
+  if (MG == 1 || lg == MG) k_loop(std::false_type{});
+  else k_loop(std::true_type{});
 
   // epilogue: lane holds D[n = 4 (lane/16) + q][m = lane % 16] of each (n-tile, m-group)
   float gsv = 1.f;
@@ -309,6 +333,46 @@ static int launch_mfma_b(const GemmArgs& a, int ng, int blocks, hipStream_t st) 
       return fail(MOE_EUNSUPPORTED, "moe_w4a16_gemm: MFMA kernel needs block_m 16/32/64/128, got %d",
                   a.block_m);
   }
+}
+
+// Resident workgroups per CU of one kernel variant on the current device, as the HIP occupancy
+// API computes them from its registers and LDS (0 when the runtime does not answer).
+template <int QT, bool BIAS, int MG, int NG, int ACT>
+static int resident_of() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(&gemm_mfma_kernel<QT, BIAS, MG, NG, ACT>), 256, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return n;
+}
+
+template <int QT, bool BIAS, int MG, int ACT>
+static void resident_mg(int* r) {
+  if constexpr (act_paired<ACT>()) r[0] = 0;
+  else r[0] = resident_of<QT, BIAS, MG, 1, ACT>();
+  r[1] = resident_of<QT, BIAS, MG, 2, ACT>();
+  r[2] = resident_of<QT, BIAS, MG, 4, ACT>();
+}
+
+template <int QT, bool BIAS, int ACT>
+static int residency_b(int block_m, int* r) {
+  switch (block_m) {
+    case 16: resident_mg<QT, BIAS, 1, ACT>(r); return 0;
+    case 32: resident_mg<QT, BIAS, 2, ACT>(r); return 0;
+    case 64: resident_mg<QT, BIAS, 4, ACT>(r); return 0;
+    case 128: resident_mg<QT, BIAS, 8, ACT>(r); return 0;
+    default: return -1;
+  }
+}
+
+// r[0..2]: resident workgroups per CU at ng = 1, 2, 4 (the SiLU variant stands for both gated
+// activations, the plain one for the others; their register use is within a few of each other).
+template <int QT>
+int mfma_residency(bool bias, bool gated, int block_m, int* r) {
+  if (gated) return bias ? residency_b<QT, true, kActSilu>(block_m, r) : residency_b<QT, false, kActSilu>(block_m, r);
+  return bias ? residency_b<QT, true, kActNone>(block_m, r) : residency_b<QT, false, kActNone>(block_m, r);
 }
 
 template <int QT>

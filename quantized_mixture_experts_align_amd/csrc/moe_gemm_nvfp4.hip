@@ -6,4 +6,5 @@
 namespace moe {
 template int launch_gemm_decode<MOE_Q_NVFP4_G16>(bool, int, const GemmArgs&, const moe_gemm_config&, int, int, hipStream_t);
 template int launch_gemm_mfma<MOE_Q_NVFP4_G16>(bool, int, const GemmArgs&, const moe_gemm_config&, int, hipStream_t);
+template int mfma_residency<MOE_Q_NVFP4_G16>(bool, bool, int, int*);
 }  // namespace moe

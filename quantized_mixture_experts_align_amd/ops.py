@@ -161,11 +161,27 @@ def gemm_config(kernel: int = L.GEMM_AUTO, ng: int = 0, ksplit: int = 0, gemv_ro
     return L.MoeGemmConfig(kernel, ng, ksplit, gemv_rows, group_m)
 
 
-def gemm_choose(W: PreparedWeights, numel: int, block_m: int, num_cus: int = 0) -> L.MoeGemmConfig:
+def gemm_choose(W: PreparedWeights, numel: int, block_m: int, num_cus: int = 0,
+                resident: Optional[tuple] = None) -> L.MoeGemmConfig:
+    """Launch configuration; `resident` = MFMA workgroups per CU at 1, 2, 4 tiles per wave
+    (moe_gemm_choose_occ), else the current device's (moe_gemm_choose)."""
     c = L.MoeGemmConfig()
-    L.check(L.lib().moe_gemm_choose(C.byref(W.desc), numel, block_m, num_cus, C.byref(c)),
-            "moe_gemm_choose")
+    if resident is None:
+        L.check(L.lib().moe_gemm_choose(C.byref(W.desc), numel, block_m, num_cus, C.byref(c)),
+                "moe_gemm_choose")
+    else:
+        r = (C.c_int32 * 3)(*resident)
+        L.check(L.lib().moe_gemm_choose_occ(C.byref(W.desc), numel, block_m, num_cus, C.byref(r), C.byref(c)),
+                "moe_gemm_choose_occ")
     return c
+
+
+def gemm_occupancy(W: PreparedWeights, block_m: int, gated: bool) -> tuple:
+    """(resident workgroups per CU at 1, 2, 4 tiles per wave) of the MFMA kernel, from the HIP
+    occupancy API on the current device."""
+    r = (C.c_int32 * 3)()
+    L.check(L.lib().moe_gemm_occupancy(C.byref(W.desc), block_m, int(gated), C.byref(r)), "moe_gemm_occupancy")
+    return tuple(r)
 
 
 def moe_w4a16_gemm(A: torch.Tensor, W: PreparedWeights, sorted_token_ids: torch.Tensor,

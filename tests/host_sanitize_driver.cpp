@@ -15,6 +15,8 @@
 namespace moe {
 int device_cu_count() { return 256; }  // (the GEMM sources that define it are not linked here)
 }
+// (the GEMM sources are not linked: no device answers, so moe_gemm_choose takes the launch bound)
+extern "C" int moe_gemm_occupancy(const moe_weights*, int32_t, int32_t, int32_t*) { return MOE_EHIP; }
 
 static int failures = 0;
 #define CHECK(cond)                                                   \
@@ -118,6 +120,15 @@ int main() {
     }
   }
   CHECK(moe_gemm_choose(nullptr, 8, 16, 256, &cfg) == MOE_EINVAL);
+  // with any residency the prefill choice is one of the built tile counts
+  for (int r4 : {1, 2, 3, 4, 8})
+    for (int64_t numel : {256, 2048, 23283, 1 << 20})
+      for (int32_t block : {32, 64, 128}) {
+        const int32_t res[3] = {8, 4, r4};
+        CHECK(moe_gemm_choose_occ(&w, numel, block, 256, res, &cfg) == MOE_OK);
+        CHECK(cfg.kernel == MOE_GEMM_MFMA && (cfg.ng == 1 || cfg.ng == 2 || cfg.ng == 4));
+      }
+  CHECK(moe_gemm_choose_occ(&w, 8, 64, 256, nullptr, &cfg) == MOE_EINVAL);
 
   moe_requant_config rq{};
   for (int32_t E : {1, 8, 32, 256, 1024})

@@ -244,6 +244,38 @@ def test_gemm_choose_tiles_for_streamed_prefill_weights():
     assert cfg("int4zp_g128", 2048, 512, 8, L.PREP_GATE_UP, numel=4608) == (2, 8)
 
 
+def test_gemm_choose_weighs_tile_counts_by_residency():
+    # four tiles per wave only when that needs no more rounds of resident workgroups than two
+    # (NVFP4 slice, down projection N = K = 4096, 64-slot blocks: 16 x 55 workgroups with four
+    # tiles, 32 x 55 with two)
+    W = P.PreparedWeights(None, L.MoeWeights(L.QTYPE["nvfp4_g16"], 32, 4096, 4096, 4096, 4096, 0, 0, 1, 1,
+                                             None, None))
+    # the 64-slot kernels' residency on gfx950: 7 / 6 / 4 per CU -> one round with four tiles,
+    # two with two tiles
+    assert P.gemm_choose(W, 1479, 64, 256, resident=(7, 6, 4)).ng == 4
+    # if four-tile workgroups fitted only one per CU they would need four rounds against two
+    assert P.gemm_choose(W, 1479, 64, 256, resident=(7, 6, 1)).ng == 2
+    # the launch bound's two per CU everywhere: two rounds each, four tiles
+    assert P.gemm_choose(W, 1479, 64, 256, resident=(2, 2, 2)).ng == 4
+    # a four-tile grid smaller than the CU count is never taken
+    assert P.gemm_choose(W, 1479, 64, 1024, resident=(7, 6, 4)).ng == 2     # 880 < 1024 CUs
+    # short K (int4, 64-slot blocks): two tiles whatever the residency; one when two leave CUs idle
+    Wi = P.PreparedWeights(None, L.MoeWeights(L.QTYPE["int4_g128"], 8, 512, 1024, 512, 1024, 0, 0, 1, 1,
+                                              None, None))
+    for res in [(7, 6, 4), (2, 2, 2), (8, 8, 8)]:
+        assert P.gemm_choose(Wi, 4608, 64, 256, resident=res).ng == 2
+        assert P.gemm_choose(Wi, 4608, 64, 1024, resident=res).ng == 1
+    c = L.MoeGemmConfig()
+    assert L.lib().moe_gemm_choose_occ(C.byref(W.desc), 1479, 64, 256, None, C.byref(c)) == L.MOE_EINVAL
+
+
+def test_block_m_takes_128_slot_blocks_for_many_live_rows_per_expert():
+    assert P.choose_block_m(8192, 128, 8192, 2880) == 128    # MXFP4 M=2048: 64 live rows per expert
+    assert P.choose_block_m(2048, 32, 256, 4096) == 64       # NVFP4 slice M=256: 8 expected live rows
+    assert P.choose_block_m(8192, 32, 1024, 4096) == 128     # NVFP4 slice M=1024: 256 slots per expert
+    assert P.choose_block_m(4608, 8, 4608, 512) == 64        # int4 M=2304: below 8192 slots
+
+
 def test_requant_choose_contract():
     lib = L.lib()
 
