@@ -10,10 +10,13 @@ Test infrastructure only (see the package docstring).
 * float8 e4m3fn: the NVFP4 per-16 block scale (``w13_sf`` in ``Weights``).
 * E8M0: the MXFP4 per-32 block scale, ``2^(e - 127)``.
 * bf16: activations, biases, int4 scales and every stored intermediate.
+* float16 (IEEE binary16): the zero points of the asymmetric int4 format with
+  float zero points (the Marlin template's ``is_zp_float`` case).
 
 Pins: e4m3fn and E8M0 against torch's ``float8_e4m3fn`` / ``float8_e8m0fnu``
 views for all 256 codes; E2M1 against its bit-field definition; bf16
-decode/rounding against torch's float32 casts plus hand-built ties.
+decode/rounding against torch's float32 casts plus hand-built ties; float16
+against numpy's ``float16`` view for all 65536 codes.
 """
 from __future__ import annotations
 
@@ -52,6 +55,19 @@ def decode_e8m0(codes: np.ndarray) -> np.ndarray:
     """E8M0: a bare exponent, 2^(e - 127); code 255 is NaN."""
     c = np.asarray(codes, dtype=np.int64)
     return np.where(c == 255, np.nan, np.exp2(c.astype(np.float64) - 127.0))
+
+
+def decode_fp16(bits: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit patterns (uint16) -> float64: 1 sign, 5 exponent bits with bias 15,
+    10 mantissa bits; exponent 0 holds the subnormals m * 2^-24, exponent 31 infinities (m = 0)
+    and NaN."""
+    c = np.asarray(bits).astype(np.int64)
+    sign = np.where(c >> 15, -1.0, 1.0)
+    e = (c >> 10) & 0x1F
+    m = (c & 0x3FF).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -24, (1.0 + m / 1024.0) * np.exp2(e.astype(np.float64) - 15.0))
+    mag = np.where(e == 0x1F, np.where(m == 0, np.inf, np.nan), mag)
+    return sign * mag
 
 
 def decode_bf16(bits: np.ndarray) -> np.ndarray:

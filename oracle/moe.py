@@ -24,11 +24,13 @@ design notes of the repository):
   gate/up halves) and ``a = relu(h)^2``;
 * ``routed_scaling_factor`` (passed as 1.0 in that test, not defined on the
   pages) multiplies the combined output of each token;
-* asymmetric int4 (the ``w1_zeros`` / ``w2_zeros`` and ``is_zp_float`` arguments of
-  the Marlin MoE call in sglang PR 31552, used with integer zero points): unsigned
-  codes, one integer zero point 0..15 and one bf16 scale per group of 128 along K,
-  stored one zero point per byte in ``[N, K/128]`` like the scales; the weight is
-  ``(u - z) * s``;
+* asymmetric int4 (the ``w1_zeros`` / ``w2_zeros`` arguments of the Marlin MoE call
+  in sglang PR 31552): unsigned codes, one zero point and one bf16 scale per group
+  of 128 along K, the weight ``(u - z) * s``.  With integer zero points
+  (``int4zp_g128``) z is 0..15, stored one per byte in ``[N, K/128]`` like the
+  scales; with float zero points (``int4zpf_g128``, the Marlin template's
+  ``is_zp_float`` flag, whose comment names float16) z is a float16 value, stored
+  as its bit pattern in the same ``[N, K/128]`` layout;
 * act-order int4 (the ``g_idx1`` / ``g_idx2`` arguments of that call; the pages pass the
   setup's result through without defining it): ``g_idx[k]`` names the group of 128 whose
   scale (and zero point) input column ``k`` uses; every group holds 128 columns, in any
@@ -41,10 +43,11 @@ from typing import Optional
 
 import numpy as np
 
-from .formats import (decode_bf16, decode_e2m1, decode_e4m3fn, decode_e8m0, decode_uint4,
+from .formats import (decode_bf16, decode_e2m1, decode_e4m3fn, decode_e8m0, decode_fp16, decode_uint4,
                       decode_uint4b8, round_to_bf16)
 
-_GROUP = {"int4_g128": 128, "nvfp4_g16": 16, "mxfp4_g32": 32, "int4zp_g128": 128}
+_GROUP = {"int4_g128": 128, "nvfp4_g16": 16, "mxfp4_g32": 32, "int4zp_g128": 128, "int4zpf_g128": 128}
+INT4_FORMATS = ("int4_g128", "int4zp_g128", "int4zpf_g128")
 
 
 # ----------------------------------------------------------------------------- routing
@@ -117,6 +120,7 @@ def dequant(qtype: str, codes: np.ndarray, scales: np.ndarray, gs: Optional[floa
     * int4_g128: ``(u - 8) * s[n, G(k)]`` with bf16 ``s`` (uint4b8, group 128).
     * int4zp_g128: ``(u - z[n, G(k)]) * s[n, G(k)]``, unsigned ``u``, integer
       zero point ``z`` in 0..15, bf16 ``s`` (asymmetric int4, group 128).
+    * int4zpf_g128: the same with ``z`` a float16 value (its bit pattern given).
     * nvfp4_g16: ``e2m1 * e4m3[n, k // 16] * gs`` (one fp32 global scale per
       expert and projection, as the experiment's ``_marlin_layer`` passes it).
     * mxfp4_g32: ``e2m1 * 2^(E[n, k // 32] - 127)``.
@@ -128,17 +132,17 @@ def dequant(qtype: str, codes: np.ndarray, scales: np.ndarray, gs: Optional[floa
     """
     q = _nibbles(codes)
     g = _GROUP[qtype]
-    if g_idx is not None and qtype not in ("int4_g128", "int4zp_g128"):
+    if g_idx is not None and qtype not in INT4_FORMATS:
         raise ValueError("act-order (g_idx) is defined for the int4 formats only")
     K = q.shape[-1]
     grp = (np.arange(K) // g) if g_idx is None else np.asarray(g_idx, dtype=np.int64)
     if qtype == "int4_g128":
         s = decode_bf16(scales)
         return decode_uint4b8(q) * s[..., grp]
-    if qtype == "int4zp_g128":
+    if qtype in ("int4zp_g128", "int4zpf_g128"):
         if zeros is None:
             raise ValueError("asymmetric int4 needs the zero points")
-        z = np.asarray(zeros, dtype=np.float64)
+        z = np.asarray(zeros, dtype=np.float64) if qtype == "int4zp_g128" else decode_fp16(zeros)
         return (decode_uint4(q) - z[..., grp]) * decode_bf16(scales)[..., grp]
     if qtype == "nvfp4_g16":
         if gs is None:

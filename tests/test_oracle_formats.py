@@ -54,6 +54,19 @@ def test_uint4b8_is_offset_binary():
     assert list(got) == list(range(-8, 8))
 
 
+def test_fp16_decode_matches_numpy_for_all_codes():
+    # every binary16 pattern: normals, subnormals, signed zeros, infinities and NaNs
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = F.decode_fp16(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    # hand values: 0x3C00 = 1, 0x4780 = 7.5, 0x0001 = 2^-24 (smallest subnormal), 0x7BFF = 65504
+    assert list(F.decode_fp16(np.array([0x3C00, 0x4780, 0x0001, 0x7BFF], np.uint16))) == [1.0, 7.5, 2.0 ** -24, 65504.0]
+
+
 def test_bf16_decode_matches_torch():
     rng = np.random.default_rng(0)
     bits = rng.integers(0, 1 << 16, size=4096, dtype=np.uint32).astype(np.uint16)

@@ -63,6 +63,10 @@ def _brute_dequant_matvec(qtype, codes, scales, gs, x, zeros=None, g_idx=None):
             elif qtype == "int4zp_g128":
                 s = struct.unpack("<f", struct.pack("<I", int(scales[n, grp[k]]) << 16))[0]
                 w = (u - int(zeros[n, grp[k]])) * s
+            elif qtype == "int4zpf_g128":
+                s = struct.unpack("<f", struct.pack("<I", int(scales[n, grp[k]]) << 16))[0]
+                z = struct.unpack("<e", struct.pack("<H", int(zeros[n, grp[k]])))[0]   # binary16
+                w = (u - z) * s
             else:
                 sign = -1.0 if u & 8 else 1.0
                 e, m = (u >> 1) & 3, u & 1
@@ -77,17 +81,19 @@ def _brute_dequant_matvec(qtype, codes, scales, gs, x, zeros=None, g_idx=None):
 
 
 @pytest.mark.parametrize("qtype,N,K", [("int4_g128", 3, 256), ("nvfp4_g16", 5, 48), ("mxfp4_g32", 4, 96),
-                                        ("int4zp_g128", 3, 384)])
+                                        ("int4zp_g128", 3, 384), ("int4zpf_g128", 3, 384)])
 def test_dequant_matches_per_element_brute_force(qtype, N, K):
     rng = np.random.default_rng(7)
     codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
     g = W.GROUP[qtype]
     zeros = None
-    if qtype in ("int4_g128", "int4zp_g128"):
+    if qtype in ("int4_g128", "int4zp_g128", "int4zpf_g128"):
         scales = W._to_bf16_bits(rng.uniform(0.002, 0.02, (N, K // g)).astype(np.float32))
         gs = None
         if qtype == "int4zp_g128":
             zeros = rng.integers(0, 16, size=(N, K // g), dtype=np.uint8)
+        if qtype == "int4zpf_g128":     # any float16, also outside 0..15 and non-integer
+            zeros = rng.uniform(-4.0, 20.0, size=(N, K // g)).astype(np.float16).view(np.uint16)
     elif qtype == "nvfp4_g16":
         scales = rng.integers(0x20, 0x70, size=(N, K // g), dtype=np.uint8)
         gs = np.float32(3.1e-3)
@@ -193,6 +199,27 @@ def test_dequant_asymmetric_int4_closed_forms():
     assert np.all(d[1, :128] == 0.0) and np.all(d[1, 128:] == 8 * 2.0 ** -7)
     d = O.dequant("int4zp_g128", np.full((1, 64), 0x2D, np.uint8), s[:1, :1], None, np.full((1, 1), 5, np.uint8))
     assert d[0, 0] == 8 * 2.0 ** -7 and d[0, 1] == -3 * 2.0 ** -7
+
+
+def test_dequant_float_zero_point_closed_forms():
+    # float16 zero points: 7.5 (0x4780), 0.1 (0x2E66 = 0.0999755859375, not 0.1) and -2 (0xC000);
+    # nibble 13 (0xDD), scale 2^-7
+    s = np.full((1, 3), _bf16(2.0 ** -7), np.uint16)
+    z = np.array([[0x4780, 0x2E66, 0xC000]], np.uint16)
+    d = O.dequant("int4zpf_g128", np.full((1, 192), 0xDD, np.uint8), s, None, z)
+    assert np.all(d[0, :128] == 5.5 * 2.0 ** -7)
+    assert np.all(d[0, 128:256] == (13 - 0.0999755859375) * 2.0 ** -7)
+    assert np.all(d[0, 256:] == 15 * 2.0 ** -7)
+
+
+def test_dequant_integer_float_zero_points_are_the_integer_format():
+    # float16 zero points holding the integers 0..15 give the integer zero-point format exactly
+    rng = np.random.default_rng(9)
+    codes = rng.integers(0, 256, size=(4, 256), dtype=np.uint8)
+    s = W._to_bf16_bits(rng.uniform(0.002, 0.02, (4, 4)).astype(np.float32))
+    zi = rng.integers(0, 16, size=(4, 4), dtype=np.uint8)
+    zf = zi.astype(np.float16).view(np.uint16)
+    assert np.array_equal(O.dequant("int4zpf_g128", codes, s, None, zf), O.dequant("int4zp_g128", codes, s, None, zi))
 
 
 def test_dequant_asymmetric_int4_with_zero_point_8_is_uint4b8():

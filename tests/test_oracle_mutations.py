@@ -6,6 +6,7 @@ import math
 import numpy as np
 import pytest
 
+import oracle.formats as F
 import oracle.moe as O
 import test_oracle_align as TA
 import test_oracle_layer as TL
@@ -113,6 +114,9 @@ MUTATIONS = {
     "zero point of the wrong group": ("dequant", lambda: (lambda q, c, s, gs=None, zeros=None, g_idx=None:
                                                           ORIG_DQ(q, c, s, gs, None if zeros is None else zeros[..., ::-1], g_idx)
                                                           if q == "int4zp_g128" else ORIG_DQ(q, c, s, gs, zeros, g_idx))),
+    "float zero point read as bf16": ("decode_fp16", lambda: F.decode_bf16),
+    "float zero point rounded to an integer": ("decode_fp16", lambda: (lambda b: np.rint(F.decode_fp16(b)))),
+    "float zero point ignored": ("decode_fp16", lambda: (lambda b: np.zeros(np.shape(b)))),
     "act-order grouping ignored": ("dequant", lambda: (lambda q, c, s, gs=None, zeros=None, g_idx=None:
                                                        ORIG_DQ(q, c, s, gs, zeros))),
     "act-order group of the sorted position": ("dequant", lambda: (lambda q, c, s, gs=None, zeros=None, g_idx=None:
@@ -127,6 +131,8 @@ PINS = [
     (TL.test_dequant_matches_per_element_brute_force, dict(qtype="nvfp4_g16", N=5, K=48)),
     (TL.test_dequant_matches_per_element_brute_force, dict(qtype="int4zp_g128", N=3, K=384)),
     (TL.test_dequant_asymmetric_int4_closed_forms, {}),
+    (TL.test_dequant_matches_per_element_brute_force, dict(qtype="int4zpf_g128", N=3, K=384)),
+    (TL.test_dequant_float_zero_point_closed_forms, {}),
     (TL.test_dequant_asymmetric_int4_with_zero_point_8_is_uint4b8, {}),
     (TL.test_dequant_act_order_brute_force_and_identity_grouping, dict(qtype="int4_g128")),
     (TL.test_dequant_act_order_is_the_plain_format_on_sorted_columns, dict(qtype="int4zp_g128")),

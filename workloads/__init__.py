@@ -14,7 +14,9 @@ Canonical layouts (shared vocabulary of every caller):
   MXFP4 (g = 32).
 * ``gs``      float32 ``[E]``: NVFP4 per-expert global scale (else ``None``).
 * ``zeros``   uint8 ``[E, N, K/128]``: zero points 0..15 of the asymmetric int4
-  format (``int4zp_g128``: unsigned codes, bf16 scales like int4), else ``None``.
+  format (``int4zp_g128``: unsigned codes, bf16 scales like int4); float16 bit
+  patterns (uint16) in the same layout for the float zero-point format
+  (``int4zpf_g128``); else ``None``.
 * ``bias``    bf16 bits ``[E, N]`` or ``None``.
 * ``x``       bf16 bits ``[M, H]``; ``topk_ids`` int32 ``[M, k]`` global ids;
   ``topk_weights`` float32 ``[M, k]``; ``norm_w`` bf16 bits ``[H]``.
@@ -38,7 +40,7 @@ import numpy as np
 import torch
 
 QTYPES = ("int4_g128", "nvfp4_g16", "mxfp4_g32", "int4zp_g128")
-GROUP = {"int4_g128": 128, "nvfp4_g16": 16, "mxfp4_g32": 32, "int4zp_g128": 128}
+GROUP = {"int4_g128": 128, "nvfp4_g16": 16, "mxfp4_g32": 32, "int4zp_g128": 128, "int4zpf_g128": 128}
 
 # stream ids of the seed sequence
 _S_WEIGHTS, _S_HIDDEN, _S_ROUTING, _S_AUX = 0, 1, 2, 3
@@ -159,6 +161,12 @@ def _projection(rng: np.random.Generator, wl: Workload, E: int, N: int, K: int) 
         # 0..15; the tails still reach both ends
         zeros = np.clip(np.rint(rng.normal(7.5, 2.5, size=(E, N, K // g))), 0, 15).astype(np.uint8)
         gs = None
+    elif wl.qtype == "int4zpf_g128":
+        scales = _to_bf16_bits(rng.uniform(0.002, 0.02, size=(E, N, K // g)).astype(np.float32))
+        # float zero points (the offset a min/max quantiser stores unrounded): about the middle
+        # of 0..15, not integers
+        zeros = np.clip(rng.normal(7.5, 2.5, size=(E, N, K // g)), 0.0, 15.0).astype(np.float16).view(np.uint16)
+        gs = None
     elif wl.qtype == "nvfp4_g16":
         scales = _to_e4m3_codes(np.exp2(rng.uniform(4.0, 8.0, size=(E, N, K // g))).astype(np.float32))
         gs = (4.92e-5 * rng.uniform(0.75, 1.25, size=(E,))).astype(np.float32)
@@ -242,6 +250,8 @@ def small_workload(qtype: str, **kw) -> Workload:
                               bias=True, act="swiglu_alpha", interleaved_w13=True, seed=102),
         "int4zp_g128": Workload("int4zp_small", "int4zp_g128", 12, 2, 8, 2, 512, 384, (37,),
                                 bias=True, seed=103),
+        "int4zpf_g128": Workload("int4zpf_small", "int4zpf_g128", 10, 1, 8, 2, 512, 384, (37,),
+                                 seed=104),
     }[qtype]
     return base.replace(**kw) if kw else base
 
