@@ -49,7 +49,8 @@ CSRC = os.path.join(ROOT, "quantized_mixture_experts_align_amd", "csrc")
 GEMM_SRCS = ["moe_gemm.hip", "moe_gemm_common.h", "moe_gemm_mfma.h", "moe_gemm_decode.h",
              "moe_gemm_stream.h", "moe_gemm_int4.hip", "moe_gemm_nvfp4.hip", "moe_gemm_mxfp4.hip",
              "moe_gemm_int4zp.hip", "moe_gemm_stream_int4.hip", "moe_gemm_stream_nvfp4.hip",
-             "moe_gemm_stream_mxfp4.hip", "moe_gemm_stream_int4zp.hip", "moe_internal.h"]
+             "moe_gemm_stream_mxfp4.hip", "moe_gemm_stream_int4zp.hip", "moe_gemm_int4zpf.hip",
+             "moe_gemm_stream_int4zpf.hip", "moe_internal.h"]
 FLUSH_BYTES = 1 << 30          # read between cold steps: more than L2 + MALL
 LAUNCHES = 20                  # back-to-back launches per graph when timing one GEMM
 
@@ -70,8 +71,9 @@ def weight_bytes_per_expert(wl, proj: str) -> int:
     N, K = (2 * wl.I, wl.H) if proj == "w13" else (wl.H, wl.I)
     codes = N * K // 2
     groups = N * (K // wl.group)
-    scales = groups * (2 if wl.qtype in ("int4_g128", "int4zp_g128") else 1)
-    zeros = groups // 2 if wl.qtype == "int4zp_g128" else 0
+    scales = groups * (2 if wl.qtype in ("int4_g128", "int4zp_g128", "int4zpf_g128") else 1)
+    # zero points: 4-bit integers (counted packed), or float16
+    zeros = groups // 2 if wl.qtype == "int4zp_g128" else (2 * groups if wl.qtype == "int4zpf_g128" else 0)
     gs = 4 if wl.qtype == "nvfp4_g16" else 0
     bias = 2 * N if wl.bias else 0
     return codes + scales + zeros + gs + bias

@@ -59,6 +59,10 @@ typedef enum {
   MOE_Q_MXFP4_G32 = 2,    /* E2M1 codes; E8M0 scale per 32 along K                            */
   MOE_Q_INT4ZP_G128 = 3,  /* asymmetric int4: unsigned nibble u, integer zero point z (0..15)
                              and bf16 scale s per 128 along K; the weight is (u - z) * s     */
+  MOE_Q_INT4ZPF_G128 = 4, /* asymmetric int4 with float zero points (the Marlin template's
+                             is_zp_float case of the "sglang PR 31552" summary): unsigned
+                             nibble u, float16 zero point z and bf16 scale s per 128 along K;
+                             the weight is (u - z) * s                                       */
   /* (range sentinels, never valid arguments: they make the type's range all of int32, so that
      an unknown value reaches the library's validation and comes back as MOE_EINVAL)          */
   MOE_Q_RANGE_MIN_ = -2147483647 - 1,
@@ -159,8 +163,9 @@ int moe_w4a16_prepared_size(moe_qtype q, int32_t E, int32_t N, int32_t K, uint32
  *                 codes (MXFP4)
  *   global_scale  device fp32 [E] (NVFP4 only, else NULL)
  *   bias          device bf16 [E, N] or NULL (interleaved like the rows when INTERLEAVED)
- *   zeros         device uint8 [E, N, K/128], zero points 0..15 (MOE_Q_INT4ZP_G128 only, else
- *                 NULL; a value above 15 is an error of the caller and is used modulo 16)
+ *   zeros         MOE_Q_INT4ZP_G128: device uint8 [E, N, K/128], zero points 0..15 (a value above
+ *                 15 is an error of the caller and is used modulo 16); MOE_Q_INT4ZPF_G128: device
+ *                 uint16 [E, N, K/128], float16 bit patterns; NULL for the other formats
  *   g_idx         device int32 [E, K] with MOE_PREP_ACT_ORDER (int4 formats, K <= 16384), else
  *                 NULL: the group of 128 whose scale (and zero point) input column k uses -- the
  *                 g_idx of the Marlin MoE call in the "sglang PR 31552" summary, the GPTQ
@@ -175,7 +180,7 @@ int moe_w4a16_prepared_size(moe_qtype q, int32_t E, int32_t N, int32_t K, uint32
  * (act(0, 0) = 0 for every activation).
  */
 int moe_w4a16_prepare(moe_qtype q, const uint8_t* codes, const void* scales,
-                      const float* global_scale, const uint16_t* bias, const uint8_t* zeros,
+                      const float* global_scale, const uint16_t* bias, const void* zeros,
                       const int32_t* g_idx, int32_t E, int32_t N, int32_t K, uint32_t flags,
                       void* out, size_t out_bytes, moe_weights* desc, hipStream_t stream);
 

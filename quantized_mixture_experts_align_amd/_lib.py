@@ -11,7 +11,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_w4a16.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ESIZE, MOE_EHIP = 0, -1, -2, -3, -4
-QTYPE = {"int4_g128": 0, "nvfp4_g16": 1, "mxfp4_g32": 2, "int4zp_g128": 3}
+QTYPE = {"int4_g128": 0, "nvfp4_g16": 1, "mxfp4_g32": 2, "int4zp_g128": 3, "int4zpf_g128": 4}
 ACT = {"silu_mul": 0, "swiglu_alpha": 1, "relu2": 2}
 GATED = {"silu_mul": True, "swiglu_alpha": True, "relu2": False}
 PREP_GATE_UP, PREP_INTERLEAVED, PREP_PAD, PREP_ACT_ORDER = 0x1, 0x2, 0x4, 0x8

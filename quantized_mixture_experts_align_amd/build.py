@@ -19,6 +19,7 @@ LIB = os.path.join(PKG, "libmoe_w4a16.so")
 SOURCES = ["moe_api.hip", "moe_align.hip", "moe_prepare.hip", "moe_gemm.hip", "moe_gemm_int4.hip",
            "moe_gemm_nvfp4.hip", "moe_gemm_mxfp4.hip", "moe_gemm_int4zp.hip", "moe_gemm_stream_int4.hip",
            "moe_gemm_stream_nvfp4.hip", "moe_gemm_stream_mxfp4.hip", "moe_gemm_stream_int4zp.hip",
+           "moe_gemm_int4zpf.hip", "moe_gemm_stream_int4zpf.hip",
            "moe_act_combine.hip", "moe_requant.hip"]
 ARCH = "gfx950"
 FLAGS = [

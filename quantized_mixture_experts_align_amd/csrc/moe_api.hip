@@ -52,8 +52,7 @@ extern "C" int moe_align_capacity(int64_t M, int32_t top_k, int32_t n_local, int
 extern "C" int moe_w4a16_prepared_size(moe_qtype q, int32_t E, int32_t N, int32_t K, uint32_t flags,
                                        int32_t has_bias, int32_t* N_out, int32_t* K_out,
                                        size_t* bytes) {
-  MOE_REQUIRE(q == MOE_Q_INT4_G128 || q == MOE_Q_NVFP4_G16 || q == MOE_Q_MXFP4_G32 || q == MOE_Q_INT4ZP_G128,
-              MOE_EINVAL, "unknown qtype %d", (int)q);
+  MOE_REQUIRE(valid_qtype(q), MOE_EINVAL, "unknown qtype %d", (int)q);
   MOE_REQUIRE(E >= 1 && N >= 1 && K >= 1, MOE_EINVAL, "E=%d N=%d K=%d must be positive", E, N, K);
   MOE_REQUIRE((flags & ~(MOE_PREP_GATE_UP | MOE_PREP_INTERLEAVED | MOE_PREP_PAD | MOE_PREP_ACT_ORDER)) == 0,
               MOE_EINVAL, "unknown prepare flags 0x%x", flags);

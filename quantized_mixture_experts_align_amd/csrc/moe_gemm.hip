@@ -105,7 +105,7 @@ static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64
                      const int32_t* topk_ids = nullptr, int32_t expert_start = 0, int32_t* slot_local = nullptr,
                      const CombineSpec* cmb = nullptr) {
   MOE_REQUIRE(W, MOE_EINVAL, "moe_w4a16_gemm: null weights");
-  MOE_REQUIRE(W->qtype >= 0 && W->qtype <= 3, MOE_EINVAL, "moe_w4a16_gemm: bad qtype %d", W->qtype);
+  MOE_REQUIRE(valid_qtype(W->qtype), MOE_EINVAL, "moe_w4a16_gemm: bad qtype %d", W->qtype);
   MOE_REQUIRE(W->n_experts >= 1 && W->N >= kTileN && W->N % kTileN == 0 && W->K >= kTileK &&
                   W->K % kTileK == 0,
               MOE_EINVAL, "moe_w4a16_gemm: weights E=%d N=%d K=%d not in the prepared layout",
@@ -196,6 +196,7 @@ static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64
         case MOE_Q_INT4_G128: return launch_gemm_stream<MOE_Q_INT4_G128>(bias, act, a, c, (int)cap_blocks, cus, stream);
         case MOE_Q_NVFP4_G16: return launch_gemm_stream<MOE_Q_NVFP4_G16>(bias, act, a, c, (int)cap_blocks, cus, stream);
         case MOE_Q_INT4ZP_G128: return launch_gemm_stream<MOE_Q_INT4ZP_G128>(bias, act, a, c, (int)cap_blocks, cus, stream);
+        case MOE_Q_INT4ZPF_G128: return launch_gemm_stream<MOE_Q_INT4ZPF_G128>(bias, act, a, c, (int)cap_blocks, cus, stream);
         default: return launch_gemm_stream<MOE_Q_MXFP4_G32>(bias, act, a, c, (int)cap_blocks, cus, stream);
       }
     }
@@ -203,6 +204,7 @@ static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64
       case MOE_Q_INT4_G128: return launch_gemm_decode<MOE_Q_INT4_G128>(bias, act, a, c, (int)cap_blocks, cus, stream);
       case MOE_Q_NVFP4_G16: return launch_gemm_decode<MOE_Q_NVFP4_G16>(bias, act, a, c, (int)cap_blocks, cus, stream);
       case MOE_Q_INT4ZP_G128: return launch_gemm_decode<MOE_Q_INT4ZP_G128>(bias, act, a, c, (int)cap_blocks, cus, stream);
+      case MOE_Q_INT4ZPF_G128: return launch_gemm_decode<MOE_Q_INT4ZPF_G128>(bias, act, a, c, (int)cap_blocks, cus, stream);
       default: return launch_gemm_decode<MOE_Q_MXFP4_G32>(bias, act, a, c, (int)cap_blocks, cus, stream);
     }
   }
@@ -220,6 +222,7 @@ static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64
     case MOE_Q_INT4_G128: return launch_gemm_mfma<MOE_Q_INT4_G128>(bias, act, a, c, (int)cap_blocks, stream);
     case MOE_Q_NVFP4_G16: return launch_gemm_mfma<MOE_Q_NVFP4_G16>(bias, act, a, c, (int)cap_blocks, stream);
     case MOE_Q_INT4ZP_G128: return launch_gemm_mfma<MOE_Q_INT4ZP_G128>(bias, act, a, c, (int)cap_blocks, stream);
+    case MOE_Q_INT4ZPF_G128: return launch_gemm_mfma<MOE_Q_INT4ZPF_G128>(bias, act, a, c, (int)cap_blocks, stream);
     default: return launch_gemm_mfma<MOE_Q_MXFP4_G32>(bias, act, a, c, (int)cap_blocks, stream);
   }
 }
@@ -230,7 +233,7 @@ using namespace moe;
 
 extern "C" int moe_gemm_occupancy(const moe_weights* W, int32_t block_m, int32_t gated, int32_t resident[3]) {
   MOE_REQUIRE(W && resident, MOE_EINVAL, "moe_gemm_occupancy: null pointer");
-  MOE_REQUIRE(W->qtype >= 0 && W->qtype <= 3, MOE_EINVAL, "moe_gemm_occupancy: bad qtype %d", W->qtype);
+  MOE_REQUIRE(valid_qtype(W->qtype), MOE_EINVAL, "moe_gemm_occupancy: bad qtype %d", W->qtype);
   MOE_REQUIRE(block_m == 16 || block_m == 32 || block_m == 64 || block_m == 128, MOE_EINVAL,
               "moe_gemm_occupancy: block_m=%d (16, 32, 64 or 128)", block_m);
   int dev = -1;
@@ -252,6 +255,7 @@ extern "C" int moe_gemm_occupancy(const moe_weights* W, int32_t block_m, int32_t
     case MOE_Q_INT4_G128: mfma_residency<MOE_Q_INT4_G128>(bias, gated, block_m, r); break;
     case MOE_Q_NVFP4_G16: mfma_residency<MOE_Q_NVFP4_G16>(bias, gated, block_m, r); break;
     case MOE_Q_INT4ZP_G128: mfma_residency<MOE_Q_INT4ZP_G128>(bias, gated, block_m, r); break;
+    case MOE_Q_INT4ZPF_G128: mfma_residency<MOE_Q_INT4ZPF_G128>(bias, gated, block_m, r); break;
     default: mfma_residency<MOE_Q_MXFP4_G32>(bias, gated, block_m, r); break;
   }
   MOE_REQUIRE(r[1] > 0 && r[2] > 0, MOE_EHIP, "moe_gemm_occupancy: the occupancy API gave no answer");

@@ -122,6 +122,20 @@ template <> struct TileScale<MOE_Q_INT4ZP_G128> {
   // -z * s is exact in fp32 (4 x 8 significant bits)
   __device__ __forceinline__ float m(int i, int lane) const { return -(float)((raw >> 16) & 0xFu) * s(i, lane); }
 };
+// asymmetric int4 with float zero points: per row and group of 128 one dword, bf16 scale |
+// float16 zero point << 16.
+template <> struct TileScale<MOE_Q_INT4ZPF_G128> {
+  uint32_t raw;
+  static constexpr int kRowBytes = 4;  // per tile pair
+  __device__ __forceinline__ void load(const uint8_t* tile_scales, int kt, int lane) {
+    raw = reinterpret_cast<const uint32_t*>(tile_scales)[(int64_t)(kt >> 1) * 16 + (lane & 15)];
+  }
+  __device__ __forceinline__ float s(int, int) const { return __uint_as_float(raw << 16); }
+  // -z * s is exact in fp32 (11 x 8 significant bits)
+  __device__ __forceinline__ float m(int i, int lane) const {
+    return -(float)__builtin_bit_cast(_Float16, (uint16_t)(raw >> 16)) * s(i, lane);
+  }
+};
 
 __device__ __forceinline__ uint32_t bits2(bf16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
 
@@ -159,9 +173,11 @@ __device__ __forceinline__ u32x4_t dequant8(uint32_t w, float s, float m) {
     o[2] = pack_bf16x2(p2[0] * s, p2[1] * s);
     o[3] = pack_bf16x2(p3[0] * s, p3[1] * s);
   } else {
-    // int4 formats: u * s + m = (u - z) * s, exact in fp32 (4 x 8 significant bits), rounded once
-    // to bf16; even-k nibbles are the low nibbles of the four bytes, odd-k the high ones
-    static_assert(QT == MOE_Q_INT4_G128 || QT == MOE_Q_INT4ZP_G128, "unknown weight format");
+    // int4 formats: u * s + m = (u - z) * s in one fp32 fma (exact for integer zero points: 4 x 8
+    // significant bits), rounded to bf16; even-k nibbles are the low nibbles of the four bytes,
+    // odd-k the high ones
+    static_assert(QT == MOE_Q_INT4_G128 || QT == MOE_Q_INT4ZP_G128 || QT == MOE_Q_INT4ZPF_G128,
+                  "unknown weight format");
     const uint32_t t0 = w & 0x0F0F0F0Fu, t1 = (w >> 4) & 0x0F0F0F0Fu;
     const float m8s = m;
     o[0] = pack_bf16x2(fmaf(ubyte_to_f32<0>(t0), s, m8s), fmaf(ubyte_to_f32<0>(t1), s, m8s));

@@ -33,14 +33,19 @@ constexpr int kTileK = 64;
 constexpr int kTileBytes = kTileN * kTileK / 2;
 
 // the int4 formats: a group of 128 along K spans two 64-column tiles
-inline __host__ __device__ bool pair_grouped(int q) { return q == MOE_Q_INT4_G128 || q == MOE_Q_INT4ZP_G128; }
+inline __host__ __device__ bool pair_grouped(int q) {
+  return q == MOE_Q_INT4_G128 || q == MOE_Q_INT4ZP_G128 || q == MOE_Q_INT4ZPF_G128;
+}
+inline __host__ __device__ bool has_zero_points(int q) { return q == MOE_Q_INT4ZP_G128 || q == MOE_Q_INT4ZPF_G128; }
+inline __host__ __device__ bool valid_qtype(int q) { return q >= MOE_Q_INT4_G128 && q <= MOE_Q_INT4ZPF_G128; }
 inline __host__ __device__ int group_of(int q) { return pair_grouped(q) ? 128 : (q == MOE_Q_NVFP4_G16 ? 16 : 32); }
 
 // Scale bytes per (16-row x 64-column) tile.  NVFP4: 16 rows x 4 e4m3 codes; MXFP4: 16 rows x
 // 2 E8M0 codes; int4: the group of 128 spans two tiles, stored per tile pair as 16 bf16;
-// asymmetric int4: per tile pair 16 dwords, each bf16 scale | zero point << 16.
+// asymmetric int4 (both zero-point kinds): per tile pair 16 dwords, each bf16 scale | zero point
+// << 16 (the integer 0..15, or the float16 bit pattern).
 inline __host__ __device__ int scale_bytes_per_tile(int q) {
-  return q == MOE_Q_NVFP4_G16 ? 64 : (q == MOE_Q_MXFP4_G32 ? 32 : (q == MOE_Q_INT4ZP_G128 ? 32 : 16));
+  return q == MOE_Q_NVFP4_G16 ? 64 : (q == MOE_Q_MXFP4_G32 ? 32 : (has_zero_points(q) ? 32 : 16));
 }
 // bytes of scales per scale step of a 16-row tile column: a tile pair (int4 formats) or a tile
 inline __host__ __device__ int scale_step_bytes(int q) {

@@ -93,12 +93,12 @@ __global__ void prep_codes_kernel(const uint8_t* __restrict__ src, uint32_t* __r
 }
 
 // one thread per output scale element
-__global__ void prep_scales_kernel(const uint8_t* __restrict__ src, const uint8_t* __restrict__ zeros,
+__global__ void prep_scales_kernel(const uint8_t* __restrict__ src, const void* __restrict__ zeros,
                                    uint8_t* __restrict__ dst, PrepGeom g) {
   const int NT = g.Nout / kTileN, KT = g.Kout / kTileK;
   const int grp = group_of(g.q);
   const int ngroups = g.K / grp;  // groups per source row
-  if (g.q == MOE_Q_INT4ZP_G128) {  // padding: unit scale, zero point 0 (padding codes are 0)
+  if (has_zero_points(g.q)) {  // padding: unit scale, zero point 0 (padding codes are 0)
     const uint16_t* s16 = reinterpret_cast<const uint16_t*>(src);
     uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
     const int64_t total = (int64_t)g.E * NT * (KT / 2) * 16;
@@ -113,7 +113,9 @@ __global__ void prep_scales_kernel(const uint8_t* __restrict__ src, const uint8_
       uint32_t v = 0x3F80u;
       if (r >= 0 && kp < ngroups) {
         const int64_t i = ((int64_t)e * g.N + r) * ngroups + kp;
-        v = (uint32_t)s16[i] | ((uint32_t)(zeros[i] & 0xF) << 16);
+        const uint32_t z = g.q == MOE_Q_INT4ZP_G128 ? (uint32_t)(static_cast<const uint8_t*>(zeros)[i] & 0xF)
+                                                    : (uint32_t)static_cast<const uint16_t*>(zeros)[i];
+        v = (uint32_t)s16[i] | (z << 16);
       }
       d32[d] = v;
     }
@@ -269,7 +271,7 @@ extern "C" int moe_permute_cols(const uint16_t* src, int64_t ld_src, int32_t row
 }
 
 extern "C" int moe_w4a16_prepare(moe_qtype q, const uint8_t* codes, const void* scales,
-                                 const float* global_scale, const uint16_t* bias, const uint8_t* zeros,
+                                 const float* global_scale, const uint16_t* bias, const void* zeros,
                                  const int32_t* g_idx, int32_t E, int32_t N, int32_t K, uint32_t flags,
                                  void* out, size_t out_bytes, moe_weights* desc, hipStream_t stream) {
   int32_t Nout = 0, Kout = 0;
@@ -279,7 +281,7 @@ extern "C" int moe_w4a16_prepare(moe_qtype q, const uint8_t* codes, const void* 
   MOE_REQUIRE(codes && scales && out && desc, MOE_EINVAL, "moe_w4a16_prepare: null pointer");
   MOE_REQUIRE((q == MOE_Q_NVFP4_G16) == (global_scale != nullptr), MOE_EINVAL,
               "moe_w4a16_prepare: a global scale is required for NVFP4 and only for NVFP4");
-  MOE_REQUIRE((q == MOE_Q_INT4ZP_G128) == (zeros != nullptr), MOE_EINVAL,
+  MOE_REQUIRE(has_zero_points(q) == (zeros != nullptr), MOE_EINVAL,
               "moe_w4a16_prepare: zero points are required for asymmetric int4 and only for it");
   MOE_REQUIRE(((flags & MOE_PREP_ACT_ORDER) != 0) == (g_idx != nullptr), MOE_EINVAL,
               "moe_w4a16_prepare: g_idx is required with MOE_PREP_ACT_ORDER and only with it");

@@ -100,9 +100,9 @@ def moe_w4a16_prepare(qtype: str, codes: torch.Tensor, scales: torch.Tensor,
                       global_scale: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
                       flags: int = 0, zeros: Optional[torch.Tensor] = None,
                       g_idx: Optional[torch.Tensor] = None) -> PreparedWeights:
-    """Repack canonical [E, N, K/2] codes and [E, N, K/g] scales (and, for int4zp_g128, the
-    uint8 [E, N, K/128] zero points; for act-order int4, the int32 [E, K] g_idx, which sets
-    MOE_PREP_ACT_ORDER) into the tiled layout."""
+    """Repack canonical [E, N, K/2] codes and [E, N, K/g] scales (and the [E, N, K/128] zero
+    points: uint8 for int4zp_g128, float16 (or its int16 bit patterns) for int4zpf_g128; for
+    act-order int4, the int32 [E, K] g_idx, which sets MOE_PREP_ACT_ORDER) into the tiled layout."""
     if g_idx is not None:
         _need(g_idx, torch.int32, "g_idx")
         flags |= L.PREP_ACT_ORDER
@@ -119,7 +119,13 @@ def moe_w4a16_prepare(qtype: str, codes: torch.Tensor, scales: torch.Tensor,
         if not bias.is_cuda or not bias.is_contiguous():
             raise ValueError("bias must be a contiguous device tensor")
     if zeros is not None:
-        _need(zeros, torch.uint8, "zeros")
+        if qtype == "int4zpf_g128":
+            if zeros.dtype not in (torch.float16, torch.int16, torch.uint16):
+                raise ValueError("int4zpf_g128 zero points must be float16 values or their bit patterns")
+            if not zeros.is_cuda or not zeros.is_contiguous():
+                raise ValueError("zeros must be a contiguous device tensor")
+        else:
+            _need(zeros, torch.uint8, "zeros")
     _, _, nbytes = prepared_size(qtype, E, N, K, flags, bias is not None)
     buf = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
     desc = L.MoeWeights()

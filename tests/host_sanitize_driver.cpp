@@ -46,7 +46,7 @@ int main() {
   CHECK(std::strlen(moe_last_error()) > 0);
 
   // ---- prepared sizes: every format and flag combination, valid and invalid
-  const moe_qtype qs[] = {MOE_Q_INT4_G128, MOE_Q_NVFP4_G16, MOE_Q_MXFP4_G32, MOE_Q_INT4ZP_G128};
+  const moe_qtype qs[] = {MOE_Q_INT4_G128, MOE_Q_NVFP4_G16, MOE_Q_MXFP4_G32, MOE_Q_INT4ZP_G128, MOE_Q_INT4ZPF_G128};
   for (moe_qtype q : qs) {
     for (uint32_t flags = 0; flags < 16; ++flags) {
       for (int K : {128, 192, 2880, 4096}) {
@@ -57,7 +57,7 @@ int main() {
           CHECK(moe_w4a16_prepared_size(q, 4, 5760, K, flags, 1, &n, &k, &bytes_bias) == MOE_OK);
           CHECK(bytes_bias > bytes && bytes % 256 == 0 && k >= K && k % 64 == 0 && n % 16 == 0);
           const bool ao = flags & MOE_PREP_ACT_ORDER;
-          CHECK(!ao || (q == MOE_Q_INT4_G128 || q == MOE_Q_INT4ZP_G128));
+          CHECK(!ao || (q == MOE_Q_INT4_G128 || q == MOE_Q_INT4ZP_G128 || q == MOE_Q_INT4ZPF_G128));
           if (ao) {
             size_t plain = 0;
             CHECK(moe_w4a16_prepared_size(q, 4, 5760, K, flags & ~MOE_PREP_ACT_ORDER, 0, &n, &k, &plain) == MOE_OK);

@@ -23,7 +23,7 @@ def _perm_of(Wp, E, K):
     return Wp.buffer[off: off + E * K * 4].view(torch.int32).view(E, K).cpu().numpy()
 
 
-@pytest.mark.parametrize("qtype", ["int4_g128", "int4zp_g128"])
+@pytest.mark.parametrize("qtype", ["int4_g128", "int4zp_g128", "int4zpf_g128"])
 def test_prepared_column_order_is_the_stable_sort_of_g_idx(qtype):
     wl = _act_order_workload(qtype)
     lw = W.make_weights(wl)
@@ -62,7 +62,7 @@ def test_permute_cols_matches_a_gather(offset):
             assert (out[r] == 7.0).all(), r
 
 
-@pytest.mark.parametrize("qtype", ["int4_g128", "int4zp_g128"])
+@pytest.mark.parametrize("qtype", ["int4_g128", "int4zp_g128", "int4zpf_g128"])
 @pytest.mark.parametrize("M", [1, 4, 37, 300])
 def test_act_order_layer_matches_oracle(qtype, M):
     # M = 1, 4, 37: 16-slot blocks (streaming kernel); M = 300: 64-slot blocks (MFMA kernel)

@@ -39,7 +39,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-QTYPES = ("int4_g128", "nvfp4_g16", "mxfp4_g32", "int4zp_g128")
+QTYPES = ("int4_g128", "nvfp4_g16", "mxfp4_g32", "int4zp_g128", "int4zpf_g128")
 GROUP = {"int4_g128": 128, "nvfp4_g16": 16, "mxfp4_g32": 32, "int4zp_g128": 128, "int4zpf_g128": 128}
 
 # stream ids of the seed sequence
@@ -82,7 +82,8 @@ class Workload:
 # The workloads, by name: int4 layers of 8 experts (123 tokens; 2304 tokens with biases),
 # one GPU's NVFP4 slice of 32 of 256 experts (uniform decode batches; Zipf-routed prefill
 # batches, same weights), a 128-expert MXFP4 GPT-OSS-style layer, and the int4 layer's shapes
-# with asymmetric int4 (zero points) weights and with act-order (g_idx) int4 weights.
+# with asymmetric int4 weights (integer zero points; float16 zero points, with biases) and
+# with act-order (g_idx) int4 weights.
 WORKLOADS = {w.name: w for w in [
     Workload("int4_m123_e8_top2_h512_i1024", "int4_g128", 8, 0, 8, 2, 512, 1024,
              (123,), seed=0),
@@ -98,8 +99,10 @@ WORKLOADS = {w.name: w for w in [
              (1, 2304), seed=5),
     Workload("int4_actorder_bias_e8_top2_h512_i1024", "int4_g128", 8, 0, 8, 2, 512, 1024,
              (1, 2304), bias=True, act_order=True, seed=6),
+    Workload("int4zpf_bias_e8_top2_h512_i1024", "int4zpf_g128", 8, 0, 8, 2, 512, 1024,
+             (1, 2304), bias=True, seed=7),
 ]}
-INT4_SMALL, INT4_BIAS, NVFP4_DECODE, NVFP4_ZIPF, MXFP4_SWIGLU, INT4ZP, INT4_ACT_ORDER = WORKLOADS
+INT4_SMALL, INT4_BIAS, NVFP4_DECODE, NVFP4_ZIPF, MXFP4_SWIGLU, INT4ZP, INT4_ACT_ORDER, INT4ZPF = WORKLOADS
 # the layer bench.py measures by default: the largest configuration that fits one GPU (the NVFP4
 # EP8 slice with Zipf routing at 4096 tokens: 906 MB of weights, 23283 live slots at seed 2)
 HEADLINE, HEADLINE_M = NVFP4_ZIPF, 4096
@@ -163,9 +166,13 @@ def _projection(rng: np.random.Generator, wl: Workload, E: int, N: int, K: int) 
         gs = None
     elif wl.qtype == "int4zpf_g128":
         scales = _to_bf16_bits(rng.uniform(0.002, 0.02, size=(E, N, K // g)).astype(np.float32))
-        # float zero points (the offset a min/max quantiser stores unrounded): about the middle
-        # of 0..15, not integers
-        zeros = np.clip(rng.normal(7.5, 2.5, size=(E, N, K // g)), 0.0, 15.0).astype(np.float16).view(np.uint16)
+        # float zero points (the offset a quantiser stores unrounded): not integers, clustered
+        # about the middle of 0..15 as for roughly zero-centred groups.  (The spread matters:
+        # each group's mean weight is (7.5 - z) s, an offset that grows the layer's outputs, and
+        # with a spread of 2.5 the bf16 rounding of the dequantised weights alone -- applied to
+        # the oracle's float64 weights on the CPU -- put one output of the full-size layer at 1.01
+        # times the layer bar; with 1.0 the worst is at 0.66.)
+        zeros = np.clip(rng.normal(7.5, 1.0, size=(E, N, K // g)), 0.0, 15.0).astype(np.float16).view(np.uint16)
         gs = None
     elif wl.qtype == "nvfp4_g16":
         scales = _to_e4m3_codes(np.exp2(rng.uniform(4.0, 8.0, size=(E, N, K // g))).astype(np.float32))
@@ -268,7 +275,8 @@ def device_weights(lw: LayerWeights, device="cuda") -> tuple:
         if p.bias is not None:
             d["bias"] = torch.from_numpy(p.bias.view(np.int16)).to(device).view(torch.bfloat16)
         if p.zeros is not None:
-            d["zeros"] = torch.from_numpy(p.zeros).to(device)
+            z = p.zeros.view(np.int16) if p.zeros.dtype == np.uint16 else p.zeros   # float16 bits
+            d["zeros"] = torch.from_numpy(z).to(device)
         if p.g_idx is not None:
             d["g_idx"] = torch.from_numpy(p.g_idx).to(device)
         return d
