@@ -236,19 +236,47 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
       const uint8_t* sb = st + XB + WB + (w * NG + g) * 64 + (lane & 15) * SROW;
       sc[g].raw = SROW == 4 ? *reinterpret_cast<const uint32_t*>(sb) : *reinterpret_cast<const uint16_t*>(sb);
     }
+    if constexpr (PARTIAL || MG < NG) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      u32x4_t af[NG];
+      for (int i = 0; i < 2; ++i) {
+        u32x4_t af[NG];
 #pragma unroll
-      for (int g = 0; g < NG; ++g) af[g] = dequant8<QT>(wq[g][i], sc[g].s(i, lane), sc[g].m(i, lane));
+        for (int g = 0; g < NG; ++g) af[g] = dequant8<QT>(wq[g][i], sc[g].s(i, lane), sc[g].m(i, lane));
+#pragma unroll
+        for (int h = 0; h < MG; ++h) {
+          if constexpr (PARTIAL) {
+            if (h >= lg) break;
+          }
+          const u32x4_t bf = xs[(i * MG + h) * 64 + lane];
+#pragma unroll
+          for (int g = 0; g < NG; ++g) acc[g][h] = mfma(af[g], bf, acc[g][h]);
+        }
+      }
+    } else {
+      // full block: the second substep's dequantisation is computed tile by tile between the
+      // first substep's MFMA groups (scheduling barriers keep each chunk in place; left to itself
+      // the compiler issues all of it after the MFMA run), so one wave keeps VALU and matrix core
+      // busy together; the activation fragment of the next group is read one chunk ahead.
+      // Measured: NVFP4 Zipf M=4096 gate/up GEMM 1436 -> 1398 us, M=1024 layer 736 -> 709 us.
+      u32x4_t a0[NG], a1[NG];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) a0[g] = dequant8<QT>(wq[g][0], sc[g].s(0, lane), sc[g].m(0, lane));
+      u32x4_t bf = xs[lane];
 #pragma unroll
       for (int h = 0; h < MG; ++h) {
-        if constexpr (PARTIAL) {
-          if (h >= lg) break;
-        }
-        const u32x4_t bf = xs[(i * MG + h) * 64 + lane];
+        const u32x4_t bn = xs[(h + 1) * 64 + lane];   // (h + 1 = MG: the first of substep 1)
 #pragma unroll
-        for (int g = 0; g < NG; ++g) acc[g][h] = mfma(af[g], bf, acc[g][h]);
+        for (int g = 0; g < NG; ++g) acc[g][h] = mfma(a0[g], bf, acc[g][h]);
+        if (h < NG) a1[h] = dequant8<QT>(wq[h][1], sc[h].s(1, lane), sc[h].m(1, lane));
+        bf = bn;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int h = 0; h < MG; ++h) {
+        const u32x4_t bn = h + 1 < MG ? xs[(MG + h + 1) * 64 + lane] : bf;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) acc[g][h] = mfma(a1[g], bf, acc[g][h]);
+        bf = bn;
       }
     }
   };
