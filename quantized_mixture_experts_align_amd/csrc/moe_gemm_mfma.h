@@ -194,8 +194,13 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
     uint8_t* st = stage_ptr(stage);
     if (xwave) {
 #pragma unroll
-      for (int l = 0; l < XL; ++l)
+      for (int l = 0; l < XL; ++l) {
+        // an all-padding 16-slot group's activations are never read (its MFMAs are skipped):
+        // not loaded.  (Safe only with two stages, whose waits are vmcnt(0): the per-step load
+        // count of the wave may then differ from the compile-time one.)
+        if (kStages == 2 && MG > 1 && ((4 * l + w) % MG) >= lg) continue;
         dma_to_lds<16>(xbase + kt * (kTileK * 2), xoff[l], st + (l * 256 + w * 64) * 16);
+      }
     }
 #pragma unroll
     for (int p = 0; p < NWD; ++p) {
