@@ -1,7 +1,7 @@
 """Full-size parity with deterministic coverage, in the launch configuration bench.py times.
 
-For the large workloads (NVFP4 slice with Zipf routing at 256 / 1024 / 4096 tokens, the NVFP4
-decode slice at 64, MXFP4 GPT-OSS at 2048):
+For the large workloads (NVFP4 slice with Zipf routing at 256 / 1024 / 4096 tokens and with
+uniform routing at 23296, the NVFP4 decode slice at 64, MXFP4 GPT-OSS at 2048):
 
 * GEMM level: every slot routed to the hottest, a middle and the last non-empty local expert
   is compared element by element with the float64 oracle -- the gate/up GEMM with its fused
@@ -25,7 +25,7 @@ from gpu_util import announce, gemm_tolerance, layer_violations, make_layer, ora
 pytestmark = pytest.mark.gpu
 
 CELLS = [(W.NVFP4_ZIPF, 256), (W.NVFP4_ZIPF, 1024), (W.NVFP4_ZIPF, 4096), (W.NVFP4_DECODE, 64),
-         (W.MXFP4_SWIGLU, 2048)]
+         (W.MXFP4_SWIGLU, 2048), (W.NVFP4_UNIFORM, 23296)]
 
 _CACHE = {}
 

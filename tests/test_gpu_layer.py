@@ -172,7 +172,8 @@ def _sample(M, n, seed=0):
                                              (W.MXFP4_SWIGLU, 1, 1), (W.MXFP4_SWIGLU, 32, 4),
                                              (W.MXFP4_SWIGLU, 2048, 4), (W.INT4ZP, 1, 1), (W.INT4ZP, 2304, 2304),
                                              (W.INT4_ACT_ORDER, 1, 1), (W.INT4_ACT_ORDER, 2304, 2304),
-                                             (W.INT4ZPF, 1, 1), (W.INT4ZPF, 2304, 2304)])
+                                             (W.INT4ZPF, 1, 1), (W.INT4ZPF, 2304, 2304),
+                                             (W.NVFP4_UNIFORM, 5760, 3), (W.NVFP4_UNIFORM, 23296, 3)])
 def test_workload_layer_matches_oracle(name, M, n_sample):
     wl, lw, layer = _workload_layer(name)
     inp = W.make_inputs(wl, M)

@@ -101,8 +101,14 @@ WORKLOADS = {w.name: w for w in [
              (1, 2304), bias=True, act_order=True, seed=6),
     Workload("int4zpf_bias_e8_top2_h512_i1024", "int4zpf_g128", 8, 0, 8, 2, 512, 1024,
              (1, 2304), bias=True, seed=7),
+    # the Zipf batches' counterpart without skew: the same slice and weights, uniform routing, and
+    # M chosen so that the live slots about match those of Zipf M = 1024 and 4096 (5800 against
+    # 5760 and 23280 against 23283 at seed 2)
+    Workload("nvfp4_ep8_slice_uniform_prefill_h4096_i4096", "nvfp4_g16", 256, 0, 32, 8, 4096, 4096,
+             (5760, 23296), norm=True, seed=2),
 ]}
-INT4_SMALL, INT4_BIAS, NVFP4_DECODE, NVFP4_ZIPF, MXFP4_SWIGLU, INT4ZP, INT4_ACT_ORDER, INT4ZPF = WORKLOADS
+(INT4_SMALL, INT4_BIAS, NVFP4_DECODE, NVFP4_ZIPF, MXFP4_SWIGLU, INT4ZP, INT4_ACT_ORDER, INT4ZPF,
+ NVFP4_UNIFORM) = WORKLOADS
 # the layer bench.py measures by default: the largest configuration that fits one GPU (the NVFP4
 # EP8 slice with Zipf routing at 4096 tokens: 906 MB of weights, 23283 live slots at seed 2)
 HEADLINE, HEADLINE_M = NVFP4_ZIPF, 4096
