@@ -9,11 +9,10 @@
 //   * each stage holds the step's activations (in B-operand order: contiguous ds_read_b128
 //     per lane), the wave's NG weight tiles (512 B each, ds_read_b64 per lane) and their group
 //     scales, all written by global_load_lds (direct global -> LDS, no register staging);
-//   * step kt + kStages - 1 is issued while step kt computes; rows of padding slots read row 0
+//   * step kt + kStages - 1 is issued when step kt starts; rows of padding slots read row 0
 //     of A (those MFMA columns are never stored);
-//   * one barrier per step: each wave waits (s_waitcnt vmcnt) until only the later steps' loads
-//     are pending -- every load is one instruction, so the count is exact -- then all waves
-//     meet at s_barrier.  __syncthreads() would wait for every prefetch in flight.
+//   * one barrier per step: at its end each wave waits for its loads (s_waitcnt vmcnt(0)), then
+//     all waves meet at s_barrier.
 // With ACT (fused gate/up epilogue) the wave's NG tiles are NG/2 gate tiles and the matching up
 // tiles I/16 tiles further down, so each lane holds gate and up of the same (slot, column).
 #pragma once
@@ -36,26 +35,15 @@ __device__ __forceinline__ void wait_vm() {
 // four, because the smaller LDS footprint lets more workgroups share a CU and hide each other's
 // load latency (a workgroup runs only K/64 steps, 8 for K = 512), which deeper per-workgroup
 // prefetch does not.
-template <int MG>
-constexpr int stages_for() { return 2; }
-
-// Wait until this wave's loads of the current step have landed, given how many later steps'
-// loads (LPER instructions each) it has already issued.
-template <int LPER, int ST>
-__device__ __forceinline__ void wait_step(int later) {
-  if constexpr (ST >= 4) {
-    if (later >= 2) { wait_vm<2 * LPER>(); return; }
-  }
-  if (later >= 1) { wait_vm<LPER>(); return; }
-  wait_vm<0>();
-}
+constexpr int kStages = 2;
 
 // All waves meet.  The wave's own LDS reads of the previous step are waited for first
 // (lgkmcnt(0)), so the global->LDS loads issued right after the barrier into that step's stage
 // can never overtake them, whatever the compiler schedules before the barrier.
 __device__ __forceinline__ void block_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Direct global -> LDS load of BYTES (4 or 16) per lane: lane l's data lands at lds + l*BYTES.
+// Direct global -> LDS load of BYTES (4 or 16) per lane: lane l's data lands at LDS address
+// lds + l*BYTES.
 // The address is a wave-uniform 64-bit base in scalar registers + the lane's 32-bit byte offset,
 // so a step's address update is scalar work and the per-lane offsets never change.  (No
 // instruction offset: for these loads it would move the LDS destination too.)
@@ -64,9 +52,8 @@ __device__ __forceinline__ void block_barrier() { asm volatile("s_waitcnt lgkmcn
 // for these loads are the explicit wait_vm<> calls.  (m0 holds the LDS address; one wait state
 // is required between writing m0 and the load.)
 template <int BYTES>
-__device__ __forceinline__ void dma_to_lds(const uint8_t* sbase, uint32_t voff, void* lds) {
-  const uint32_t off = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(off);
+__device__ __forceinline__ void dma_to_lds(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
   if constexpr (BYTES == 16)
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                  ::"s"(m0), "v"(voff), "s"(sbase) : "memory", "m0");
@@ -104,11 +91,12 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
   constexpr int SB = 4 * NG * 64;                          //   scales (64-B slot per tile)
   constexpr int STAGE = XB + WB + SB;
   constexpr int NWD = (NG + 1) / 2;                        // weight loads per wave and step
-  constexpr int LW = NWD + 1;                              // weight + scale loads per wave and step
-  constexpr int kStages = stages_for<MG>();
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * STAGE];
   __shared__ int s_crow[BM];
   auto stage_ptr = [&](int stage) -> uint8_t* { return smem + stage * STAGE; };
+  // the LDS address of smem as a 32-bit integer, so that the DMA destinations are plain scalar
+  // sums (a generic pointer converted per load costs a null test and two registers per address)
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
 
   const int NT = a.N / kTileN, KT = a.K / kTileK;
   const int NTA = act_paired<ACT>() ? NT / 2 : NT;          // tiles to assign (gate tiles if fused)
@@ -191,24 +179,23 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
     if (sg == g) sdist = (uint32_t)(sbase[g] - sbase[0]);
   const uint32_t soffl = sdist + (uint32_t)sr * 4;
   auto issue = [&](int kt, int stage) {
-    uint8_t* st = stage_ptr(stage);
+    const uint32_t st = smem_lds + (uint32_t)(stage * STAGE);
     if (xwave) {
 #pragma unroll
       for (int l = 0; l < XL; ++l) {
         // an all-padding 16-slot group's activations are never read (its MFMAs are skipped):
-        // not loaded.  (Safe only with two stages, whose waits are vmcnt(0): the per-step load
-        // count of the wave may then differ from the compile-time one.)
-        if (kStages == 2 && MG > 1 && ((4 * l + w) % MG) >= lg) continue;
-        dma_to_lds<16>(xbase + kt * (kTileK * 2), xoff[l], st + (l * 256 + w * 64) * 16);
+        // not loaded.  (Every wait is vmcnt(0), so the wave's load count may vary.)
+        if (MG > 1 && ((4 * l + w) % MG) >= lg) continue;
+        dma_to_lds<16>(xbase + kt * (kTileK * 2), xoff[l], st + (uint32_t)(l * 256 + w * 64) * 16);
       }
     }
 #pragma unroll
     for (int p = 0; p < NWD; ++p) {
-      uint8_t* wt = st + XB + (w * NG + 2 * p) * kTileBytes;
+      const uint32_t wt = st + (uint32_t)(XB + (w * NG + 2 * p) * kTileBytes);
       if (NG > 1 || lane < 32) dma_to_lds<16>(wbase[2 * p] + (int64_t)kt * kTileBytes, woff[p], wt);
     }
     const int64_t soff = (int64_t)(pair_grouped(QT) ? kt >> 1 : kt) * scale_step_bytes(QT);
-    if (s_act) dma_to_lds<4>(sbase[0] + soff, soffl, st + XB + WB + (w * NG) * 64);
+    if (s_act) dma_to_lds<4>(sbase[0] + soff, soffl, st + (uint32_t)(XB + WB + (w * NG) * 64));
   };
 
   f32x4_t acc[NG][MG];
@@ -217,30 +204,34 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
 #pragma unroll
     for (int h = 0; h < MG; ++h) acc[g][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < KT) issue(s, s);
-
-  // one K step: wait for its operands, prefetch a later step, dequantise and multiply.  With
-  // PARTIAL (an expert's last block), the 16-slot groups from lg on are all padding and their
-  // MFMAs are skipped; full blocks run the loop without those branches.
-  auto step = [&](auto partial, int kt, int u) {
-    constexpr bool PARTIAL = decltype(partial)::value;
-    // this wave's loads of step kt have landed once only later steps' loads are pending
-    const int later = min(kStages - 2, KT - 1 - kt);
-    if (xwave) wait_step<XL + LW, kStages>(later); else wait_step<LW, kStages>(later);
-    block_barrier();  // everyone's step kt is in LDS, and everyone is done with step kt-1
-    if (kt + kStages - 1 < KT) issue(kt + kStages - 1, (u + kStages - 1) % kStages);
-    const uint8_t* st = stage_ptr(u);
-    const u32x4_t* xs = reinterpret_cast<const u32x4_t*>(st);
-    u32x2_t wq[NG];
-    TileScale<QT> sc[NG];
+  // this wave's codes and group scales of one step, from its stage
+  auto read_tiles = [&](const uint8_t* st, u32x2_t* wq, TileScale<QT>* sc) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       wq[g] = reinterpret_cast<const u32x2_t*>(st + XB + (w * NG + g) * kTileBytes)[lane];
       const uint8_t* sb = st + XB + WB + (w * NG + g) * 64 + (lane & 15) * SROW;
       sc[g].raw = SROW == 4 ? *reinterpret_cast<const uint32_t*>(sb) : *reinterpret_cast<const uint16_t*>(sb);
     }
+  };
+
+  // Every wait is vmcnt(0) at the end of a step (or of the prologue), followed by the barrier:
+  // the loads issued at the start of step kt (step kt + kStages - 1) have then landed for every
+  // wave, and every wave is done with step kt's stage, which the next step's loads overwrite.
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < KT) issue(s, s);
+  wait_vm<0>();
+  block_barrier();
+
+  // One step's dequantisation and MFMAs.  With PARTIAL (an expert's last block), the 16-slot
+  // groups from lg on are all padding and their MFMAs are skipped; full blocks run without those
+  // branches.
+  auto compute = [&](auto partial, const uint8_t* st) {
+    constexpr bool PARTIAL = decltype(partial)::value;
+    const u32x4_t* xs = reinterpret_cast<const u32x4_t*>(st);
+    u32x2_t wq[NG];
+    TileScale<QT> sc[NG];
+    read_tiles(st, wq, sc);
     if constexpr (PARTIAL || MG < NG) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -284,6 +275,13 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
         bf = bn;
       }
     }
+  };
+
+  auto step = [&](auto partial, int kt, int u) {
+    if (kt + kStages - 1 < KT) issue(kt + kStages - 1, (u + kStages - 1) % kStages);
+    compute(partial, stage_ptr(u));
+    wait_vm<0>();
+    block_barrier();
   };
   // whole rounds of kStages steps (stage index = compile-time constant), then the remaining steps;
   // no early exit inside the unrolled round, which would make the accumulators change registers
