@@ -7,19 +7,26 @@
 // assignments are dropped, and the order inside an expert is ascending slot id, so the result
 // is unique and reproducible.
 //
-// One workgroup of 16 waves; wave w owns a contiguous chunk of slots, a multiple of 64 long.
-//   1. count:   LDS histogram cnt[w][e] (atomics only add; the totals do not depend on order)
+// One or more workgroups of 16 waves; workgroup g owns the slots [g*span, (g+1)*span) and
+// wave w of it a contiguous chunk of those, a multiple of 64 long.
+//   0. totals:  with several workgroups, each one counts the whole batch per expert -- the slots
+//               before its span, then the rest, each wave into its own LDS row, rows summed --
+//               (one read of every id from L2 per workgroup: no workspace and no communication
+//               between workgroups, and every workgroup derives the same segment starts)
+//   1. count:   LDS histogram cnt[w][e] of the span (atomics only add; the totals do not depend
+//               on order)
 //   2. scan:    per expert, exclusive scan over the waves (a 16-lane segmented shuffle scan per
-//               expert) -> offset of wave w inside the expert's segment and the expert's total;
+//               expert) -> offset of wave w inside the span's part of the expert's segment;
 //               padded totals scanned over experts -> segment starts (up to 64 experts: wave 0
 //               alone does both, one lane per expert, behind a single barrier)
 //   3. scatter: each wave walks its chunk in order, 64 slots at a time; the rank of a lane among
 //               the lanes of its batch with the same expert comes from ballots over the bits of
 //               the expert id (a wave multi-split), so the write position is
-//               seg[e] + off[w][e] + rank, strictly in slot order.  A chunk of up to
+//               seg[e] + before[e] + off[w][e] + rank, strictly in slot order.  A chunk of up to
 //               64 * kAlignUnroll slots keeps its ids in registers from step 1 (one read of ids)
 //   4. fill:    padding entries (in parallel over expert x position) and the tail get the
-//               sentinel, block -> expert by binary search over the segment starts
+//               sentinel, block -> expert by binary search over the segment starts; these index
+//               ranges are split over the workgroups
 #include "moe_internal.h"
 
 namespace moe {
@@ -28,31 +35,96 @@ constexpr int kAlignWaves = 16;
 constexpr int kAlignThreads = kAlignWaves * 64;
 constexpr int kAlignMaxLocal = 512;
 constexpr int kAlignUnroll = 8;
+// Batches of more slots than this are split over workgroups of kAlignSpan slots each.  Measured
+// (kernel trace, NVFP4 EP8 slice): 32768 slots 30.6 -> 9.6 us, 8192 slots 9.0 -> 6.7 us (32
+// experts) and 14.4 -> 9.3 us (128 experts), 186368 slots 25.5 us.
+constexpr int kAlignSingleMax = 4096;
+constexpr int kAlignSpan = 2048;
 
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int32_t* __restrict__ ids, int32_t numel, int32_t start, int32_t n_local, int32_t B,
-    int32_t cap, int32_t cap_blocks, int32_t* __restrict__ sorted, int32_t* __restrict__ eids,
-    int32_t* __restrict__ ntpp, int32_t* __restrict__ slot_local) {
+    int32_t cap, int32_t cap_blocks, int32_t span, int32_t* __restrict__ sorted,
+    int32_t* __restrict__ eids, int32_t* __restrict__ ntpp, int32_t* __restrict__ slot_local) {
   __shared__ int32_t cnt[kAlignWaves * kAlignMaxLocal];  // per wave and expert
   __shared__ int32_t seg[kAlignMaxLocal + 1];            // segment start of each expert
-  __shared__ int32_t tot[kAlignMaxLocal];                // live slots of each expert
+  __shared__ int32_t tot[kAlignMaxLocal];                // live slots of each expert (whole batch)
+  __shared__ int32_t bef[kAlignMaxLocal];                // live slots of each expert before the span
   __shared__ int32_t wave_sum[kAlignWaves];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  // every wave owns a chunk (the scatter is serial per 64-slot batch within a wave, so short
-  // chunks are faster even when most waves are idle)
-  const int nwv = kAlignWaves;
-  // each wave zeroes and then counts into its own row only: a wave barrier suffices here
-  for (int i = lane; i < n_local; i += 64) cnt[w * n_local + i] = 0;
+  const int G = (int)gridDim.x, g = (int)blockIdx.x;
+  const int s0 = (int)min((int64_t)numel, (int64_t)g * span), s1 = (int)min((int64_t)numel, (int64_t)s0 + span);
+  auto local_of = [&](int id) { return (id >= start && id - start < n_local) ? id - start : -1; };
+
+  int nbits = 0;
+  while ((1 << nbits) < n_local) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // lanes of a 64-slot batch with the same local expert as this lane (live lanes only): ballots
+  // over the bits of the expert id (a wave multi-split)
+  auto same_expert = [&](int le) {
+    const bool live = le >= 0;
+    uint64_t same = __ballot(live);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = live && ((le >> b) & 1);
+      const uint64_t m = __ballot(bit);
+      same &= bit ? m : ~m;
+    }
+    return same;
+  };
+
+  int32_t* my_cnt = cnt + w * n_local;
+  // per-wave counts of the slots [i0, i1) into the wave's own row (per-lane LDS atomics: lanes of
+  // one wave only ever meet on a counter), four 64-slot batches' ids in flight
+  auto count_rows = [&](int i0, int i1) {
+    for (int i = lane; i < n_local; i += 64) my_cnt[i] = 0;
+    __builtin_amdgcn_wave_barrier();
+    constexpr int kU = 4;
+    for (int base = i0 + w * 64; base < i1; base += kU * kAlignThreads) {
+      int idq[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = base + u * kAlignThreads + lane;
+        idq[u] = i < i1 ? ids[i] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int le = local_of(idq[u]);
+        if (le >= 0) atomicAdd(&my_cnt[le], 1);
+      }
+    }
+    __syncthreads();
+  };
+  if (G > 1) {
+    // the slots before the span, then the rest of the batch; the rows summed per expert
+    count_rows(0, s0);
+    for (int e = tid; e < n_local; e += kAlignThreads) {
+      int t = 0;
+      for (int v = 0; v < kAlignWaves; ++v) t += cnt[v * n_local + e];
+      bef[e] = t;
+    }
+    __syncthreads();
+    count_rows(s0, numel);
+    for (int e = tid; e < n_local; e += kAlignThreads) {
+      int t = bef[e];
+      for (int v = 0; v < kAlignWaves; ++v) t += cnt[v * n_local + e];
+      tot[e] = t;
+    }
+    __syncthreads();
+  } else {
+    for (int e = tid; e < n_local; e += kAlignThreads) bef[e] = 0;
+  }
+  // each wave zeroes and then counts into its own row only: a wave barrier suffices there
+  for (int i = lane; i < n_local; i += 64) my_cnt[i] = 0;
   __builtin_amdgcn_wave_barrier();
 
-  // chunk of wave w: [c0, c1), a multiple of 64 slots long (empty for waves >= nwv)
-  const int per = ((numel + nwv - 1) / nwv + 63) & ~63;
-  const int c0 = w < nwv ? min(numel, w * per) : numel, c1 = w < nwv ? min(numel, c0 + per) : numel;
+  // every wave owns a chunk of the span (the scatter is serial per 64-slot batch within a wave,
+  // so short chunks are faster even when most waves are idle)
+  const int nwv = kAlignWaves;
+  const int len = s1 - s0;
+  const int per = ((len + nwv - 1) / nwv + 63) & ~63;
+  const int c0 = min(s1, s0 + w * per), c1 = min(s1, c0 + per);
   const bool keep = per <= 64 * kAlignUnroll;  // the chunk's ids stay in registers
-  int32_t* my_cnt = cnt + w * n_local;
 
-  auto local_of = [&](int id) { return (id >= start && id - start < n_local) ? id - start : -1; };
   // (ids are read kAlignUnroll batches at a time so their load latencies overlap)
   int idv[kAlignUnroll];
   for (int base = c0; base < c1; base += 64 * kAlignUnroll) {
@@ -88,6 +160,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
           cnt[v * n_local + lane] = t;
           t += c[v];
         }
+        if (G > 1) t = tot[lane];
       }
       const int p = lane < n_local ? (t + B - 1) / B * B : 0;
       int incl = p;
@@ -116,7 +189,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
       }
       if (e < n_local) {
         if (v < nwv) cnt[v * n_local + e] = x - c;
-        if (v == 15) tot[e] = x;
+        if (v == 15 && G == 1) tot[e] = x;
       }
     }
     __syncthreads();
@@ -141,9 +214,6 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   }
 
   // scatter in slot order
-  int nbits = 0;
-  while ((1 << nbits) < n_local) ++nbits;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int base = c0; base < c1; base += 64 * kAlignUnroll) {
     if (!keep) {
 #pragma unroll
@@ -157,31 +227,27 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
       const int i = base + 64 * u + lane;
       if (base + 64 * u >= c1) break;  // uniform: the wave's chunk has ended
       const int le = i < c1 ? local_of(idv[u]) : -1;
-      const bool live = le >= 0;
-      uint64_t same = __ballot(live);
-      for (int b = 0; b < nbits; ++b) {
-        const bool bit = live && ((le >> b) & 1);
-        const uint64_t m = __ballot(bit);
-        same &= bit ? m : ~m;
-      }
-      if (live) {
+      const uint64_t same = same_expert(le);
+      if (le >= 0) {
         const int rank = __popcll(same & lt_mask);
         const int before = my_cnt[le];
-        sorted[seg[le] + before + rank] = i;
+        sorted[seg[le] + bef[le] + before + rank] = i;
         if ((same >> lane) == 1ull) my_cnt[le] = before + __popcll(same);  // last lane of the group
       }
       __builtin_amdgcn_wave_barrier();
     }
   }
 
-  // padding of each expert's last block (expert x position in parallel), then the tail
-  for (int i = tid; i < n_local * B; i += kAlignThreads) {
+  // padding of each expert's last block (expert x position in parallel), then the tail; each
+  // index range split over the workgroups
+  const int gt = g * kAlignThreads + tid, gstride = G * kAlignThreads;
+  for (int i = gt; i < n_local * B; i += gstride) {
     const int e = i / B, p = seg[e] + tot[e] + (i - e * B);
     if (p < seg[e + 1]) sorted[p] = numel;
   }
   const int total = seg[n_local];
-  for (int p = total + tid; p < cap; p += kAlignThreads) sorted[p] = numel;
-  for (int b = tid; b < cap_blocks; b += kAlignThreads) {
+  for (int p = total + gt; p < cap; p += gstride) sorted[p] = numel;
+  for (int b = gt; b < cap_blocks; b += gstride) {
     int e = -1;
     if (b * B < total) {
       int lo = 0, hi = n_local;  // first index with seg[idx] > b*B, minus one
@@ -194,7 +260,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     }
     eids[b] = e;
   }
-  if (tid == 0) *ntpp = total;
+  if (gt == 0) *ntpp = total;
 }
 
 }  // namespace moe
@@ -220,8 +286,11 @@ extern "C" int moe_align(const int32_t* topk_ids, int64_t M, int32_t top_k, int3
   MOE_REQUIRE(num_tokens_post_padded && ((sorted_token_ids && expert_ids) || cap == 0), MOE_EINVAL,
               "moe_align: null output pointer");
   MOE_REQUIRE(topk_ids || M == 0, MOE_EINVAL, "moe_align: null topk_ids");
-  hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, stream, topk_ids, (int32_t)(M * top_k),
-                     expert_start, n_local, block_m, (int32_t)cap, (int32_t)cap_blocks, sorted_token_ids,
+  const int64_t numel = M * top_k;
+  const int32_t span = numel <= kAlignSingleMax ? (int32_t)std::max<int64_t>(numel, 1) : kAlignSpan;
+  const unsigned grid = (unsigned)std::max<int64_t>(1, (numel + span - 1) / span);
+  hipLaunchKernelGGL(align_kernel, dim3(grid), dim3(kAlignThreads), 0, stream, topk_ids, (int32_t)numel,
+                     expert_start, n_local, block_m, (int32_t)cap, (int32_t)cap_blocks, span, sorted_token_ids,
                      expert_ids, num_tokens_post_padded, slot_local_ids);
   return check_launch("moe_align");
 }

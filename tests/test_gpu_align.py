@@ -77,3 +77,20 @@ def test_align_deterministic_and_optional_slot_ids():
     a = _run(inp.topk_ids, 0, 32, 128)
     b = _run(inp.topk_ids, 0, 32, 128, slot_ids=False)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2] and b[3] is None
+
+
+@pytest.mark.parametrize("M,k,n_local,B,seed", [
+    (4097, 1, 33, 16, 1),      # just above one workgroup's batch: spans of 2048, 2048 and 1
+    (2049, 4, 64, 7, 2),       # five spans, the wave-0 scan (64 experts), an odd block size
+    (1025, 8, 65, 128, 3),     # the segmented scan (65 experts)
+    (20000, 8, 512, 1, 4),     # 79 spans, the largest expert count, block size 1
+    (30000, 6, 300, 256, 5),   # 88 spans, the largest block size
+])
+def test_align_several_workgroups(M, k, n_local, B, seed):
+    # batches above 4096 slots are split over workgroups that each count the whole batch: the
+    # result must be the single sorted order, with skewed routing (a few hot experts) and junk ids
+    rng = np.random.default_rng(seed)
+    start = int(rng.integers(0, 40))
+    p = (np.arange(n_local + 60) + 1.0) ** -1.1
+    ids = (rng.choice(n_local + 60, size=(M, k), p=p / p.sum()) + start - 10).astype(np.int32)
+    _check(ids, start, n_local, B)
