@@ -11,8 +11,9 @@
 //     scales, all written by global_load_lds (direct global -> LDS, no register staging);
 //   * step kt + kStages - 1 is issued when step kt starts; rows of padding slots read row 0
 //     of A (those MFMA columns are never stored);
-//   * one barrier per step: at its end each wave waits for its loads (s_waitcnt vmcnt(0)), then
-//     all waves meet at s_barrier.
+//   * one barrier per step: at its end each wave waits until its loads of the next step have
+//     landed (s_waitcnt vmcnt(n), n = its loads of the steps after that: every load is one
+//     instruction, so the count is exact), then all waves meet at s_barrier.
 // With ACT (fused gate/up epilogue) the wave's NG tiles are NG/2 gate tiles and the matching up
 // tiles I/16 tiles further down, so each lane holds gate and up of the same (slot, column).
 #pragma once
@@ -31,11 +32,39 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Pipeline depth.  Measured on all prefill shapes: two stages (double buffering) beat three and
-// four, because the smaller LDS footprint lets more workgroups share a CU and hide each other's
-// load latency (a workgroup runs only K/64 steps, 8 for K = 512), which deeper per-workgroup
-// prefetch does not.
-constexpr int kStages = 2;
+// Pipeline depth.  Two stages (double buffering) for blocks of 32 slots and more: measured on
+// the prefill shapes, three or four are slower (NVFP4 Zipf M=4096 gate/up 1323 -> 1351 us, MXFP4
+// M=2048 343 -> 356 us, int4 M=2304 21.2 -> 23.3 us): the smaller LDS footprint lets more
+// workgroups share a CU, and those kernels are not limited by the weight stream's latency.
+// Three for 16-slot blocks (the decode MFMA configuration), whose few workgroups per CU stream
+// weights with little arithmetic in between, so that the bytes in flight set the rate: NVFP4
+// slice M=64 layer 170 -> 162 us cold, its down GEMM 50.1 -> 47.6 us (four stages no better).
+template <int MG>
+constexpr int stages_for() { return MG == 1 ? 3 : 2; }
+
+// Wait until at most n (0..15) of this wave's vector-memory loads are outstanding: s_waitcnt takes
+// its count as an immediate, so a wave-uniform run-time count goes through a switch.
+__device__ __forceinline__ void wait_vm_upto(int n) {
+  switch (n) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<1>(); break;
+    case 2: wait_vm<2>(); break;
+    case 3: wait_vm<3>(); break;
+    case 4: wait_vm<4>(); break;
+    case 5: wait_vm<5>(); break;
+    case 6: wait_vm<6>(); break;
+    case 7: wait_vm<7>(); break;
+    case 8: wait_vm<8>(); break;
+    case 9: wait_vm<9>(); break;
+    case 10: wait_vm<10>(); break;
+    case 11: wait_vm<11>(); break;
+    case 12: wait_vm<12>(); break;
+    case 13: wait_vm<13>(); break;
+    case 14: wait_vm<14>(); break;
+    case 15: wait_vm<15>(); break;
+    default: wait_vm<0>(); break;
+  }
+}
 
 // All waves meet.  The wave's own LDS reads of the previous step are waited for first
 // (lgkmcnt(0)), so the global->LDS loads issued right after the barrier into that step's stage
@@ -89,6 +118,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
   constexpr int XB = FRAGS * 16;                           // stage layout: activations,
   constexpr int WB = 4 * NG * kTileBytes;                  //   weight tiles of the 4 waves,
   constexpr int SB = 4 * NG * 64;                          //   scales (64-B slot per tile)
+  constexpr int kStages = stages_for<MG>();
   constexpr int STAGE = XB + WB + SB;
   constexpr int NWD = (NG + 1) / 2;                        // weight loads per wave and step
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * STAGE];
@@ -184,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
 #pragma unroll
       for (int l = 0; l < XL; ++l) {
         // an all-padding 16-slot group's activations are never read (its MFMAs are skipped):
-        // not loaded.  (Every wait is vmcnt(0), so the wave's load count may vary.)
+        // not loaded (nload counts what is)
         if (MG > 1 && ((4 * l + w) % MG) >= lg) continue;
         dma_to_lds<16>(xbase + kt * (kTileK * 2), xoff[l], st + (uint32_t)(l * 256 + w * 64) * 16);
       }
@@ -214,14 +244,32 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
     }
   };
 
-  // Every wait is vmcnt(0) at the end of a step (or of the prologue), followed by the barrier:
-  // the loads issued at the start of step kt (step kt + kStages - 1) have then landed for every
-  // wave, and every wave is done with step kt's stage, which the next step's loads overwrite.
+  // This wave's loads per step (each load is one instruction whatever its lane mask, and every
+  // one of them is issued with lane 0 active): its activation fragments of the live 16-slot
+  // groups, its weight loads and its scale load.
+  int nload = NWD + 1;
+  if (xwave) {
+#pragma unroll
+    for (int l = 0; l < XL; ++l)
+      if (!(MG > 1 && ((4 * l + w) % MG) >= lg)) ++nload;
+  }
+  // At the end of step kt (or of the prologue, "step -1") each wave waits until its loads of step
+  // kt + 1 have landed -- only those of the steps after it may still be in flight -- and all waves
+  // meet at the barrier: step kt + 1's operands are then in LDS for everyone, and everyone is done
+  // with step kt's stage, which the loads issued at the start of step kt + 1 overwrite.
+  auto wait_next = [&](int kt) {
+    if constexpr (kStages == 2) {
+      wait_vm<0>();  // (no later step's loads have been issued yet)
+    } else {
+      const int later = max(0, min(kt + kStages - 1, KT - 1) - (kt + 1));
+      wait_vm_upto(later * nload);
+    }
+    block_barrier();
+  };
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s)
     if (s < KT) issue(s, s);
-  wait_vm<0>();
-  block_barrier();
+  wait_next(-1);
 
   // One step's dequantisation and MFMAs.  With PARTIAL (an expert's last block), the 16-slot
   // groups from lg on are all padding and their MFMAs are skipped; full blocks run without those
@@ -280,8 +328,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
   auto step = [&](auto partial, int kt, int u) {
     if (kt + kStages - 1 < KT) issue(kt + kStages - 1, (u + kStages - 1) % kStages);
     compute(partial, stage_ptr(u));
-    wait_vm<0>();
-    block_barrier();
+    wait_next(kt);
   };
   // whole rounds of kStages steps (stage index = compile-time constant), then the remaining steps;
   // no early exit inside the unrolled round, which would make the accumulators change registers
