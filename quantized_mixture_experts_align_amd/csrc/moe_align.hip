@@ -40,6 +40,9 @@ constexpr int kAlignUnroll = 8;
 // experts) and 14.4 -> 9.3 us (128 experts), 186368 slots 25.5 us.
 constexpr int kAlignSingleMax = 4096;
 constexpr int kAlignSpan = 2048;
+// At most this many workgroups (longer spans beyond 512K slots): each counts the whole batch, so
+// the ids are read workgroups x numel times in all.
+constexpr int kAlignMaxGroups = 256;
 
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int32_t* __restrict__ ids, int32_t numel, int32_t start, int32_t n_local, int32_t B,
@@ -287,7 +290,9 @@ extern "C" int moe_align(const int32_t* topk_ids, int64_t M, int32_t top_k, int3
               "moe_align: null output pointer");
   MOE_REQUIRE(topk_ids || M == 0, MOE_EINVAL, "moe_align: null topk_ids");
   const int64_t numel = M * top_k;
-  const int32_t span = numel <= kAlignSingleMax ? (int32_t)std::max<int64_t>(numel, 1) : kAlignSpan;
+  const int32_t span = numel <= kAlignSingleMax
+                           ? (int32_t)std::max<int64_t>(numel, 1)
+                           : (int32_t)std::max<int64_t>(kAlignSpan, (numel + kAlignMaxGroups - 1) / kAlignMaxGroups);
   const unsigned grid = (unsigned)std::max<int64_t>(1, (numel + span - 1) / span);
   hipLaunchKernelGGL(align_kernel, dim3(grid), dim3(kAlignThreads), 0, stream, topk_ids, (int32_t)numel,
                      expert_start, n_local, block_m, (int32_t)cap, (int32_t)cap_blocks, span, sorted_token_ids,

@@ -85,6 +85,7 @@ def test_align_deterministic_and_optional_slot_ids():
     (1025, 8, 65, 128, 3),     # the segmented scan (65 experts)
     (20000, 8, 512, 1, 4),     # 79 spans, the largest expert count, block size 1
     (30000, 6, 300, 256, 5),   # 88 spans, the largest block size
+    (75000, 8, 32, 128, 6),    # 600000 slots: the workgroup cap, 256 spans of 2344
 ])
 def test_align_several_workgroups(M, k, n_local, B, seed):
     # batches above 4096 slots are split over workgroups that each count the whole batch: the
