@@ -409,6 +409,37 @@ def gemm13_kernel_name(layer, M, block_m, routed: bool) -> str:
     return name + (" (gate/up, align and activation fused)" if routed else " (gate/up, activation fused)")
 
 
+def dense_reference(name: str, M: int, reps: int = 20) -> dict:
+    """The MFMA ceiling this chip reaches on the layer's shapes without quantisation or grouping:
+    torch's dense bf16 GEMM (hipBLASLt) of the same total shape -- [live slots, K] x [K, N] for
+    each projection -- timed back to back with HIP events on random operands.  A calibration
+    figure reported beside the layer, never part of it."""
+    import torch
+    import workloads as W
+    wl = W.WORKLOADS[name]
+    ids = np.asarray(W.make_inputs(wl, M).topk_ids)
+    live = int(np.count_nonzero((ids >= wl.expert_start) & (ids < wl.expert_start + wl.n_local)))
+    out = {"workload": name, "M": M, "live_slots": live, "gemms": {}}
+    for proj, (k, n) in (("gate_up", (wl.H, 2 * wl.I)), ("down", (wl.I, wl.H))):
+        a = torch.randn(live, k, dtype=torch.bfloat16, device="cuda")
+        b = torch.randn(k, n, dtype=torch.bfloat16, device="cuda")
+        for _ in range(3):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / reps
+        flops = 2.0 * live * k * n
+        out["gemms"][proj] = {"shape": [live, k, n], "us": round(t * 1e6, 1),
+                              "TFLOPs": round(flops / t / 1e12, 1),
+                              "frac": round(flops / t / (PEAK_BF16_TFLOPS * 1e12), 4)}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -427,6 +458,9 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true", help="one line per configuration cell")
     ap.add_argument("--fused-combine", action="store_true",
                     help="decode layers without norm: the weighted sum fused into the down GEMM")
+    ap.add_argument("--dense-reference", action="store_true",
+                    help="only time torch's dense bf16 GEMM (hipBLASLt) on the workload's GEMM shapes "
+                         "with the live slots as rows: the MFMA ceiling without quantisation")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only copy a buffer of this many MiB 10 times (reference kernel of known "
                          "traffic for calibrating the HBM byte counters)")
@@ -449,6 +483,11 @@ def main() -> int:
         print(json.dumps({"copy_bytes": n, "copies": 10}), flush=True)
         return 0
     import workloads as W
+    if a.dense_reference:
+        name = a.workload or W.HEADLINE
+        M = a.M or (W.HEADLINE_M if name == W.HEADLINE else W.WORKLOADS[name].Ms[0])
+        print(json.dumps(dense_reference(name, M)), flush=True)
+        return 0
     if a.sweep:
         for name, wl in W.WORKLOADS.items():
             for M in wl.Ms:
