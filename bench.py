@@ -139,7 +139,7 @@ _LAYERS: dict = {}   # prepared weights reused across cells of one weight set
 
 
 def run_cell(name: str, M: int, steps: int, warmup: int, want_cpu: bool, seed=None,
-             fused_combine: bool = False, block_m=None, group_m=None, ng=(None, None)) -> dict:
+             fused_combine: bool = False, block_m=None, group_m=(None, None), ng=(None, None)) -> dict:
     import torch
     import workloads as W
     from quantized_mixture_experts_align_amd import MoELayer
@@ -162,12 +162,12 @@ def run_cell(name: str, M: int, steps: int, warmup: int, want_cpu: bool, seed=No
     inp = W.make_inputs(wl, M, seed)
     x, ids, gw = W.device_inputs(inp, dev)
     ws = layer.workspace(M, block_m, device=dev)
-    if group_m is not None or ng != (None, None):
+    if group_m != (None, None) or ng != (None, None):
         # launch choices of the MFMA GEMMs only (their results are the same bit for bit)
         from quantized_mixture_experts_align_amd import _lib as L
         ws.cfgs = tuple(P.gemm_config(c.kernel, n or c.ng, c.ksplit, c.gemv_rows,
-                                      c.group_m if group_m is None else group_m)
-                        if c.kernel == L.GEMM_MFMA else c for c, n in zip(ws.cfgs, ng))
+                                      c.group_m if gm is None else gm)
+                        if c.kernel == L.GEMM_MFMA else c for c, n, gm in zip(ws.cfgs, ng, group_m))
     numel = M * wl.top_k
     local = (inp.topk_ids >= wl.expert_start) & (inp.topk_ids < wl.expert_start + wl.n_local)
     live = int(local.sum())
@@ -453,6 +453,8 @@ def main() -> int:
                     help="align block size (default: the library's choice); a launch option only")
     ap.add_argument("--group-m", type=int, default=None,
                     help="MFMA GEMMs: align blocks per XCD group (default: the library's choice)")
+    ap.add_argument("--group-m2", type=int, default=None,
+                    help="MFMA down GEMM only: align blocks per XCD group (overrides --group-m there)")
     ap.add_argument("--ng13", type=int, default=None, help="MFMA gate/up GEMM: tiles per wave")
     ap.add_argument("--ng2", type=int, default=None, help="MFMA down GEMM: tiles per wave")
     ap.add_argument("--sweep", action="store_true", help="one line per configuration cell")
@@ -505,7 +507,8 @@ def main() -> int:
         return 2
     M = a.M or (W.HEADLINE_M if name == W.HEADLINE else W.WORKLOADS[name].Ms[0])
     r = run_cell(name, M, a.steps, a.warmup, not a.no_cpu_baseline, fused_combine=a.fused_combine,
-                 block_m=a.block_m, group_m=a.group_m, ng=(a.ng13, a.ng2))
+                 block_m=a.block_m, group_m=(a.group_m, a.group_m2 if a.group_m2 is not None else a.group_m),
+                 ng=(a.ng13, a.ng2))
     print(json.dumps(r), flush=True)
     return 0
 
