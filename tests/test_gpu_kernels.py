@@ -104,6 +104,57 @@ def test_mfma_result_is_independent_of_tile_width(qtype):
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
+@pytest.mark.parametrize("kind", ["mfma16", "mfma64", "mfma128"])
+@pytest.mark.parametrize("which", [13, 2])
+def test_mfma_store_paths_agree(kind, which):
+    # The MFMA epilogue stages its outputs through LDS and stores 16 bytes per lane when the output
+    # is 16-byte aligned with a row pitch of a multiple of 8 elements, else 8 bytes per lane
+    # directly: an output 8 bytes off alignment with a pitch of N + 4 takes the second path, and
+    # both give the same bytes (columns beyond N untouched).
+    B, cfg = CFGS[kind]
+    qtype = "nvfp4_g16"
+    wl = W.small_workload(qtype)
+    lw = W.make_weights(wl)
+    M = 61
+    inp = W.make_inputs(wl, M)
+    w13, w2, _ = W.device_weights(lw)
+    if which == 13:
+        Wp = P.moe_w4a16_prepare(qtype, w13["codes"], w13["scales"], w13.get("gs"), w13.get("bias"),
+                                 L.PREP_GATE_UP, w13.get("zeros"))
+        A, top_k = _bf16_dev(inp.x), wl.top_k
+    else:
+        Wp = P.moe_w4a16_prepare(qtype, w2["codes"], w2["scales"], w2.get("gs"), w2.get("bias"), 0, w2.get("zeros"))
+        rng = np.random.default_rng(3)
+        A = _bf16_dev(W._to_bf16_bits(rng.standard_normal((M * wl.top_k, wl.I)).astype(np.float32)))
+        top_k = 1
+    s, e, n, _ = P.moe_align(torch.from_numpy(inp.topk_ids).cuda(), wl.expert_start, wl.n_local, B)
+    numel = M * wl.top_k
+    N = Wp.N
+    print(f"store paths W{which} {kind} N={N}", flush=True)
+    aligned = torch.zeros((numel, N), dtype=torch.bfloat16, device="cuda")
+    buf = torch.full((numel * (N + 4) + 4,), 7.0, dtype=torch.bfloat16, device="cuda")
+    offset = buf[4:].view(numel, N + 4)
+    assert offset.data_ptr() % 16 == 8 and (N + 4) % 8 == 4
+    P.moe_w4a16_gemm(A, Wp, s, e, n, numel, top_k, B, out=aligned, cfg=cfg)
+    P.moe_w4a16_gemm(A, Wp, s, e, n, numel, top_k, B, out=offset, cfg=cfg)
+    torch.cuda.synchronize()
+    live = torch.from_numpy(np.nonzero((inp.topk_ids.reshape(-1) >= wl.expert_start)
+                                       & (inp.topk_ids.reshape(-1) < wl.expert_start + wl.n_local))[0]).cuda()
+    assert torch.equal(aligned[live].view(torch.int16), offset[live, :N].contiguous().view(torch.int16))
+    assert torch.all(offset[:, N:] == 7.0)
+    if which == 13:   # the fused activation's epilogue (I = N / 2 columns per row)
+        I = N // 2
+        a_al = torch.zeros((numel, I), dtype=torch.bfloat16, device="cuda")
+        buf2 = torch.full((numel * (I + 4) + 4,), 7.0, dtype=torch.bfloat16, device="cuda")
+        a_off = buf2[4:].view(numel, I + 4)
+        cfg_act = P.gemm_config(L.GEMM_MFMA, max(2, cfg.ng), 0, 0)   # (gate/up tile pairs)
+        P.moe_w4a16_gemm_act("silu_mul", A, Wp, s, e, n, numel, top_k, B, out=a_al, cfg=cfg_act)
+        P.moe_w4a16_gemm_act("silu_mul", A, Wp, s, e, n, numel, top_k, B, out=a_off, cfg=cfg_act)
+        torch.cuda.synchronize()
+        assert torch.equal(a_al[live].view(torch.int16), a_off[live, :I].contiguous().view(torch.int16))
+        assert torch.all(a_off[:, I:] == 7.0)
+
+
 @pytest.mark.parametrize("gemv_rows", [4, 0])
 def test_decode_is_reproducible(gemv_rows):
     cfg = P.gemm_config(L.GEMM_DECODE, 2, 4, gemv_rows)
