@@ -72,6 +72,16 @@ def test_align_edge_cases():
     _check(rng.integers(0, 256, (16384, 8)).astype(np.int32), 0, 32, 128)    # 131072 slots
 
 
+def test_align_several_workgroups_edge_cases():
+    rng = np.random.default_rng(11)
+    _check(np.full((5000, 2), 7, np.int32), 7, 1, 64)                         # one expert, 5 spans
+    _check(rng.integers(100, 300, (3000, 4)).astype(np.int32), 0, 64, 16)     # all off-slice
+    _check(rng.integers(0, 40, (1024, 8)).astype(np.int32), 0, 32, 128)       # 8192 = 4 spans exactly
+    ids = rng.integers(0, 32, (4097, 2)).astype(np.int32)
+    ids[:2048] = 40                                                           # first span all off-slice
+    _check(ids, 0, 32, 32)
+
+
 def test_align_deterministic_and_optional_slot_ids():
     inp = W.make_inputs(W.WORKLOADS[W.NVFP4_ZIPF], 4096)
     a = _run(inp.topk_ids, 0, 32, 128)
