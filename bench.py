@@ -166,7 +166,7 @@ def run_cell(name: str, M: int, steps: int, warmup: int, want_cpu: bool, seed=No
         # launch choices of the MFMA GEMMs only (their results are the same bit for bit)
         from quantized_mixture_experts_align_amd import _lib as L
         ws.cfgs = tuple(P.gemm_config(c.kernel, n or c.ng, c.ksplit, c.gemv_rows,
-                                      c.group_m if gm is None else gm)
+                                      c.group_m if gm is None else gm, c.block_order)
                         if c.kernel == L.GEMM_MFMA else c for c, n, gm in zip(ws.cfgs, ng, group_m))
     numel = M * wl.top_k
     local = (inp.topk_ids >= wl.expert_start) & (inp.topk_ids < wl.expert_start + wl.n_local)

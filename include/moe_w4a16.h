@@ -120,6 +120,32 @@ int moe_align(const int32_t* topk_ids, int64_t M, int32_t top_k, int32_t expert_
               int32_t n_local, int32_t block_m, int32_t* sorted_token_ids, int32_t* expert_ids,
               int32_t* num_tokens_post_padded, int32_t* slot_local_ids, hipStream_t stream);
 
+/*
+ * moe_align plus a block schedule for the MFMA GEMM (moe_gemm_config.block_order): the same
+ * four outputs, bit for bit, and
+ *   block_order       device int32 [blocks_len]: entry q < nb (nb = num_tokens_post_padded /
+ *                     block_m, the live blocks) is a block index; entries from nb on are -1.
+ *                     The live blocks appear once each, ordered by falling 16-slot group count
+ *                     ceil(live rows / 16) -- every full block, and every last block of an expert
+ *                     that is fewer than 16 rows short of full, first; then the shorter last
+ *                     blocks -- and by block index among equal counts.
+ * Why: a block costs its GEMM workgroups roughly in proportion to its live 16-slot groups (an
+ * expert's short last block about half a full one), and the GEMM gives whole align blocks to the
+ * eight XCDs in turn.  In align order a regular pattern of full and short blocks can give some XCDs
+ * only full blocks (uniform routing: full, short, full, short, ...), and the launch ends on
+ * whichever blocks come last.  In falling-cost order the XCDs' shares differ by at most one block
+ * and the launch ends on the shortest blocks.  Measured (one MI355X, NVFP4 expert slice with Zipf
+ * routing, whole layer): 1024 tokens 718 -> 695 us (down GEMM 231 -> 218 us), 256 tokens 335 ->
+ * 326 us, 4096 tokens 2250 -> 2227 us; keeping align order and alternating costly and cheap blocks
+ * inside rounds of eight gained less (1024 tokens 712 us).  (The pages give no block scheduler:
+ * this is a launch-order choice of this library's GEMM and changes no result.)
+ * Errors as moe_align; block_order NULL with blocks_len > 0 is MOE_EINVAL.
+ */
+int moe_align_sched(const int32_t* topk_ids, int64_t M, int32_t top_k, int32_t expert_start,
+                    int32_t n_local, int32_t block_m, int32_t* sorted_token_ids, int32_t* expert_ids,
+                    int32_t* num_tokens_post_padded, int32_t* slot_local_ids, int32_t* block_order,
+                    hipStream_t stream);
+
 /* ----------------------------------------------------------------------------- weights */
 
 /* prepare flags */
@@ -233,6 +259,11 @@ typedef struct moe_gemm_config {
   int32_t group_m;        /* MFMA: align blocks per workgroup group, 0..64 (0 = chosen from
                              the shapes); a group's workgroups run on one XCD, sharing its
                              L2.  Launch order only: results do not depend on it             */
+  const int32_t* block_order; /* MFMA: device int32 [blocks_len], the block schedule that
+                             moe_align_sched wrote for the same align call, or NULL (blocks
+                             in align order).  The workgroups take their align blocks in this
+                             order.  Launch order only: results do not depend on it; an entry
+                             that names no live block makes its workgroups skip it */
 } moe_gemm_config;
 
 /* Host heuristics (pure host functions).  moe_choose_block_m: block_m for the align from the

@@ -30,7 +30,7 @@ class MoeWeights(C.Structure):
 
 class MoeGemmConfig(C.Structure):
     _fields_ = [("kernel", C.c_int32), ("ng", C.c_int32), ("ksplit", C.c_int32),
-                ("gemv_rows", C.c_int32), ("group_m", C.c_int32)]
+                ("gemv_rows", C.c_int32), ("group_m", C.c_int32), ("block_order", C.c_void_p)]
 
 
 class MoeRequantConfig(C.Structure):
@@ -47,6 +47,7 @@ SIGNATURES = {
     "moe_abi_version": (_I32, []),
     "moe_align_capacity": (C.c_int, [_I64, _I32, _I32, _I32, C.POINTER(_I64), C.POINTER(_I64)]),
     "moe_align": (C.c_int, [_P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
+    "moe_align_sched": (C.c_int, [_P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "moe_w4a16_prepared_size": (C.c_int, [C.c_int, _I32, _I32, _I32, C.c_uint32, _I32,
                                           C.POINTER(_I32), C.POINTER(_I32), C.POINTER(_SZ)]),
     "moe_w4a16_prepare": (C.c_int, [C.c_int, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, C.c_uint32, _P,

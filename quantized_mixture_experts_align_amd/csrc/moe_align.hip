@@ -27,6 +27,12 @@
 //   4. fill:    padding entries (in parallel over expert x position) and the tail get the
 //               sentinel, block -> expert by binary search over the segment starts; these index
 //               ranges are split over the workgroups
+//   5. schedule (moe_align_sched only): the position of every live block in the GEMM's block
+//               order, computed in each workgroup from the per-expert totals alone (so all agree):
+//               an expert's last block with fewer than C = ceil(B/16) live 16-slot groups (a
+//               "short" block) sets bit (C-1-groups) * n_local + e of a key bitmap, and a short
+//               block's position is the number of full-class blocks plus the set bits below its key;
+//               any other block keeps its index minus the short blocks of the experts before it
 #include "moe_internal.h"
 
 namespace moe {
@@ -43,11 +49,14 @@ constexpr int kAlignSpan = 2048;
 // At most this many workgroups (longer spans beyond 512K slots): each counts the whole batch, so
 // the ids are read workgroups x numel times in all.
 constexpr int kAlignMaxGroups = 256;
+// key bitmap of the block schedule: (16-slot classes below full) x experts, at most 15 x 512 bits
+constexpr int kSchedKeyWords = (15 * kAlignMaxLocal + 31) / 32;
 
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int32_t* __restrict__ ids, int32_t numel, int32_t start, int32_t n_local, int32_t B,
     int32_t cap, int32_t cap_blocks, int32_t span, int32_t* __restrict__ sorted,
-    int32_t* __restrict__ eids, int32_t* __restrict__ ntpp, int32_t* __restrict__ slot_local) {
+    int32_t* __restrict__ eids, int32_t* __restrict__ ntpp, int32_t* __restrict__ slot_local,
+    int32_t* __restrict__ border) {
   __shared__ int32_t cnt[kAlignWaves * kAlignMaxLocal];  // per wave and expert
   __shared__ int32_t seg[kAlignMaxLocal + 1];            // segment start of each expert
   __shared__ int32_t tot[kAlignMaxLocal];                // live slots of each expert (whole batch)
@@ -250,6 +259,49 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   }
   const int total = seg[n_local];
   for (int p = total + gt; p < cap; p += gstride) sorted[p] = numel;
+
+  // block schedule: key bitmap of the short blocks, their experts, and prefix counts of the keys
+  __shared__ uint32_t key_bits[kSchedKeyWords];
+  __shared__ uint32_t short_bits[kAlignMaxLocal / 32];
+  __shared__ int32_t key_pre[kSchedKeyWords + 1];
+  const int C = (B + 15) >> 4;                 // 16-slot groups of a full block
+  const int nkw = ((C - 1) * n_local + 31) >> 5;
+  // the short last block of expert e: its key, or -1
+  auto short_key = [&](int e) {
+    const int r = tot[e] % B, lg = (r + 15) >> 4;
+    return (r > 0 && lg < C) ? (C - 1 - lg) * n_local + e : -1;
+  };
+  if (border) {
+    for (int i = tid; i < nkw; i += kAlignThreads) key_bits[i] = 0u;
+    for (int i = tid; i < kAlignMaxLocal / 32; i += kAlignThreads) short_bits[i] = 0u;
+    __syncthreads();
+    for (int e = tid; e < n_local; e += kAlignThreads) {
+      const int k = short_key(e);
+      if (k >= 0) {
+        atomicOr(&key_bits[k >> 5], 1u << (k & 31));
+        atomicOr(&short_bits[e >> 5], 1u << (e & 31));
+      }
+    }
+    __syncthreads();
+    if (w == 0) {
+      int run = 0;
+      for (int base = 0; base < nkw; base += 64) {
+        const int i = base + lane;
+        const int c = i < nkw ? __popc(key_bits[i]) : 0;
+        int x = c;
+        for (int d = 1; d < 64; d <<= 1) {
+          const int o = __shfl_up(x, d);
+          if (lane >= d) x += o;
+        }
+        if (i < nkw) key_pre[i] = run + x - c;
+        run += __shfl(x, 63);
+      }
+      if (lane == 0) key_pre[nkw] = run;
+    }
+    __syncthreads();
+  }
+  const int nb_live = total / B;
+  const int n_top = border ? nb_live - key_pre[nkw] : 0;  // blocks of the full class
   for (int b = gt; b < cap_blocks; b += gstride) {
     int e = -1;
     if (b * B < total) {
@@ -262,6 +314,22 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
       e = lo;
     }
     eids[b] = e;
+    if (border) {
+      if (b >= nb_live) {
+        border[b] = -1;  // (positions from nb_live on hold no block)
+      } else {
+        const int k = (b + 1) * B == seg[e + 1] ? short_key(e) : -1;
+        int pos;
+        if (k >= 0) {
+          pos = n_top + key_pre[k >> 5] + __popc(key_bits[k >> 5] & ((1u << (k & 31)) - 1u));
+        } else {
+          int before = __popc(short_bits[e >> 5] & ((1u << (e & 31)) - 1u));
+          for (int j = 0; j < (e >> 5); ++j) before += __popc(short_bits[j]);
+          pos = b - before;
+        }
+        border[pos] = b;
+      }
+    }
   }
   if (gt == 0) *ntpp = total;
 }
@@ -270,10 +338,10 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
 
 using namespace moe;
 
-extern "C" int moe_align(const int32_t* topk_ids, int64_t M, int32_t top_k, int32_t expert_start,
-                         int32_t n_local, int32_t block_m, int32_t* sorted_token_ids,
-                         int32_t* expert_ids, int32_t* num_tokens_post_padded,
-                         int32_t* slot_local_ids, hipStream_t stream) {
+static int align_launch(const int32_t* topk_ids, int64_t M, int32_t top_k, int32_t expert_start,
+                        int32_t n_local, int32_t block_m, int32_t* sorted_token_ids, int32_t* expert_ids,
+                        int32_t* num_tokens_post_padded, int32_t* slot_local_ids, bool sched,
+                        int32_t* block_order, hipStream_t stream) {
   MOE_REQUIRE(M >= 0 && top_k >= 1 && top_k <= 64, MOE_EINVAL, "moe_align: M=%lld top_k=%d",
               (long long)M, top_k);
   MOE_REQUIRE(n_local >= 1 && n_local <= kAlignMaxLocal, MOE_EUNSUPPORTED,
@@ -289,6 +357,7 @@ extern "C" int moe_align(const int32_t* topk_ids, int64_t M, int32_t top_k, int3
   MOE_REQUIRE(num_tokens_post_padded && ((sorted_token_ids && expert_ids) || cap == 0), MOE_EINVAL,
               "moe_align: null output pointer");
   MOE_REQUIRE(topk_ids || M == 0, MOE_EINVAL, "moe_align: null topk_ids");
+  MOE_REQUIRE(!sched || block_order || cap_blocks == 0, MOE_EINVAL, "moe_align_sched: null block_order");
   const int64_t numel = M * top_k;
   const int32_t span = numel <= kAlignSingleMax
                            ? (int32_t)std::max<int64_t>(numel, 1)
@@ -296,6 +365,22 @@ extern "C" int moe_align(const int32_t* topk_ids, int64_t M, int32_t top_k, int3
   const unsigned grid = (unsigned)std::max<int64_t>(1, (numel + span - 1) / span);
   hipLaunchKernelGGL(align_kernel, dim3(grid), dim3(kAlignThreads), 0, stream, topk_ids, (int32_t)numel,
                      expert_start, n_local, block_m, (int32_t)cap, (int32_t)cap_blocks, span, sorted_token_ids,
-                     expert_ids, num_tokens_post_padded, slot_local_ids);
+                     expert_ids, num_tokens_post_padded, slot_local_ids, block_order);
   return check_launch("moe_align");
+}
+
+extern "C" int moe_align(const int32_t* topk_ids, int64_t M, int32_t top_k, int32_t expert_start,
+                         int32_t n_local, int32_t block_m, int32_t* sorted_token_ids,
+                         int32_t* expert_ids, int32_t* num_tokens_post_padded,
+                         int32_t* slot_local_ids, hipStream_t stream) {
+  return align_launch(topk_ids, M, top_k, expert_start, n_local, block_m, sorted_token_ids, expert_ids,
+                      num_tokens_post_padded, slot_local_ids, false, nullptr, stream);
+}
+
+extern "C" int moe_align_sched(const int32_t* topk_ids, int64_t M, int32_t top_k, int32_t expert_start,
+                               int32_t n_local, int32_t block_m, int32_t* sorted_token_ids,
+                               int32_t* expert_ids, int32_t* num_tokens_post_padded,
+                               int32_t* slot_local_ids, int32_t* block_order, hipStream_t stream) {
+  return align_launch(topk_ids, M, top_k, expert_start, n_local, block_m, sorted_token_ids, expert_ids,
+                      num_tokens_post_padded, slot_local_ids, true, block_order, stream);
 }

@@ -33,7 +33,7 @@ using namespace moe;
 
 extern "C" const char* moe_last_error(void) { return g_err; }
 
-extern "C" int32_t moe_abi_version(void) { return 5; }
+extern "C" int32_t moe_abi_version(void) { return 6; }
 
 extern "C" int moe_align_capacity(int64_t M, int32_t top_k, int32_t n_local, int32_t block_m,
                                   int64_t* sorted_len, int64_t* blocks_len) {

@@ -216,6 +216,7 @@ static int gemm_impl(int act, float alpha, float limit, const uint16_t* A, int64
   MOE_REQUIRE(c.group_m >= 0 && c.group_m <= 64, MOE_EINVAL, "moe_w4a16_gemm: group_m=%d (0..64)", c.group_m);
   if (c.group_m == 0) c.group_m = moe::default_group_m(W->K, block_m);
   a.group_m = c.group_m;
+  a.border = c.block_order;
   MOE_REQUIRE((int64_t)((W->N / kTileN + 4 * c.ng - 1) / (4 * c.ng)) * cap_blocks < (1ll << 31),
               MOE_EUNSUPPORTED, "moe_w4a16_gemm: grid too large");
   switch (W->qtype) {

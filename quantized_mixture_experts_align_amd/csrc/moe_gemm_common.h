@@ -52,6 +52,8 @@ struct GemmArgs {
   int32_t cmb_k, cmb_ntok;
   int64_t cmb_ldo;
   float cmb_rsf;           // routed scaling factor
+  // MFMA: block schedule (moe_align_sched), or null for the align order
+  const int32_t* border;
 };
 constexpr int kFusedAlignSlots = 64;  // one slot per lane of one wave
 

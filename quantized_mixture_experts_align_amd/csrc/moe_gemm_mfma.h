@@ -141,7 +141,18 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs a) {
   const int nblk = (NTA + 4 * NGA - 1) / (4 * NGA);
   int mb, nb;
   grouped_block(nblk, a.group_m, mb, nb);
-  if (mb * BM >= *a.ntpp) return;
+  {
+    // with a block schedule, position mb of the launch takes the block the schedule names there
+    // (read together with the live length: the schedule has an entry for every position)
+    const int ntpp = *a.ntpp;
+    if (a.border) {
+      const int q = mb;
+      mb = a.border[q];
+      if (q * BM >= ntpp || mb < 0 || mb >= ntpp / BM) return;  // (no product of an untrusted entry)
+    } else if (mb * BM >= ntpp) {
+      return;
+    }
+  }
   const int e = a.eids[mb];
   if (e < 0 || e >= a.E) return;
   // the wave index is uniform: keep it (and every LDS address derived from it) in scalar registers

@@ -31,6 +31,7 @@ class Workspace:
     cfgs: Optional[tuple] = None    # (gate/up, down) GEMM launch configurations
     perm: Optional[torch.Tensor] = None   # act-order: the gathered A of a GEMM [numel, max(H, I)]
     counters: Optional[torch.Tensor] = None  # fused weighted sum: arrival counters, kept zero
+    sched: Optional[torch.Tensor] = None  # MFMA GEMMs: the align's block schedule [blocks_len]
 
 
 class MoELayer:
@@ -102,11 +103,20 @@ class MoELayer:
         perm = None
         if any(self.act_order):
             perm = torch.empty(numel * max(self.W13.K, self.W2.K), **bf)
+        cfgs = self.configs(M, B)
+        sched = None
+        if B > 16 and any(c.kernel == L.GEMM_MFMA for c in cfgs):
+            # the align writes the MFMA GEMMs' block schedule, the GEMMs take their blocks in it
+            # (16-slot blocks all have one 16-slot group: their schedule is the align order)
+            sched = torch.empty(b_len, **i32)
+            for c in cfgs:
+                if c.kernel == L.GEMM_MFMA:
+                    c.block_order = sched.data_ptr()
         return Workspace(M, B, torch.empty(s_len, **i32), torch.empty(b_len, **i32),
                          torch.empty(1, **i32), torch.empty((M, self.top_k), **i32),
                          torch.empty(numel * max(self.W13.N, self.H), **bf),
                          torch.empty((numel, self.I), **bf), torch.empty((M, self.H), **bf),
-                         self.configs(M, B), perm)
+                         cfgs, perm, sched=sched)
 
     def _combinable(self, B: int, cfg2) -> bool:
         # the weighted sum fuses into the streaming decode kernel's down GEMM when there is no norm
@@ -147,14 +157,19 @@ class MoELayer:
                              "streaming decode kernel")
         align_out = (ws.sorted_ids, ws.expert_ids, ws.ntpp, ws.slot_local)
         if fused_act and self.gated and cfg13.ng < 2:
-            cfg13 = ops.gemm_config(cfg13.kernel, 2, cfg13.ksplit, cfg13.gemv_rows, cfg13.group_m)
+            cfg13 = ops.gemm_config(cfg13.kernel, 2, cfg13.ksplit, cfg13.gemv_rows, cfg13.group_m,
+                                    cfg13.block_order)
+        if fused_align and cfg2.block_order:
+            # the align fused into GEMM1 writes no schedule: the down GEMM takes the align order
+            cfg2 = ops.gemm_config(cfg2.kernel, cfg2.ng, cfg2.ksplit, cfg2.gemv_rows, cfg2.group_m)
         if fused_align:
             _, (sorted_ids, eids, ntpp, loc) = ops.moe_w4a16_gemm_act_routed(
                 self.act, x, self.W13, topk_ids, self.expert_start, B, self.alpha, self.limit,
                 out=ws.a, align_out=align_out, cfg=cfg13)
         else:
+            # (a configuration that names the workspace's schedule gets it written by this align)
             sorted_ids, eids, ntpp, loc = ops.moe_align(topk_ids, self.expert_start, self.n_local, B,
-                                                        out=align_out)
+                                                        out=align_out, schedule=ws.sched)
             a1, k1 = x, self.top_k
             if self.act_order[0]:   # one gathered row per slot, read with top_k = 1
                 a1 = ops.moe_permute_cols(x, self.W13, loc.view(-1), self.top_k,

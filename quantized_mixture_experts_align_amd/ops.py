@@ -48,8 +48,10 @@ def choose_block_m(numel: int, n_local: int, expected_live: int = 0, K: int = 0)
 
 
 def moe_align(topk_ids: torch.Tensor, expert_start: int, n_local: int, block_m: int,
-              slot_local_ids: bool = True, out=None):
-    """-> (sorted_token_ids, expert_ids, num_tokens_post_padded, slot_local_ids or None)."""
+              slot_local_ids: bool = True, out=None, schedule: Optional[torch.Tensor] = None):
+    """-> (sorted_token_ids, expert_ids, num_tokens_post_padded, slot_local_ids or None).
+    With `schedule` (int32 [blocks_len]) the call is moe_align_sched, which also writes the MFMA
+    GEMM's block schedule there (pass it on as gemm_config(..., block_order=schedule))."""
     _need(topk_ids, torch.int32, "topk_ids")
     M, k = topk_ids.shape
     s_len, b_len = align_capacity(M, k, n_local, block_m)
@@ -60,8 +62,16 @@ def moe_align(topk_ids: torch.Tensor, expert_start: int, n_local: int, block_m: 
                torch.empty(1, dtype=torch.int32, device=dev),
                torch.empty((M, k), dtype=torch.int32, device=dev) if slot_local_ids else None)
     sorted_ids, eids, ntpp, loc = out
-    L.check(L.lib().moe_align(_ptr(topk_ids), M, k, expert_start, n_local, block_m, _ptr(sorted_ids),
-                              _ptr(eids), _ptr(ntpp), _ptr(loc), _stream()), "moe_align")
+    if schedule is None:
+        L.check(L.lib().moe_align(_ptr(topk_ids), M, k, expert_start, n_local, block_m, _ptr(sorted_ids),
+                                  _ptr(eids), _ptr(ntpp), _ptr(loc), _stream()), "moe_align")
+    else:
+        _need(schedule, torch.int32, "schedule")
+        if schedule.numel() < b_len:
+            raise ValueError(f"schedule holds {schedule.numel()} entries, need {b_len}")
+        L.check(L.lib().moe_align_sched(_ptr(topk_ids), M, k, expert_start, n_local, block_m, _ptr(sorted_ids),
+                                        _ptr(eids), _ptr(ntpp), _ptr(loc), _ptr(schedule), _stream()),
+                "moe_align_sched")
     return sorted_ids, eids, ntpp, loc
 
 
@@ -163,8 +173,13 @@ def moe_norm_weight(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> torc
 
 
 def gemm_config(kernel: int = L.GEMM_AUTO, ng: int = 0, ksplit: int = 0, gemv_rows: int = 0,
-                group_m: int = 0):
-    return L.MoeGemmConfig(kernel, ng, ksplit, gemv_rows, group_m)
+                group_m: int = 0, block_order=None):
+    """block_order: the schedule tensor moe_align(..., schedule=) filled, or its device address
+    (the tensor must outlive every launch that uses the configuration)."""
+    if isinstance(block_order, torch.Tensor):
+        _need(block_order, torch.int32, "block_order")
+        block_order = block_order.data_ptr()
+    return L.MoeGemmConfig(kernel, ng, ksplit, gemv_rows, group_m, block_order)
 
 
 def gemm_choose(W: PreparedWeights, numel: int, block_m: int, num_cus: int = 0,

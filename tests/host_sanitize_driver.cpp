@@ -195,7 +195,7 @@ int main() {
     CHECK(same_xcd);
   }
 
-  CHECK(moe_abi_version() == 5);
+  CHECK(moe_abi_version() == 6);
   if (failures) {
     std::printf("%d checks failed\n", failures);
     return 1;
