@@ -105,9 +105,11 @@ class MoELayer:
             perm = torch.empty(numel * max(self.W13.K, self.W2.K), **bf)
         cfgs = self.configs(M, B)
         sched = None
-        if B > 16 and any(c.kernel == L.GEMM_MFMA for c in cfgs):
-            # the align writes the MFMA GEMMs' block schedule, the GEMMs take their blocks in it
-            # (16-slot blocks all have one 16-slot group: their schedule is the align order)
+        if B > 16 and min(self.W13.K, self.W2.K) >= 2048 and any(c.kernel == L.GEMM_MFMA for c in cfgs):
+            # the align writes the MFMA GEMMs' block schedule, the GEMMs take their blocks in it.
+            # Only for long K loops: measured on the int4 layers (K = 512 / 1024, 64-slot blocks)
+            # the schedule's align work and prologue read cost 1-1.5 us of a 40-75 us step with
+            # the GEMMs unchanged; 16-slot blocks all have one 16-slot group (the align order).
             sched = torch.empty(b_len, **i32)
             for c in cfgs:
                 if c.kernel == L.GEMM_MFMA:
