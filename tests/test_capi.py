@@ -83,6 +83,10 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert b"n_local" in lib.moe_last_error()
     assert lib.moe_align(None, 4, 8, 0, 32, 0, s, e, n, None, None) == L.MOE_EUNSUPPORTED
     assert lib.moe_align(None, 4, 8, 0, 32, 16, None, e, n, None, None) == L.MOE_EINVAL
+    # the scheduling align: the same checks, and a schedule buffer whenever there are blocks
+    assert lib.moe_align_sched(None, 4, 8, 0, 0, 16, s, e, n, None, s, None) == L.MOE_EUNSUPPORTED
+    assert lib.moe_align_sched(s, 4, 8, 0, 32, 16, s, e, n, None, None, None) == L.MOE_EINVAL
+    assert b"block_order" in lib.moe_last_error()
     assert lib.moe_act(7, s, 16, s, 8, 4, 8, None, 1.0, 1.0, None) == L.MOE_EINVAL
     assert lib.moe_act(0, s, 16, s, 8, 4, 12, None, 1.0, 1.0, None) == L.MOE_EUNSUPPORTED
     assert lib.moe_combine(s, s, s, None, 1e-8, 1.0, 4, 17, 64, s, None) == L.MOE_EUNSUPPORTED
