@@ -126,9 +126,10 @@ int moe_align(const int32_t* topk_ids, int64_t M, int32_t top_k, int32_t expert_
  *   block_order       device int32 [blocks_len]: entry q < nb (nb = num_tokens_post_padded /
  *                     block_m, the live blocks) is a block index; entries from nb on are -1.
  *                     The live blocks appear once each, ordered by falling 16-slot group count
- *                     ceil(live rows / 16) -- every full block, and every last block of an expert
- *                     that is fewer than 16 rows short of full, first; then the shorter last
- *                     blocks -- and by block index among equal counts.
+ *                     ceil(live rows / 16) -- first every block with a full block's count
+ *                     (the full blocks and the experts' last blocks that fill as many groups),
+ *                     then the experts' shorter last blocks -- and by block index among equal
+ *                     counts.
  * Why: a block costs its GEMM workgroups roughly in proportion to its live 16-slot groups (an
  * expert's short last block about half a full one), and the GEMM gives whole align blocks to the
  * eight XCDs in turn.  In align order a regular pattern of full and short blocks can give some XCDs
