@@ -343,14 +343,14 @@ int moe_w4a16_gemm_act(moe_act_kind kind, float alpha, float limit, const uint16
 /*
  * moe_align fused into moe_w4a16_gemm_act, for small batches: the single-token fast path that
  * the Muse Spark experiment's kernel_fn takes with moe_align_single_token (decode batches), here
- * for up to 64 slots (M * top_k <= 64) and block_m <= 16.  One launch computes exactly what
+ * for up to 128 slots (M * top_k <= 128) and block_m <= 16.  One launch computes exactly what
  * moe_align(topk_ids, M, top_k, expert_start, W13->n_experts, block_m, ...) followed by
  * moe_w4a16_gemm_act(..., numel = M * top_k, ...) computes, bit for bit: `out` as
  * moe_w4a16_gemm_act, and sorted_token_ids [cap], expert_ids [cap / block_m],
  * num_tokens_post_padded [1] and slot_local_ids [M * top_k] (capacity and contents as moe_align;
  * all four are outputs here, device memory owned by the caller) for the down GEMM and the
  * combine that follow.  Runs the streaming decode kernel: cfg NULL or AUTO, or kernel DECODE with
- * gemv_rows 0.  Errors: MOE_EUNSUPPORTED for more than 64 slots, block_m > 16, n_experts > 512 or
+ * gemv_rows 0.  Errors: MOE_EUNSUPPORTED for more than 128 slots, block_m > 16, n_experts > 512 or
  * another kernel; otherwise as moe_align and moe_w4a16_gemm_act.
  */
 int moe_w4a16_gemm_act_routed(moe_act_kind kind, float alpha, float limit, const uint16_t* A,

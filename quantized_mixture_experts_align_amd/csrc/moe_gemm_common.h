@@ -55,7 +55,7 @@ struct GemmArgs {
   // MFMA: block schedule (moe_align_sched), or null for the align order
   const int32_t* border;
 };
-constexpr int kFusedAlignSlots = 64;  // one slot per lane of one wave
+constexpr int kFusedAlignSlots = 128;  // two 64-slot batches of one wave
 
 // Fused gate/up epilogue: the GEMM's output tiles come in (gate, up) pairs held by the same lane;
 // both are rounded to bf16 as the stored GEMM output would be, then the activation is applied

@@ -32,47 +32,80 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Route-and-align of at most kFusedAlignSlots slots, computed by wave 0 with one slot per lane
-// (the same result as moe_align: local expert = id - start inside [start, start + E), else the
-// slot is dropped; slots grouped by ascending expert, ascending slot order inside an expert,
-// each expert's run padded to whole blocks of B rows with the sentinel numel).
+// Route-and-align of at most kFusedAlignSlots slots, computed by wave 0, one slot per lane in each
+// 64-slot batch (the same result as moe_align: local expert = id - start inside [start, start + E),
+// else the slot is dropped; slots grouped by ascending expert, ascending slot order inside an
+// expert, each expert's run padded to whole blocks of B rows with the sentinel numel).
 //   f_rows[b * 16 + r] = slot of row r of block b (numel for padding), f_be[b] = its expert,
 //   returns the block count.  Workgroup 0 also writes sorted_out[cap], eids_out[cap_blocks]
 //   (-1 past the last block), *ntpp_out and slot_local_out[numel].  Every thread calls it.
 __device__ int fused_align(const GemmArgs& a, int* f_rows, int* f_be, int* f_nblk) {
+  constexpr int NB = kFusedAlignSlots / 64;  // 64-slot batches
   const int tid = (int)threadIdx.x, lane = tid & 63, B = a.block_m, numel = a.numel;
   for (int p = tid; p < kFusedAlignSlots * 16; p += (int)blockDim.x) f_rows[p] = numel;
   __syncthreads();
   if (tid < 64) {
-    const int id = lane < numel ? a.topk_ids[lane] : -1;
-    const bool live = lane < numel && id >= a.expert_start && id - a.expert_start < a.E;
-    const int le = live ? id - a.expert_start : -1;
-    // lanes routed to the same expert: ballots over the bits of the expert id
-    uint64_t same = __ballot(live);
-    for (int b = 0; (1 << b) < a.E; ++b) {
-      const bool bit = live && ((le >> b) & 1);
-      const uint64_t m = __ballot(bit);
-      same &= bit ? m : ~m;
+    int le[NB];
+    bool live[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int s = 64 * j + lane;
+      const int id = s < numel ? a.topk_ids[s] : -1;
+      live[j] = s < numel && id >= a.expert_start && id - a.expert_start < a.E;
+      le[j] = live[j] ? id - a.expert_start : -1;
     }
+    // the slots of batch jj routed to local expert e (e is this lane's own; the ballots over the
+    // bits of the batch's expert ids are the same for every lane)
+    auto same_in = [&](int jj, int e) {
+      uint64_t m = __ballot(live[jj]);
+      for (int b = 0; (1 << b) < a.E; ++b) {
+        const uint64_t mb = __ballot(live[jj] && ((le[jj] >> b) & 1));
+        m &= ((e >> b) & 1) ? mb : ~mb;
+      }
+      return m;
+    };
     const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-    const int r = __popcll(same & below);               // rank among the expert's slots
-    const int nbe = (__popcll(same) + B - 1) / B;       // blocks of the expert
-    const bool first = live && r == 0;
-    // blocks of the experts before this one: a walk over the first slot of every live expert
-    uint64_t fm = __ballot(first);
-    int bs = 0, tot = 0;
-    while (fm) {
-      const int j = __builtin_ctzll(fm);
-      fm &= fm - 1;
-      const int lej = __shfl(le, j), nj = __shfl(nbe, j);
-      if (lej < le) bs += nj;
-      tot += nj;
+    int r[NB], nbe[NB];
+    bool first[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      int before = 0, count = 0;   // the expert's slots in earlier batches / in all batches
+#pragma unroll
+      for (int jj = 0; jj < NB; ++jj) {
+        const uint64_t m = same_in(jj, le[j]);
+        if (jj < j) before += __popcll(m);
+        if (jj == j) before += __popcll(m & below);
+        count += __popcll(m);
+      }
+      r[j] = before;                          // rank among the expert's slots
+      nbe[j] = (count + B - 1) / B;           // blocks of the expert
+      first[j] = live[j] && r[j] == 0;
     }
-    if (live) f_rows[(bs + r / B) * 16 + r % B] = lane;
-    if (first)
-      for (int t = 0; t < nbe; ++t) f_be[bs + t] = le;
+    // blocks of the experts before each slot's: a walk over the first slot of every live expert
+    int bs[NB], tot = 0;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) bs[j] = 0;
+#pragma unroll
+    for (int jj = 0; jj < NB; ++jj) {
+      uint64_t fm = __ballot(first[jj]);
+      while (fm) {
+        const int q = __builtin_ctzll(fm);
+        fm &= fm - 1;
+        const int lej = __shfl(le[jj], q), nj = __shfl(nbe[jj], q);
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          if (lej < le[j]) bs[j] += nj;
+        tot += nj;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (live[j]) f_rows[(bs[j] + r[j] / B) * 16 + r[j] % B] = 64 * j + lane;
+      if (first[j])
+        for (int t = 0; t < nbe[j]; ++t) f_be[bs[j] + t] = le[j];
+      if (blockIdx.x == 0 && 64 * j + lane < numel) a.slot_local_out[64 * j + lane] = le[j];
+    }
     if (lane == 0) *f_nblk = tot;
-    if (blockIdx.x == 0 && lane < numel) a.slot_local_out[lane] = le;
   }
   __syncthreads();
   const int nb = *f_nblk;

@@ -132,7 +132,7 @@ class MoELayer:
         """align -> gate/up GEMM -> activation -> down GEMM -> combine.  With fused_act the
         activation runs in the GEMM1 epilogue (bitwise the same result, one launch and one
         [numel, N13] round trip less); for a gated activation cfg13 then needs ng 2 or 4.
-        With fused_align (default: whenever it applies -- at most 64 slots, the streaming decode
+        With fused_align (default: whenever it applies -- at most 128 slots, the streaming decode
         kernel, fused_act) the align runs inside that same launch as well (bitwise the same).
         With fused_combine (no norm, the streaming decode kernel for the down GEMM) the weighted
         sum runs in the down GEMM's launch (bitwise the same; counters are added to the workspace
@@ -155,7 +155,7 @@ class MoELayer:
         if fused_align is None:
             fused_align = fused_act and routable
         if fused_align and not (fused_act and routable):
-            raise ValueError("fused_align needs fused_act, at most 64 slots, block_m <= 16 and the "
+            raise ValueError("fused_align needs fused_act, at most 128 slots, block_m <= 16 and the "
                              "streaming decode kernel")
         align_out = (ws.sorted_ids, ws.expert_ids, ws.ntpp, ws.slot_local)
         if fused_act and self.gated and cfg13.ng < 2:

@@ -243,14 +243,14 @@ def moe_w4a16_gemm_act(kind: str, A: torch.Tensor, W13: PreparedWeights, sorted_
     return out
 
 
-FUSED_ALIGN_SLOTS = 64  # most slots (M * top_k) of moe_w4a16_gemm_act_routed
+FUSED_ALIGN_SLOTS = 128  # most slots (M * top_k) of moe_w4a16_gemm_act_routed
 
 
 def moe_w4a16_gemm_act_routed(kind: str, A: torch.Tensor, W13: PreparedWeights, topk_ids: torch.Tensor,
                               expert_start: int, block_m: int, alpha: float = 1.702,
                               limit: float = float("inf"), out: Optional[torch.Tensor] = None,
                               align_out=None, cfg: Optional[L.MoeGemmConfig] = None):
-    """moe_align + moe_w4a16_gemm_act in one launch for at most 64 slots (block_m <= 16).
+    """moe_align + moe_w4a16_gemm_act in one launch for at most 128 slots (block_m <= 16).
     -> (out, (sorted_token_ids, expert_ids, num_tokens_post_padded, slot_local_ids))."""
     _need(A, torch.bfloat16, "A")
     _need(topk_ids, torch.int32, "topk_ids")

@@ -142,11 +142,11 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.moe_w4a16_gemm_act(L.ACT["silu_mul"], 1.0, 1.0, s, 8, 4096, s, 8192, C.byref(W), s, s, s, 8, 8,
                                   16, None, None) == L.MOE_EINVAL and b"gate/up pair" in lib.moe_last_error()
     W.flags = 1
-    # the fused align: at most 64 slots, block_m <= 16, every align output given, streaming kernel
+    # the fused align: at most 128 slots, block_m <= 16, every align output given, streaming kernel
     routed = lib.moe_w4a16_gemm_act_routed
     a16 = C.c_void_p(4096)
-    assert routed(L.ACT["silu_mul"], 1.0, 1.0, a16, 40, 4096, a16, 4096, C.byref(W), s, 40, 2, 0, 16,
-                  s, s, s, s, None, None) == L.MOE_EUNSUPPORTED and b"at most 64" in lib.moe_last_error()
+    assert routed(L.ACT["silu_mul"], 1.0, 1.0, a16, 65, 4096, a16, 4096, C.byref(W), s, 65, 2, 0, 16,
+                  s, s, s, s, None, None) == L.MOE_EUNSUPPORTED and b"at most 128" in lib.moe_last_error()
     assert routed(L.ACT["silu_mul"], 1.0, 1.0, a16, 1, 4096, a16, 4096, C.byref(W), s, 1, 8, 0, 32,
                   s, s, s, s, None, None) == L.MOE_EUNSUPPORTED and b"block_m" in lib.moe_last_error()
     assert routed(L.ACT["silu_mul"], 1.0, 1.0, a16, 1, 4096, a16, 4096, C.byref(W), s, 1, 8, 0, 16,

@@ -1,5 +1,5 @@
 """The fused route-and-align (moe_w4a16_gemm_act_routed, the single-token fast path widened to
-64 slots): its align outputs and its activated gate/up output equal those of moe_align followed
+128 slots): its align outputs and its activated gate/up output equal those of moe_align followed
 by moe_w4a16_gemm_act bit for bit, and the whole layer with it meets the layer bar against the
 oracle."""
 import numpy as np
@@ -52,8 +52,8 @@ def _compare(qtype, ids: np.ndarray, start: int, B: int, cfg=None, seed=0):
 def test_routed_equals_align_then_gemm_act(qtype, M):
     wl, _ = _w13(qtype)
     k = wl.top_k
-    if M * k > 64:
-        pytest.skip("more than 64 slots")
+    if M * k > 128:
+        pytest.skip("more than 128 slots")
     inp = W.make_inputs(wl, M, seed=200 + M)
     _compare(qtype, inp.topk_ids, wl.expert_start, 16)
 
@@ -61,13 +61,13 @@ def test_routed_equals_align_then_gemm_act(qtype, M):
 @pytest.mark.parametrize("seed", range(8))
 def test_routed_random_ids(seed):
     # junk ids, repeated experts inside a token, off-slice slots, no live slot at all, block
-    # sizes 1..16, up to 64 slots, several launch shapes
+    # sizes 1..16, up to 128 slots (one and two 64-slot batches), several launch shapes
     rng = np.random.default_rng(300 + seed)
     qtype = W.QTYPES[seed % len(W.QTYPES)]
     wl, W13 = _w13(qtype)
     n_local = W13.desc.n_experts
     k = int(rng.integers(1, 9))
-    M = int(rng.integers(1, 64 // k + 1))
+    M = int(rng.integers(1, 128 // k + 1))
     start = int(rng.integers(0, 6))
     ids = rng.integers(-3, start + n_local + 4, size=(M, k)).astype(np.int32)
     if seed == 5:
@@ -79,17 +79,37 @@ def test_routed_random_ids(seed):
     _compare(qtype, ids, start, B, cfg, seed)
 
 
+def test_routed_two_batches():
+    # 65..128 slots run as two 64-slot batches of one wave: ranks and block starts across the batches
+    wl, W13 = _w13("nvfp4_g16")
+    n_local, start = W13.desc.n_experts, wl.expert_start
+    cases = [
+        np.full((16, 8), start + 3),                                      # one expert, 128 slots
+        np.concatenate([np.full(64, start + 3), np.full(64, start + 1)]).reshape(16, 8),  # later batch, lower expert
+        np.concatenate([np.full(64, start + 2), np.full(1, start + 2)]).reshape(65, 1),   # 65 slots, one in batch 1
+        np.concatenate([np.full(64, start + n_local + 5), np.arange(63) % n_local + start]).reshape(127, 1),  # batch 0 off-slice
+        np.concatenate([np.arange(64) % n_local + start, np.full(64, -1)]).reshape(32, 4),                     # batch 1 junk
+        (np.arange(128) * 7) % n_local + start,                           # every expert in both batches
+    ]
+    for i, ids in enumerate(cases):
+        ids = np.asarray(ids, dtype=np.int32).reshape(-1, 8) if ids.size % 8 == 0 and ids.ndim == 1 else np.asarray(ids, dtype=np.int32)
+        for B in (1, 5, 16):
+            _compare("nvfp4_g16", ids, start, B, seed=i)
+
+
 def test_routed_rejects_large_batches():
     wl, W13 = _w13("int4_g128")
-    x = torch.zeros((40, wl.H), dtype=torch.bfloat16, device="cuda")
-    ids = torch.zeros((40, 2), dtype=torch.int32, device="cuda")
-    with pytest.raises(ValueError, match="at most 64"):
+    x = torch.zeros((65, wl.H), dtype=torch.bfloat16, device="cuda")
+    ids = torch.zeros((65, 2), dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError, match="at most 128"):
         P.moe_w4a16_gemm_act_routed(wl.act, x, W13, ids, 0, 16)
 
 
 @pytest.mark.parametrize("qtype,M", [("int4_g128", 1), ("int4_g128", 32), ("nvfp4_g16", 1), ("nvfp4_g16", 8),
-                                     ("mxfp4_g32", 1), ("mxfp4_g32", 16)])
+                                     ("nvfp4_g16", 12), ("mxfp4_g32", 1), ("mxfp4_g32", 16)])
 def test_layer_with_fused_align(qtype, M):
+    # (nvfp4 M=12: 96 slots, about a quarter of them on the slice -- 16-slot blocks on the streaming
+    # kernel, the align fused as two 64-slot batches)
     wl = W.small_workload(qtype)
     lw = W.make_weights(wl)
     inp = W.make_inputs(wl, M, seed=400 + M)
