@@ -32,6 +32,74 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Wave 0's part: the align of the slots in NB 64-slot batches (numel <= 64 * NB), one slot per
+// lane in each batch.
+template <int NB>
+__device__ void fused_align_wave(const GemmArgs& a, int* f_rows, int* f_be, int* f_nblk) {
+  const int lane = (int)threadIdx.x & 63, B = a.block_m, numel = a.numel;
+  int le[NB];
+  bool live[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int s = 64 * j + lane;
+    const int id = s < numel ? a.topk_ids[s] : -1;
+    live[j] = s < numel && id >= a.expert_start && id - a.expert_start < a.E;
+    le[j] = live[j] ? id - a.expert_start : -1;
+  }
+  // the slots of batch jj routed to local expert e (e is this lane's own; the ballots over the
+  // bits of the batch's expert ids are the same for every lane)
+  auto same_in = [&](int jj, int e) {
+    uint64_t m = __ballot(live[jj]);
+    for (int b = 0; (1 << b) < a.E; ++b) {
+      const uint64_t mb = __ballot(live[jj] && ((le[jj] >> b) & 1));
+      m &= ((e >> b) & 1) ? mb : ~mb;
+    }
+    return m;
+  };
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int r[NB], nbe[NB];
+  bool first[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    int before = 0, count = 0;   // the expert's slots in earlier batches / in all batches
+#pragma unroll
+    for (int jj = 0; jj < NB; ++jj) {
+      const uint64_t m = same_in(jj, le[j]);
+      if (jj < j) before += __popcll(m);
+      if (jj == j) before += __popcll(m & below);
+      count += __popcll(m);
+    }
+    r[j] = before;                          // rank among the expert's slots
+    nbe[j] = (count + B - 1) / B;           // blocks of the expert
+    first[j] = live[j] && r[j] == 0;
+  }
+  // blocks of the experts before each slot's: a walk over the first slot of every live expert
+  int bs[NB], tot = 0;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) bs[j] = 0;
+#pragma unroll
+  for (int jj = 0; jj < NB; ++jj) {
+    uint64_t fm = __ballot(first[jj]);
+    while (fm) {
+      const int q = __builtin_ctzll(fm);
+      fm &= fm - 1;
+      const int lej = __shfl(le[jj], q), nj = __shfl(nbe[jj], q);
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        if (lej < le[j]) bs[j] += nj;
+      tot += nj;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    if (live[j]) f_rows[(bs[j] + r[j] / B) * 16 + r[j] % B] = 64 * j + lane;
+    if (first[j])
+      for (int t = 0; t < nbe[j]; ++t) f_be[bs[j] + t] = le[j];
+    if (blockIdx.x == 0 && 64 * j + lane < numel) a.slot_local_out[64 * j + lane] = le[j];
+  }
+  if (lane == 0) *f_nblk = tot;
+}
+
 // Route-and-align of at most kFusedAlignSlots slots, computed by wave 0, one slot per lane in each
 // 64-slot batch (the same result as moe_align: local expert = id - start inside [start, start + E),
 // else the slot is dropped; slots grouped by ascending expert, ascending slot order inside an
@@ -39,74 +107,13 @@ __device__ __forceinline__ void lds_barrier() {
 //   f_rows[b * 16 + r] = slot of row r of block b (numel for padding), f_be[b] = its expert,
 //   returns the block count.  Workgroup 0 also writes sorted_out[cap], eids_out[cap_blocks]
 //   (-1 past the last block), *ntpp_out and slot_local_out[numel].  Every thread calls it.
+template <int NB>
 __device__ int fused_align(const GemmArgs& a, int* f_rows, int* f_be, int* f_nblk) {
-  constexpr int NB = kFusedAlignSlots / 64;  // 64-slot batches
-  const int tid = (int)threadIdx.x, lane = tid & 63, B = a.block_m, numel = a.numel;
-  for (int p = tid; p < kFusedAlignSlots * 16; p += (int)blockDim.x) f_rows[p] = numel;
+  const int tid = (int)threadIdx.x, B = a.block_m, numel = a.numel;
+  // (a block holds at least one live slot, so at most numel blocks are ever read)
+  for (int p = tid; p < min(numel, 64 * NB) * 16; p += (int)blockDim.x) f_rows[p] = numel;
   __syncthreads();
-  if (tid < 64) {
-    int le[NB];
-    bool live[NB];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int s = 64 * j + lane;
-      const int id = s < numel ? a.topk_ids[s] : -1;
-      live[j] = s < numel && id >= a.expert_start && id - a.expert_start < a.E;
-      le[j] = live[j] ? id - a.expert_start : -1;
-    }
-    // the slots of batch jj routed to local expert e (e is this lane's own; the ballots over the
-    // bits of the batch's expert ids are the same for every lane)
-    auto same_in = [&](int jj, int e) {
-      uint64_t m = __ballot(live[jj]);
-      for (int b = 0; (1 << b) < a.E; ++b) {
-        const uint64_t mb = __ballot(live[jj] && ((le[jj] >> b) & 1));
-        m &= ((e >> b) & 1) ? mb : ~mb;
-      }
-      return m;
-    };
-    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-    int r[NB], nbe[NB];
-    bool first[NB];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      int before = 0, count = 0;   // the expert's slots in earlier batches / in all batches
-#pragma unroll
-      for (int jj = 0; jj < NB; ++jj) {
-        const uint64_t m = same_in(jj, le[j]);
-        if (jj < j) before += __popcll(m);
-        if (jj == j) before += __popcll(m & below);
-        count += __popcll(m);
-      }
-      r[j] = before;                          // rank among the expert's slots
-      nbe[j] = (count + B - 1) / B;           // blocks of the expert
-      first[j] = live[j] && r[j] == 0;
-    }
-    // blocks of the experts before each slot's: a walk over the first slot of every live expert
-    int bs[NB], tot = 0;
-#pragma unroll
-    for (int j = 0; j < NB; ++j) bs[j] = 0;
-#pragma unroll
-    for (int jj = 0; jj < NB; ++jj) {
-      uint64_t fm = __ballot(first[jj]);
-      while (fm) {
-        const int q = __builtin_ctzll(fm);
-        fm &= fm - 1;
-        const int lej = __shfl(le[jj], q), nj = __shfl(nbe[jj], q);
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          if (lej < le[j]) bs[j] += nj;
-        tot += nj;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      if (live[j]) f_rows[(bs[j] + r[j] / B) * 16 + r[j] % B] = 64 * j + lane;
-      if (first[j])
-        for (int t = 0; t < nbe[j]; ++t) f_be[bs[j] + t] = le[j];
-      if (blockIdx.x == 0 && 64 * j + lane < numel) a.slot_local_out[64 * j + lane] = le[j];
-    }
-    if (lane == 0) *f_nblk = tot;
-  }
+  if (tid < 64) fused_align_wave<NB>(a, f_rows, f_be, f_nblk);
   __syncthreads();
   const int nb = *f_nblk;
   if (blockIdx.x == 0) {
@@ -118,7 +125,7 @@ __device__ int fused_align(const GemmArgs& a, int* f_rows, int* f_be, int* f_nbl
   return nb;
 }
 
-template <int QT, bool BIAS, int NG, int KS, int ACT, bool FA, bool CMB>
+template <int QT, bool BIAS, int NG, int KS, int ACT, int FA, bool CMB>
 __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   static_assert(!act_paired<ACT>() || NG % 2 == 0, "the fused gated epilogue pairs gate and up tiles");
   static_assert(!CMB || (ACT == kActNone && !FA), "the fused weighted sum follows a plain projection");
@@ -136,10 +143,14 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   const int NTA = act_paired<ACT>() ? NT / 2 : NT;  // tiles to assign (gate tiles if fused)
   const int NS = (NTA + NGA - 1) / NGA;           // strips per block
   const int B = a.block_m;
-  __shared__ int f_rows[FA ? kFusedAlignSlots * 16 : 1];
-  __shared__ int f_be[FA ? kFusedAlignSlots : 1];
+  // fused align (FA = its 64-slot batches, 0 = none)
+  __shared__ int f_rows[FA ? FA * 64 * 16 : 1];
+  __shared__ int f_be[FA ? FA * 64 : 1];
   __shared__ int f_nblk;
-  const int nblocks = FA ? fused_align(a, f_rows, f_be, &f_nblk) : *a.ntpp / B;
+  const int nblocks = [&] {
+    if constexpr (FA > 0) return fused_align<FA>(a, f_rows, f_be, &f_nblk);
+    else return *a.ntpp / B;
+  }();
   const int items = nblocks * NS;
   if constexpr (CMB) {  // a token without a live slot sums to zero: no item ever reaches it
     for (int t = blockIdx.x; t < a.cmb_ntok; t += gridDim.x) {
@@ -351,7 +362,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   }
 }
 
-template <int QT, bool BIAS, int NG, int ACT, bool FA, bool CMB>
+template <int QT, bool BIAS, int NG, int ACT, int FA, bool CMB>
 static int launch_stream_ng(const GemmArgs& a, int ks, int grid, hipStream_t st) {
   switch (ks) {
     case 1: hipLaunchKernelGGL((gemm_stream_kernel<QT, BIAS, NG, 1, ACT, FA, CMB>), dim3(grid), dim3(64), 0, st, a); break;
@@ -363,7 +374,7 @@ static int launch_stream_ng(const GemmArgs& a, int ks, int grid, hipStream_t st)
   return check_launch("moe_w4a16_gemm (decode stream)");
 }
 
-template <int QT, bool BIAS, int ACT, bool FA, bool CMB = false>
+template <int QT, bool BIAS, int ACT, int FA, bool CMB = false>
 static int launch_stream_b(const GemmArgs& a, const moe_gemm_config& c, int grid, hipStream_t st) {
   if constexpr (!act_paired<ACT>()) {
     if (c.ng == 1) return launch_stream_ng<QT, BIAS, 1, ACT, FA, CMB>(a, c.ksplit, grid, st);
@@ -380,11 +391,13 @@ template <int QT, bool BIAS, int ACT>
 static int launch_stream_fa(const GemmArgs& a, const moe_gemm_config& c, int grid, hipStream_t st) {
   if constexpr (ACT == kActNone) {
     if (a.topk_ids) return fail(MOE_EUNSUPPORTED, "moe_w4a16_gemm: the fused align needs a fused activation");
-    return a.cmb_out ? launch_stream_b<QT, BIAS, ACT, false, true>(a, c, grid, st)
-                     : launch_stream_b<QT, BIAS, ACT, false>(a, c, grid, st);
+    return a.cmb_out ? launch_stream_b<QT, BIAS, ACT, 0, true>(a, c, grid, st)
+                     : launch_stream_b<QT, BIAS, ACT, 0>(a, c, grid, st);
   } else {
-    return a.topk_ids ? launch_stream_b<QT, BIAS, ACT, true>(a, c, grid, st)
-                      : launch_stream_b<QT, BIAS, ACT, false>(a, c, grid, st);
+    // (the fused align's second 64-slot batch only when the slots need it: a kernel of its own)
+    if (!a.topk_ids) return launch_stream_b<QT, BIAS, ACT, 0>(a, c, grid, st);
+    return a.numel > 64 ? launch_stream_b<QT, BIAS, ACT, 2>(a, c, grid, st)
+                        : launch_stream_b<QT, BIAS, ACT, 1>(a, c, grid, st);
   }
 }
 
